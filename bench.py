@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked-prefill hot path on one MI355X.
+
+Step = one chunked prefill of a 4000-token GQA prompt (32 query / 8 KV
+heads, head dim 128, bf16, cache bound at capacity 8192) in W = 512 chunks
+through the C ABI: chunk split, ladder, padded append (the 416-row tail is
+padded to 512), chunk attention, truncation and rewind.  Inputs are seeded
+synthetic N(0,1) values already resident in HBM.
+
+value  = algorithmic attention TFLOP/s of the whole step: 4*D*Hq flops per
+         visible (query, key) pair, 131.10 GFLOP per step, / step time.
+roofline = the attention kernel alone: per-launch algorithmic flops over its
+         average launch duration (HIP events on the launch stream), against
+         the bf16 dense MFMA peak of 2.5 PFLOP/s.
+secondary = decode rows of the mixed-step workload (64 sequences, contexts
+         uniform in [512, 16384]) as a decode-only packed step: KV bytes read
+         per second against the 8 TB/s HBM peak; plus a steady-state W=512
+         chunk at past_len 7680.
+cpu_baseline = the fp64 CPU oracle timed on this host on a bounded sample of
+         the same workload (rows of the last chunk), same flop accounting.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_w512_traffic.txt")
+ATTN_SRC = os.path.join(ROOT, "chunked_prefill_causal_kv_amd", "csrc", "k_attn.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def chunk_flops(past, real, Hq, D):
+    """Algorithmic flops of one chunk: 4*D per visible (query, key) pair per
+    query head; row i of the chunk sees past + i + 1 keys."""
+    pairs = real * past + real * (real + 1) // 2
+    return 4 * D * Hq * pairs
+
+
+def attn_src_sha():
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(sha):
+    """Measured HBM bytes per attention launch from the committed counter
+    summary, or None if absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def bench_chunked(cpk, si, torch, steps, warmup):
+    L, Hq, Hkv, D, W, CAP = 4000, 32, 8, 128, 512, 8192
+    q, k, v = (x.cuda() for x in si.gqa_prompt(L=L, Hq=Hq, Hkv=Hkv, D=D))
+    cache = cpk.KVCache(1, Hkv, CAP, D, torch.bfloat16)
+    out = torch.empty_like(q)
+    chunks = cpk.cpk_split_chunks(L, W)
+    stream = torch.cuda.current_stream()
+    flops = [chunk_flops(p, r, Hq, D) for p, r in chunks]
+
+    def step(events):
+        if cache.lens[0]:
+            cpk.cpk_rewind(cache, 0, 0)
+        for i, (past, rows) in enumerate(chunks):
+            width = cpk.cpk_ladder_width(W, rows)
+            sl = slice(past, past + rows)
+            cpk.cpk_kv_append(cache, 0, k[sl], v[sl], past, rows=width)
+            if events is not None:
+                events[i][0].record(stream)
+            cpk.cpk_chunk_attention(q[sl], cache, 0, past, rows=width, out=out[sl])
+            if events is not None:
+                events[i][1].record(stream)
+            cpk.cpk_rewind(cache, 0, past + rows)
+
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in chunks] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per_chunk_ms = [[evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)]
+                    for i in range(len(chunks))]
+    ms_step = (t1 - t0) * 1e3 / steps
+    total_flops = sum(flops)
+    kern_ms = [sum(c) / len(c) for c in per_chunk_ms]
+    achieved = (total_flops / len(chunks)) / (sum(kern_ms) / len(chunks) * 1e-3) / 1e12
+    table = [{"past_len": p, "rows": r, "gflop": round(f / 1e9, 3),
+              "ms": round(m, 4), "tflops": round(f / (m * 1e-3) / 1e12, 1)}
+             for (p, r), f, m in zip(chunks, flops, kern_ms)]
+    return dict(ms_step=ms_step, total_flops=total_flops, achieved=achieved,
+                kern_ms_avg=sum(kern_ms) / len(kern_ms), table=table, chunks=chunks,
+                q=q, k=k, v=v)
+
+
+def bench_steady_chunk(cpk, si, torch, reps=20):
+    """One W=512 chunk at past_len 7680 (cache 8192): steady-state point."""
+    Hq, Hkv, D, P, W = 32, 8, 128, 7680, 512
+    cache = cpk.KVCache(1, Hkv, 8192, D, torch.bfloat16)
+    si.fill_seeded(cache.k, 11)
+    si.fill_seeded(cache.v, 12)
+    q = si.randn((W, Hq, D), "bf16", si.generator(13)).cuda()
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        cpk.cpk_chunk_attention(q, cache, 0, P, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        cpk.cpk_chunk_attention(q, cache, 0, P, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    f = chunk_flops(P, W, Hq, D)
+    return {"past_len": P, "rows": W, "gflop": round(f / 1e9, 2), "ms": round(ms, 4),
+            "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
+
+
+def bench_decode(cpk, si, torch, reps=10):
+    """Decode rows of the mixed-step workload as a decode-only packed step."""
+    Hq, Hkv, D, CAP = 32, 8, 128, 16400
+    ctxs = si.mixed_contexts()
+    n = len(ctxs)
+    cache = cpk.KVCache(n, Hkv, CAP, D, torch.bfloat16)
+    si.fill_seeded(cache.k, 21)
+    si.fill_seeded(cache.v, 22)
+    g = si.generator(23)
+    q = si.randn((n, Hq, D), "bf16", g).cuda()
+    kn = si.randn((n, Hkv, D), "bf16", g).cuda()
+    vn = si.randn((n, Hkv, D), "bf16", g).cuda()
+    slots = list(range(n))
+    cu = list(range(n + 1))
+    meta = torch.tensor(slots + cu + ctxs, dtype=torch.int32).cuda()
+    max_ctx = max(ctxs) + 1
+    ws = torch.empty(cpk.cpk_varlen_workspace_size(n, Hq, max_ctx, D) // 4 + 4,
+                     dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        cpk.cpk_varlen_step(q, kn, vn, cache, slots, cu, ctxs, out=out, ws=ws, dev_meta=meta)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        cpk.cpk_varlen_step(q, kn, vn, cache, slots, cu, ctxs, out=out, ws=ws, dev_meta=meta)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    kv_bytes = sum((c + 1) * Hkv * D * 2 * 2 for c in ctxs)
+    io_bytes = n * Hq * D * 2 * 2 + n * Hkv * D * 2 * 2 * 2
+    gbps = (kv_bytes + io_bytes) / (ms * 1e-3) / 1e9
+    return {"sequences": n, "kv_gb": round(kv_bytes / 1e9, 3), "ms": round(ms, 4),
+            "GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+            "note": "whole packed step (append + split-KV decode + combine)"}
+
+
+def cpu_baseline(si, budget_s=10.0):
+    """The fp64 oracle on rows of the last chunk (past_len 3584, 416 real
+    rows), sampled until about budget_s seconds of CPU work."""
+    import numpy as np
+
+    import oracle
+    L, Hq, Hkv, D = 4000, 32, 8, 128
+    q, k, v = si.gqa_prompt(L=L, Hq=Hq, Hkv=Hkv, D=D)
+    qs, ks, vs = (si.storage(x) for x in (q, k, v))
+    kk = oracle.widen(np.ascontiguousarray(ks.transpose(1, 0, 2)), oracle.BF16)
+    vv = oracle.widen(np.ascontiguousarray(vs.transpose(1, 0, 2)), oracle.BF16)
+    rows_all = np.arange(3584, 4000)
+    rng = np.random.default_rng(0)
+    rows_all = rng.permutation(rows_all)
+    done_rows, flops, t_total = 0, 0, 0.0
+    batch = 16
+    while done_rows < len(rows_all) and t_total < budget_s:
+        rows = np.sort(rows_all[done_rows:done_rows + batch])
+        qq = oracle.widen(np.ascontiguousarray(qs[rows]), oracle.BF16)
+        t0 = time.perf_counter()
+        oracle.attention(qq, kk, vv, np.zeros(len(rows), np.int32), rows.astype(np.int32),
+                         1.0 / math.sqrt(D))
+        t_total += time.perf_counter() - t0
+        flops += sum(4 * D * Hq * (int(r) + 1) for r in rows)
+        done_rows += len(rows)
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done_rows} of the 416 rows of the last W=512 chunk (past_len 3584) "
+                      f"of the 4000-token prompt, all 32 heads, fp64; {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by KV head or by sequence with no exchange inside "
+              "attention, but this build runs and reports a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import chunked_prefill_causal_kv_amd as cpk
+    import synth_inputs as si
+
+    torch.cuda.set_device(0)
+    log("bench: chunked prefill 4000 tokens, W=512, GQA 32/8, D=128, bf16")
+    r = bench_chunked(cpk, si, torch, args.steps, args.warmup)
+    log(f"bench: {r['ms_step']:.3f} ms/step, attention {r['achieved']:.1f} TFLOP/s")
+    secondary = {}
+    if not args.no_secondary:
+        secondary["steady_chunk"] = bench_steady_chunk(cpk, si, torch)
+        log(f"bench: steady chunk {secondary['steady_chunk']}")
+        secondary["decode_rows"] = bench_decode(cpk, si, torch)
+        log(f"bench: decode {secondary['decode_rows']}")
+        secondary["per_chunk"] = r["table"]
+    sha = attn_src_sha()
+    value = r["total_flops"] / (r["ms_step"] * 1e-3) / 1e12
+    line = {
+        "metric": "chunk-attn TFLOP/s & % bf16 MFMA peak at W=512; decode-row KV GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "GQA chunked prefill: 4000-token prompt in W=512 chunks "
+                               "(7x512 + 416 padded to 512), 32 query / 8 KV heads, "
+                               "head_dim 128, cache capacity 8192, seqlens_k",
+                   "global_batch": 1, "seq_len": 4000, "chunk": 512, "parallelism": "none"},
+        "roofline": {"bound": "mfma", "achieved": round(r["achieved"], 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(r["achieved"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": read_traffic(sha),
+                     "kernel": "attn_mfma_kernel<bf16,128>",
+                     "avg_launch_ms": round(r["kern_ms_avg"], 4),
+                     "kernel_source_sha": sha},
+        "secondary": secondary,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(si)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,329 @@
+"""Python binding of libcpk: chunked-prefill causal attention over a KV cache
+on AMD MI355X (gfx950).
+
+Argument marshalling only.  Every step of the path (append, attention,
+rewind, rolling shift, decode, combine) runs in the HIP kernels of
+``libcpk.so``; the host logic (ladder, chunk split, step planner) runs in its
+C code.  PyTorch provides device memory and the current stream.  There is no
+CPU fallback: importing this package fails if the library is not built.
+
+The function names are the C ABI's (``include/cpk.h``).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcpk.so")
+
+CPK_OK, CPK_EINVAL, CPK_EDTYPE, CPK_ECAPACITY, CPK_EALIGN, CPK_EWORKSPACE, CPK_EHIP = \
+    0, -1, -2, -3, -4, -5, -6
+CPK_F32, CPK_F16, CPK_BF16 = 0, 1, 2
+DTYPE_CODE = {torch.float32: CPK_F32, torch.float16: CPK_F16, torch.bfloat16: CPK_BF16}
+DECODE_SEGMENT = 256
+
+
+class CpkError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"cpk status {status}: {message}")
+        self.status = status
+
+
+class cpk_kv_cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("seqlens_k", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run "
+                          "`python -m chunked_prefill_causal_kv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    IP = ctypes.POINTER(ctypes.c_int)
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    CP = ctypes.POINTER(cpk_kv_cache)
+    F = ctypes.c_float
+    sig = {
+        "cpk_version": ([], I),
+        "cpk_last_error": ([], ctypes.c_char_p),
+        "cpk_device_info": ([ctypes.c_char_p, I, IP], I),
+        "cpk_ladder_rungs": ([I, IP, IP], I),
+        "cpk_ladder_width": ([I, I, IP], I),
+        "cpk_split_chunks": ([I, I, I32P, I32P, I, IP], I),
+        "cpk_plan_step": ([I, I, I, IP], I),
+        "cpk_kv_append": ([CP, I, P, P, I, I, I, P], I),
+        "cpk_chunk_attention": ([P, CP, I, I, I, I, I, F, P, P], I),
+        "cpk_rewind": ([CP, I, I, I, P], I),
+        "cpk_prefill_chunk": ([P, P, P, CP, I, I, I, I, I, I, F, P, IP, P], I),
+        "cpk_varlen_workspace_size": ([I, I, I, I], Z),
+        "cpk_varlen_step": ([P, P, P, CP, P, P, P, I32P, I32P, I32P, I, I, I, F, P, P, Z, P], I),
+        "cpk_roll_append": ([P, P, P, P, P, P, I, I, I, I, I, I, P], I),
+        "cpk_roll_attention": ([P, P, P, P, I, I, I, I, I, I, I, I, F, P, P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int):
+    if status != CPK_OK:
+        raise CpkError(status, _lib.cpk_last_error().decode())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libcpk must be contiguous")
+    return t.data_ptr()
+
+
+class KVCache:
+    """Device cache [batch, kv_heads, capacity, head_dim] bound at physical
+    capacity, with seqlens_k on the device and a host mirror `lens`."""
+
+    def __init__(self, batch: int, kv_heads: int, capacity: int, head_dim: int,
+                 dtype=torch.bfloat16, device="cuda", k=None, v=None):
+        shape = (batch, kv_heads, capacity, head_dim)
+        self.k = torch.zeros(shape, dtype=dtype, device=device) if k is None else k
+        self.v = torch.zeros(shape, dtype=dtype, device=device) if v is None else v
+        self.seqlens_k = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.lens = [0] * batch
+        self.dtype = dtype
+        self.desc = cpk_kv_cache(self.k.data_ptr(), self.v.data_ptr(), self.seqlens_k.data_ptr(),
+                                 batch, kv_heads, capacity, head_dim, DTYPE_CODE[dtype])
+
+    @property
+    def batch(self):
+        return self.desc.batch
+
+    @property
+    def kv_heads(self):
+        return self.desc.kv_heads
+
+    @property
+    def capacity(self):
+        return self.desc.capacity
+
+    @property
+    def head_dim(self):
+        return self.desc.head_dim
+
+
+# ---------------------------------------------------------------- host logic
+
+def cpk_version() -> int:
+    return _lib.cpk_version()
+
+
+def cpk_last_error() -> str:
+    return _lib.cpk_last_error().decode()
+
+
+def cpk_device_info() -> Tuple[str, int]:
+    buf = ctypes.create_string_buffer(128)
+    cu = ctypes.c_int(0)
+    _check(_lib.cpk_device_info(buf, 128, ctypes.byref(cu)))
+    return buf.value.decode(), cu.value
+
+
+def cpk_ladder_rungs(W: int) -> List[int]:
+    out = (ctypes.c_int * 3)()
+    n = ctypes.c_int(0)
+    _check(_lib.cpk_ladder_rungs(W, out, ctypes.byref(n)))
+    return list(out[:n.value])
+
+
+def cpk_ladder_width(W: int, rows: int) -> int:
+    w = ctypes.c_int(0)
+    _check(_lib.cpk_ladder_width(W, rows, ctypes.byref(w)))
+    return w.value
+
+
+def cpk_split_chunks(L: int, W: int) -> List[Tuple[int, int]]:
+    n = ctypes.c_int(0)
+    _lib.cpk_split_chunks(L, W, None, None, 0, ctypes.byref(n))
+    cnt = max(n.value, 1)
+    past = (ctypes.c_int32 * cnt)()
+    rows = (ctypes.c_int32 * cnt)()
+    _check(_lib.cpk_split_chunks(L, W, past, rows, cnt, ctypes.byref(n)))
+    return [(past[i], rows[i]) for i in range(n.value)]
+
+
+def cpk_plan_step(budget: int, n_decode: int, prompt_remaining: int) -> int:
+    r = ctypes.c_int(0)
+    _check(_lib.cpk_plan_step(budget, n_decode, prompt_remaining, ctypes.byref(r)))
+    return r.value
+
+
+# -------------------------------------------------------------- device calls
+
+def cpk_kv_append(cache: KVCache, b: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                  past_len: int, rows: Optional[int] = None, stream=None):
+    """Append k_new/v_new [real_rows, Hkv, D] at past_len; with rows >
+    real_rows the last real row is repeated into the padded positions."""
+    real = k_new.shape[0]
+    rows = real if rows is None else rows
+    _check(_lib.cpk_kv_append(ctypes.byref(cache.desc), b, _ptr(k_new), _ptr(v_new),
+                              past_len, rows, real, _stream(stream)))
+    cache.lens[b] = past_len + rows
+
+
+def cpk_chunk_attention(q: torch.Tensor, cache: KVCache, b: int, past_len: int,
+                        rows: Optional[int] = None, scale: float = 0.0,
+                        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Attention of q [real_rows, Hq, D] at past_len; `rows` >= real_rows
+    rows are computed (padding repeats q's last row), real rows written."""
+    real, Hq, D = q.shape
+    rows = real if rows is None else rows
+    if out is None:
+        out = torch.empty((real, Hq, D), dtype=q.dtype, device=q.device)
+    _check(_lib.cpk_chunk_attention(_ptr(q), ctypes.byref(cache.desc), b, Hq, past_len, rows,
+                                    real, float(scale), _ptr(out), _stream(stream)))
+    return out
+
+
+def cpk_rewind(cache: KVCache, b: int, new_len: int, stream=None):
+    _check(_lib.cpk_rewind(ctypes.byref(cache.desc), b, new_len, cache.lens[b], _stream(stream)))
+    cache.lens[b] = new_len
+
+
+def cpk_prefill_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cache: KVCache, b: int,
+                      past_len: int, W: int, pad: bool = True, scale: float = 0.0,
+                      out: Optional[torch.Tensor] = None, stream=None):
+    """One padded forward; returns (out [real_rows, Hq, D], issued width)."""
+    real, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((real, Hq, D), dtype=q.dtype, device=q.device)
+    width = ctypes.c_int(0)
+    _check(_lib.cpk_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(cache.desc), b, Hq,
+                                  past_len, real, W, 1 if pad else 0, float(scale), _ptr(out),
+                                  ctypes.byref(width), _stream(stream)))
+    cache.lens[b] = past_len + real
+    return out, width.value
+
+
+def cpk_varlen_workspace_size(n_seqs: int, q_heads: int, max_ctx: int, head_dim: int) -> int:
+    return int(_lib.cpk_varlen_workspace_size(n_seqs, q_heads, max_ctx, head_dim))
+
+
+def cpk_varlen_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache: KVCache,
+                    slots: Sequence[int], cu_rows: Sequence[int], past_lens: Sequence[int],
+                    scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None, dev_meta: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """One packed mixed step.  slots/cu_rows/past_lens are host sequences;
+    their device copies go in dev_meta (int32 [3*n+1], built here if not
+    given)."""
+    n = len(slots)
+    total, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    h_slots = (ctypes.c_int32 * n)(*slots)
+    h_cu = (ctypes.c_int32 * (n + 1))(*cu_rows)
+    h_past = (ctypes.c_int32 * n)(*past_lens)
+    if dev_meta is None:
+        dev_meta = torch.tensor(list(slots) + list(cu_rows) + list(past_lens),
+                                dtype=torch.int32).to(q.device)
+    base = dev_meta.data_ptr()
+    d_slots, d_cu, d_past = base, base + 4 * n, base + 4 * (2 * n + 1)
+    max_ctx = max([p + 1 for p, a, b in zip(past_lens, cu_rows[:-1], cu_rows[1:]) if b - a == 1],
+                  default=0)
+    need = cpk_varlen_workspace_size(n, Hq, max_ctx, D)
+    if ws is None:
+        ws = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.cpk_varlen_step(_ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(cache.desc),
+                                d_slots, d_cu, d_past, h_slots, h_cu, h_past, n, total, Hq,
+                                float(scale), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+    for s, slot in enumerate(slots):
+        cache.lens[slot] = past_lens[s] + cu_rows[s + 1] - cu_rows[s]
+    return out
+
+
+def cpk_roll_append(k_old, v_old, k_chunk, v_chunk, k_new, v_new, stream=None):
+    """new = cat(old, chunk)[c:]; caches [B, H, C, D], chunks [B, c, H, D]."""
+    B, H, C, D = k_old.shape
+    c = k_chunk.shape[1]
+    _check(_lib.cpk_roll_append(_ptr(k_old), _ptr(v_old), _ptr(k_chunk), _ptr(v_chunk),
+                                _ptr(k_new), _ptr(v_new), B, H, C, c, D,
+                                DTYPE_CODE[k_old.dtype], _stream(stream)))
+
+
+def cpk_roll_attention(q, k, v, abs_end: int, n_leftpad: int, mask=None, scale: float = 0.0,
+                       out=None, stream=None):
+    """q [c, Hq, D] over a rolling cache k/v [Hkv, C, D]."""
+    c, Hq, D = q.shape
+    Hkv, C, _ = k.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(_lib.cpk_roll_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(mask), abs_end, n_leftpad,
+                                   Hq, Hkv, C, c, D, DTYPE_CODE[q.dtype], float(scale),
+                                   _ptr(out), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------- drivers
+
+def prefill_chunked(cache: KVCache, b: int, q, k, v, W: int, pad: bool = True,
+                    scale: float = 0.0, out=None, stream=None):
+    """Chunked prefill of a whole prompt into sequence b: split by the
+    library, one padded forward per chunk.  Returns (out, widths)."""
+    L, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    widths = []
+    for past, rows in cpk_split_chunks(L, W):
+        sl = slice(past, past + rows)
+        _, w = cpk_prefill_chunk(q[sl], k[sl], v[sl], cache, b, past, W, pad, scale,
+                                 out=out[sl], stream=stream)
+        widths.append(w)
+    return out, widths
+
+
+def roll_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream=None):
+    """Rolling fixed-capacity prefill of one sequence (batch 1).  q/k/v are
+    token-major real tokens; the sequence is left-padded with zero rows to a
+    multiple of c.  masks: optional list of per-chunk (c, C) additive masks;
+    without it visibility is computed in the kernel.  Returns
+    (out over the padded sequence, n_leftpad, k cache, v cache)."""
+    L, Hq, D = q.shape
+    Hkv = k.shape[1]
+    n_left = (-L) % c
+    if n_left:
+        z = lambda x: torch.cat([torch.zeros((n_left,) + tuple(x.shape[1:]), dtype=x.dtype,
+                                             device=x.device), x])
+        q, k, v = z(q), z(k), z(v)
+    Lp = L + n_left
+    bufs = [torch.zeros((1, Hkv, C, D), dtype=q.dtype, device=q.device) for _ in range(4)]
+    out = torch.empty_like(q)
+    cur = 0
+    for j in range(Lp // c):
+        sl = slice(j * c, (j + 1) * c)
+        ko, vo = bufs[2 * cur], bufs[2 * cur + 1]
+        kn, vn = bufs[2 * (1 - cur)], bufs[2 * (1 - cur) + 1]
+        cpk_roll_append(ko, vo, k[sl].unsqueeze(0), v[sl].unsqueeze(0), kn, vn, stream)
+        cur = 1 - cur
+        m = None if masks is None else masks[j]
+        cpk_roll_attention(q[sl], kn[0], vn[0], (j + 1) * c, n_left, mask=m, scale=scale,
+                           out=out[sl], stream=stream)
+    return out, n_left, bufs[2 * cur][0], bufs[2 * cur + 1][0]

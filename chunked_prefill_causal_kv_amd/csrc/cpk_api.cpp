@@ -1,0 +1,423 @@
+// C-ABI entry points: argument validation, host logic (ladder, chunk split,
+// step planner) and kernel dispatch.  Every check runs before any launch, so
+// a call that fails writes no device memory.
+#include "../../include/cpk.h"
+#include "cpk_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok()
+{
+    g_err.clear();
+    return CPK_OK;
+}
+
+int hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) return fail(CPK_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int elem_size(int dtype)
+{
+    return dtype == CPK_F32 ? 4 : (dtype == CPK_F16 || dtype == CPK_BF16) ? 2 : 0;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_dtype_dim(int dtype, int D)
+{
+    if (elem_size(dtype) == 0) return fail(CPK_EDTYPE, "unknown dtype %d", dtype);
+    if (D != 64 && D != 128) return fail(CPK_EDTYPE, "head_dim %d not supported (64 or 128)", D);
+    return CPK_OK;
+}
+
+int check_cache(const cpk_kv_cache *c)
+{
+    if (!c) return fail(CPK_EINVAL, "cache is NULL");
+    if (!c->k || !c->v || !c->seqlens_k) return fail(CPK_EINVAL, "cache pointers must be set");
+    if (c->batch < 1 || c->kv_heads < 1 || c->capacity < 1)
+        return fail(CPK_EINVAL, "cache sizes must be positive");
+    int r = check_dtype_dim(c->dtype, c->head_dim);
+    if (r) return r;
+    if (!aligned16(c->k) || !aligned16(c->v)) return fail(CPK_EALIGN, "cache k/v not 16-byte aligned");
+    if (((uintptr_t)c->seqlens_k & 3u) != 0) return fail(CPK_EALIGN, "seqlens_k not 4-byte aligned");
+    return CPK_OK;
+}
+
+int check_heads(int Hq, int Hkv)
+{
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return fail(CPK_EINVAL, "q_heads %d must be a positive multiple of kv_heads %d", Hq, Hkv);
+    if (Hq / Hkv > 64) return fail(CPK_EINVAL, "group size %d above 64", Hq / Hkv);
+    return CPK_OK;
+}
+
+float resolve_scale(float scale, int D)
+{
+    return scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
+}
+
+void fill_scale(cpk::AttnArgs &a, float scale)
+{
+    a.scale = scale;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
+}
+
+int ladder_width_impl(int W, int rows)
+{
+    const int step = (W + 2) / 3;
+    for (int i = 1; i <= 3; ++i) {
+        const int r = i * step < W ? i * step : W;
+        if (r >= rows) return r;
+    }
+    return W;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cpk_version(void) { return 100; }
+
+const char *cpk_last_error(void) { return g_err.c_str(); }
+
+int cpk_device_info(char *name, int name_len, int *compute_units)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDeviceProperties");
+    if (name && name_len > 0) snprintf(name, (size_t)name_len, "%s", prop.gcnArchName);
+    if (compute_units) *compute_units = prop.multiProcessorCount;
+    return ok();
+}
+
+int cpk_ladder_rungs(int W, int *out, int *n)
+{
+    if (W < 1 || !out || !n) return fail(CPK_EINVAL, "ladder: W=%d must be >= 1", W);
+    const int step = (W + 2) / 3;
+    int cnt = 0;
+    for (int i = 1; i <= 3; ++i) {
+        const int r = i * step < W ? i * step : W;
+        if (cnt == 0 || out[cnt - 1] != r) out[cnt++] = r;
+    }
+    *n = cnt;
+    return ok();
+}
+
+int cpk_ladder_width(int W, int rows, int *width)
+{
+    if (!width) return fail(CPK_EINVAL, "width is NULL");
+    if (W < 1 || rows < 1 || rows > W)
+        return fail(CPK_EINVAL, "ladder: rows=%d outside [1, W=%d]", rows, W);
+    *width = ladder_width_impl(W, rows);
+    return ok();
+}
+
+int cpk_split_chunks(int L, int W, int32_t *past, int32_t *rows, int max, int *n)
+{
+    if (L < 0 || W < 1 || !n) return fail(CPK_EINVAL, "split: L=%d W=%d", L, W);
+    const int need = (L + W - 1) / W;
+    *n = need;
+    if (need > max || (need > 0 && (!past || !rows)))
+        return fail(CPK_EINVAL, "split: %d chunks do not fit max=%d", need, max);
+    for (int i = 0; i < need; ++i) {
+        past[i] = i * W;
+        rows[i] = (L - i * W) < W ? (L - i * W) : W;
+    }
+    return ok();
+}
+
+int cpk_plan_step(int budget, int n_decode, int prompt_remaining, int *prompt_rows)
+{
+    if (!prompt_rows || budget < 0 || n_decode < 0 || prompt_remaining < 0 || n_decode > budget)
+        return fail(CPK_EINVAL, "plan: budget=%d n_decode=%d remaining=%d", budget, n_decode,
+                    prompt_remaining);
+    const int room = budget - n_decode;
+    *prompt_rows = room < prompt_remaining ? room : prompt_remaining;
+    return ok();
+}
+
+int cpk_kv_append(const cpk_kv_cache *cache, int b, const void *k_new, const void *v_new,
+                  int past_len, int rows, int real_rows, void *stream)
+{
+    int r = check_cache(cache);
+    if (r) return r;
+    if (b < 0 || b >= cache->batch) return fail(CPK_EINVAL, "append: b=%d out of range", b);
+    if (!k_new || !v_new) return fail(CPK_EINVAL, "append: NULL input");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(CPK_EALIGN, "append: input not aligned");
+    if (past_len < 0 || rows < 1 || real_rows < 1 || real_rows > rows)
+        return fail(CPK_EINVAL, "append: past_len=%d rows=%d real_rows=%d", past_len, rows,
+                    real_rows);
+    if ((int64_t)past_len + rows > cache->capacity)
+        return fail(CPK_ECAPACITY, "append: %d + %d rows exceed capacity %d", past_len, rows,
+                    cache->capacity);
+    const int rb = cache->head_dim * elem_size(cache->dtype);
+    return hip_status(cpk::launch_kv_append(k_new, v_new, cache->k, cache->v, cache->seqlens_k,
+                                            cache->kv_heads, cache->capacity, rb, b, past_len,
+                                            rows, real_rows, (hipStream_t)stream),
+                      "kv_append launch");
+}
+
+static int attention_common(const void *q, const cpk_kv_cache *cache, int b, int q_heads,
+                            int past_len, int rows, int real_rows, float scale, void *out,
+                            hipStream_t st)
+{
+    int r = check_cache(cache);
+    if (r) return r;
+    if ((r = check_heads(q_heads, cache->kv_heads))) return r;
+    if (b < 0 || b >= cache->batch) return fail(CPK_EINVAL, "attention: b=%d out of range", b);
+    if (!q || !out) return fail(CPK_EINVAL, "attention: NULL q/out");
+    if (!aligned16(q) || !aligned16(out)) return fail(CPK_EALIGN, "attention: q/out not aligned");
+    if (rows < 1 || real_rows < 1 || real_rows > rows || past_len < 0)
+        return fail(CPK_EINVAL, "attention: rows=%d real_rows=%d past_len=%d", rows, real_rows,
+                    past_len);
+    if ((int64_t)past_len + rows > cache->capacity)
+        return fail(CPK_ECAPACITY, "attention: %d + %d rows exceed capacity %d", past_len, rows,
+                    cache->capacity);
+    cpk::AttnArgs a = {};
+    a.q = q; a.k = cache->k; a.v = cache->v; a.out = out; a.mask = nullptr;
+    a.Hq = q_heads; a.Hkv = cache->kv_heads; a.D = cache->head_dim; a.cap = cache->capacity;
+    fill_scale(a, resolve_scale(scale, a.D));
+    a.slot = b; a.q_row0 = 0; a.out_row0 = 0; a.rows = rows; a.q_src_rows = real_rows;
+    a.out_rows = real_rows; a.n_keys = past_len + rows; a.key_lo = 0; a.causal_base = past_len;
+    const int br = cpk::attn_rows_per_block(cache->dtype, q_heads / cache->kv_heads);
+    return hip_status(cpk::launch_attention(a, cache->dtype, (rows + br - 1) / br, 1, st),
+                      "attention launch");
+}
+
+int cpk_chunk_attention(const void *q, const cpk_kv_cache *cache, int b, int q_heads,
+                        int past_len, int rows, int real_rows, float scale, void *out,
+                        void *stream)
+{
+    return attention_common(q, cache, b, q_heads, past_len, rows, real_rows, scale, out,
+                            (hipStream_t)stream);
+}
+
+int cpk_rewind(const cpk_kv_cache *cache, int b, int new_len, int cur_len, void *stream)
+{
+    int r = check_cache(cache);
+    if (r) return r;
+    if (b < 0 || b >= cache->batch) return fail(CPK_EINVAL, "rewind: b=%d out of range", b);
+    if (new_len < 0 || new_len > cur_len || cur_len > cache->capacity)
+        return fail(CPK_EINVAL, "rewind: new_len=%d cur_len=%d", new_len, cur_len);
+    return hip_status(cpk::launch_set_len(cache->seqlens_k, b, new_len, (hipStream_t)stream),
+                      "rewind launch");
+}
+
+int cpk_prefill_chunk(const void *q, const void *k, const void *v, const cpk_kv_cache *cache,
+                      int b, int q_heads, int past_len, int real_rows, int W, int pad,
+                      float scale, void *out, int *issued_rows, void *stream)
+{
+    int r = check_cache(cache);
+    if (r) return r;
+    if (W < 1 || real_rows < 1 || real_rows > W)
+        return fail(CPK_EINVAL, "prefill_chunk: real_rows=%d outside [1, W=%d]", real_rows, W);
+    if (!k || !v) return fail(CPK_EINVAL, "prefill_chunk: NULL k/v");
+    if (!aligned16(k) || !aligned16(v)) return fail(CPK_EALIGN, "prefill_chunk: k/v not aligned");
+    const int width = pad ? ladder_width_impl(W, real_rows) : real_rows;
+    // validate everything the three launches need before the first one
+    if ((r = check_heads(q_heads, cache->kv_heads))) return r;
+    if (b < 0 || b >= cache->batch) return fail(CPK_EINVAL, "prefill_chunk: b=%d out of range", b);
+    if (!q || !out) return fail(CPK_EINVAL, "prefill_chunk: NULL q/out");
+    if (!aligned16(q) || !aligned16(out)) return fail(CPK_EALIGN, "prefill_chunk: q/out not aligned");
+    if (past_len < 0) return fail(CPK_EINVAL, "prefill_chunk: past_len=%d", past_len);
+    if ((int64_t)past_len + width > cache->capacity)
+        return fail(CPK_ECAPACITY, "prefill_chunk: %d + %d padded rows exceed capacity %d",
+                    past_len, width, cache->capacity);
+    hipStream_t st = (hipStream_t)stream;
+    const int rb = cache->head_dim * elem_size(cache->dtype);
+    r = hip_status(cpk::launch_kv_append(k, v, cache->k, cache->v, cache->seqlens_k,
+                                         cache->kv_heads, cache->capacity, rb, b, past_len, width,
+                                         real_rows, st),
+                   "prefill_chunk append");
+    if (r) return r;
+    r = attention_common(q, cache, b, q_heads, past_len, width, real_rows, scale, out, st);
+    if (r) return r;
+    r = hip_status(cpk::launch_set_len(cache->seqlens_k, b, past_len + real_rows, st),
+                   "prefill_chunk rewind");
+    if (r) return r;
+    if (issued_rows) *issued_rows = width;
+    return ok();
+}
+
+size_t cpk_varlen_workspace_size(int n_seqs, int q_heads, int max_ctx, int head_dim)
+{
+    if (n_seqs < 1 || q_heads < 1 || head_dim < 1) return 0;
+    const int segs = max_ctx < 1 ? 1 : (max_ctx + cpk::kDecodeSeg - 1) / cpk::kDecodeSeg;
+    return (size_t)n_seqs * (size_t)q_heads * (size_t)segs * (size_t)(head_dim + 4) * sizeof(float);
+}
+
+int cpk_varlen_step(const void *q, const void *k_new, const void *v_new,
+                    const cpk_kv_cache *cache, const int32_t *slots, const int32_t *cu_rows,
+                    const int32_t *past_lens, const int32_t *h_slots, const int32_t *h_cu_rows,
+                    const int32_t *h_past_lens, int n_seqs, int total_rows, int q_heads,
+                    float scale, void *out, void *ws, size_t ws_bytes, void *stream)
+{
+    int r = check_cache(cache);
+    if (r) return r;
+    if ((r = check_heads(q_heads, cache->kv_heads))) return r;
+    if (n_seqs < 1 || total_rows < 1) return fail(CPK_EINVAL, "varlen: n_seqs=%d total_rows=%d", n_seqs, total_rows);
+    if (!q || !k_new || !v_new || !out || !slots || !cu_rows || !past_lens || !h_slots ||
+        !h_cu_rows || !h_past_lens)
+        return fail(CPK_EINVAL, "varlen: NULL argument");
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+        return fail(CPK_EALIGN, "varlen: q/k/v/out not aligned");
+    if (h_cu_rows[0] != 0 || h_cu_rows[n_seqs] != total_rows)
+        return fail(CPK_EINVAL, "varlen: cu_rows must run from 0 to total_rows");
+    std::vector<char> used((size_t)cache->batch, 0);
+    int max_ctx = 0, max_rows = 0, n_dec = 0, n_pre = 0;
+    const int G = q_heads / cache->kv_heads;
+    const bool dec_ok = cpk::decode_supported(cache->dtype, cache->head_dim, G);
+    for (int s = 0; s < n_seqs; ++s) {
+        const int rows = h_cu_rows[s + 1] - h_cu_rows[s];
+        if (rows < 1) return fail(CPK_EINVAL, "varlen: sequence %d has %d rows", s, rows);
+        const int slot = h_slots[s];
+        if (slot < 0 || slot >= cache->batch) return fail(CPK_EINVAL, "varlen: slot %d out of range", slot);
+        if (used[(size_t)slot]) return fail(CPK_EINVAL, "varlen: slot %d used twice", slot);
+        used[(size_t)slot] = 1;
+        const int past = h_past_lens[s];
+        if (past < 0) return fail(CPK_EINVAL, "varlen: past_len %d", past);
+        if ((int64_t)past + rows > cache->capacity)
+            return fail(CPK_ECAPACITY, "varlen: sequence %d needs %d positions, capacity %d", s,
+                        past + rows, cache->capacity);
+        if (rows == 1 && dec_ok) {
+            ++n_dec;
+            if (past + 1 > max_ctx) max_ctx = past + 1;
+        } else {
+            ++n_pre;
+            if (rows > max_rows) max_rows = rows;
+        }
+    }
+    const int max_segs = (max_ctx + cpk::kDecodeSeg - 1) / cpk::kDecodeSeg;
+    if (n_dec > 0) {
+        const size_t need = cpk_varlen_workspace_size(n_seqs, q_heads, max_ctx, cache->head_dim);
+        if (!ws || ws_bytes < need)
+            return fail(CPK_EWORKSPACE, "varlen: workspace %zu bytes, need %zu", ws_bytes, need);
+        if (!aligned16(ws)) return fail(CPK_EALIGN, "varlen: workspace not aligned");
+    }
+    hipStream_t st = (hipStream_t)stream;
+    const int rb = cache->head_dim * elem_size(cache->dtype);
+    r = hip_status(cpk::launch_kv_append_varlen(k_new, v_new, cache->k, cache->v, cache->seqlens_k,
+                                                cache->kv_heads, cache->capacity, rb, cu_rows,
+                                                past_lens, slots, n_seqs, total_rows, st),
+                   "varlen append");
+    if (r) return r;
+    const float sc = resolve_scale(scale, cache->head_dim);
+    if (n_dec > 0) {
+        cpk::DecodeArgs d = {};
+        d.q = q; d.k = cache->k; d.v = cache->v; d.out = out; d.ws = (float *)ws;
+        d.Hq = q_heads; d.Hkv = cache->kv_heads; d.D = cache->head_dim; d.cap = cache->capacity;
+        d.scale_log2 = (float)((double)sc * 1.4426950408889634);
+        d.max_segs = max_segs;
+        d.cu_rows = cu_rows; d.past_lens = past_lens; d.slots = slots; d.n_seqs = n_seqs;
+        r = hip_status(cpk::launch_decode(d, cache->dtype, max_segs, st), "varlen decode");
+        if (r) return r;
+    }
+    if (n_pre > 0) {
+        cpk::AttnArgs a = {};
+        a.q = q; a.k = cache->k; a.v = cache->v; a.out = out; a.mask = nullptr;
+        a.Hq = q_heads; a.Hkv = cache->kv_heads; a.D = cache->head_dim; a.cap = cache->capacity;
+        fill_scale(a, sc);
+        a.varlen = 1; a.cu_rows = cu_rows; a.past_lens = past_lens; a.slots = slots;
+        a.n_seqs = n_seqs; a.min_rows = dec_ok ? 2 : 1;
+        const int br = cpk::attn_rows_per_block(cache->dtype, G);
+        r = hip_status(cpk::launch_attention(a, cache->dtype, (max_rows + br - 1) / br, n_seqs, st),
+                       "varlen prefill");
+        if (r) return r;
+    }
+    return ok();
+}
+
+int cpk_roll_append(const void *k_old, const void *v_old, const void *k_chunk,
+                    const void *v_chunk, void *k_new, void *v_new, int B, int H, int C, int c,
+                    int D, int dtype, void *stream)
+{
+    int r = check_dtype_dim(dtype, D);
+    if (r) return r;
+    if (B < 1 || H < 1 || C < 1 || c < 1 || c > C)
+        return fail(CPK_EINVAL, "roll_append: B=%d H=%d C=%d c=%d", B, H, C, c);
+    if (!k_old || !v_old || !k_chunk || !v_chunk || !k_new || !v_new)
+        return fail(CPK_EINVAL, "roll_append: NULL buffer");
+    if (!aligned16(k_old) || !aligned16(v_old) || !aligned16(k_chunk) || !aligned16(v_chunk) ||
+        !aligned16(k_new) || !aligned16(v_new))
+        return fail(CPK_EALIGN, "roll_append: buffer not aligned");
+    const size_t cache_bytes = (size_t)B * H * C * D * elem_size(dtype);
+    const size_t chunk_bytes = (size_t)B * H * c * D * elem_size(dtype);
+    const void *srcs[4] = {k_old, v_old, k_chunk, v_chunk};
+    const size_t sz[4] = {cache_bytes, cache_bytes, chunk_bytes, chunk_bytes};
+    for (int i = 0; i < 4; ++i)
+        if (overlaps(srcs[i], sz[i], k_new, cache_bytes) || overlaps(srcs[i], sz[i], v_new, cache_bytes))
+            return fail(CPK_EINVAL, "roll_append: output overlaps an input");
+    if (overlaps(k_new, cache_bytes, v_new, cache_bytes))
+        return fail(CPK_EINVAL, "roll_append: k_new and v_new overlap");
+    return hip_status(cpk::launch_roll_append(k_old, v_old, k_chunk, v_chunk, k_new, v_new, B, H,
+                                              C, c, D * elem_size(dtype), (hipStream_t)stream),
+                      "roll_append launch");
+}
+
+int cpk_roll_attention(const void *q, const void *k, const void *v, const void *mask,
+                       int abs_end, int n_leftpad, int Hq, int Hkv, int C, int c, int D,
+                       int dtype, float scale, void *out, void *stream)
+{
+    int r = check_dtype_dim(dtype, D);
+    if (r) return r;
+    if ((r = check_heads(Hq, Hkv))) return r;
+    if (C < 1 || c < 1 || c > C || abs_end < c || n_leftpad < 0)
+        return fail(CPK_EINVAL, "roll_attention: C=%d c=%d abs_end=%d n_leftpad=%d", C, c, abs_end,
+                    n_leftpad);
+    if (!q || !k || !v || !out) return fail(CPK_EINVAL, "roll_attention: NULL buffer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(CPK_EALIGN, "roll_attention: buffer not aligned");
+    if (mask && ((uintptr_t)mask & 3u)) return fail(CPK_EALIGN, "roll_attention: mask not aligned");
+    cpk::AttnArgs a = {};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.mask = mask;
+    a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.cap = C; a.mask_ld = C;
+    fill_scale(a, resolve_scale(scale, D));
+    a.slot = 0; a.q_row0 = 0; a.out_row0 = 0; a.rows = c; a.q_src_rows = c; a.out_rows = c;
+    a.n_keys = C;
+    if (mask) {
+        // the additive mask decides visibility over every slot
+        a.key_lo = 0;
+        a.causal_base = C - 1;
+    } else {
+        // slot s holds position abs_end - C + s; visible iff
+        // n_leftpad <= position <= abs_end - c + i
+        const int64_t lo = (int64_t)n_leftpad - ((int64_t)abs_end - C);
+        a.key_lo = lo < 0 ? 0 : (lo > C ? C : (int)lo);
+        a.causal_base = C - c;
+    }
+    const int br = cpk::attn_rows_per_block(dtype, Hq / Hkv);
+    return hip_status(cpk::launch_attention(a, dtype, (c + br - 1) / br, 1, (hipStream_t)stream),
+                      "roll_attention launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal declarations shared by the HIP kernels and the C-ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpk {
+
+// One attention launch: a chunk of query rows of one sequence (scalar mode)
+// or of every sequence of a packed step (varlen mode), over keys read from a
+// [batch][kv_heads][cap][D] cache.
+//
+// Query row i of a sequence sits at causal position causal_base + i and sees
+// key j iff  key_lo <= j <= causal_base + i  and  j < n_keys.  Optionally an
+// additive mask [rows][mask_ld] (same dtype as q) is added to the scaled
+// scores instead (rolling cache form).
+struct AttnArgs {
+    const void *q;      // token-major [*, Hq, D]; the sequence's rows start at q_row0
+    const void *k;      // cache [batch][Hkv][cap][D]
+    const void *v;
+    void *out;          // token-major [*, Hq, D]; rows start at out_row0
+    const void *mask;   // optional additive mask [rows][mask_ld]
+    int Hq, Hkv, D;
+    int cap;            // positions per (slot, head) in k / v
+    int mask_ld;
+    float scale;        // softmax scale
+    float scale_log2;   // scale * log2(e)
+
+    // scalar mode (varlen == 0)
+    int slot;           // cache batch index
+    int q_row0, out_row0;
+    int rows;           // issued rows (padded width)
+    int q_src_rows;     // rows present in q: pad rows repeat row q_src_rows - 1
+    int out_rows;       // rows written to out
+    int n_keys;         // keys [0, n_keys) exist for this call
+    int key_lo;         // keys below key_lo are invisible
+    int causal_base;    // row i sees keys <= causal_base + i
+
+    // varlen mode: per-sequence device arrays (rows of sequence s are
+    // cu_rows[s] .. cu_rows[s+1], its cache slot slots[s], its cached length
+    // past_lens[s]); sequences with fewer than min_rows rows are skipped.
+    int varlen;
+    const int32_t *cu_rows;
+    const int32_t *past_lens;
+    const int32_t *slots;
+    int n_seqs;
+    int min_rows;
+};
+
+// Split-KV decode: one query row per sequence.
+struct DecodeArgs {
+    const void *q;      // token-major [*, Hq, D]
+    const void *k;      // cache
+    const void *v;
+    void *out;
+    float *ws;          // partials [n_seqs][Hq][max_segs][D + 2] (m, l, acc[D])
+    int Hq, Hkv, D, cap;
+    float scale_log2;
+    int max_segs;       // segments allocated per (seq, head) in ws
+    // varlen arrays (a sequence takes part iff it has exactly one row)
+    const int32_t *cu_rows;
+    const int32_t *past_lens;
+    const int32_t *slots;
+    int n_seqs;
+};
+
+constexpr int kDecodeSeg = 256;   // keys per decode work item
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_kv_append(const void *k_new, const void *v_new, void *ck, void *cv,
+                            int32_t *seqlens, int Hkv, int cap, int row_bytes, int slot,
+                            int past, int rows, int src_rows, hipStream_t st);
+hipError_t launch_kv_append_varlen(const void *k_new, const void *v_new, void *ck, void *cv,
+                                   int32_t *seqlens, int Hkv, int cap, int row_bytes,
+                                   const int32_t *cu_rows, const int32_t *past_lens,
+                                   const int32_t *slots, int n_seqs, int total_rows,
+                                   hipStream_t st);
+hipError_t launch_set_len(int32_t *seqlens, int b, int len, hipStream_t st);
+hipError_t launch_roll_append(const void *k_old, const void *v_old, const void *k_chunk,
+                              const void *v_chunk, void *k_new, void *v_new, int B, int H,
+                              int C, int c, int row_bytes, hipStream_t st);
+
+// Attention: grid.x = row blocks, grid.y = KV heads, grid.z = sequences.
+int attn_rows_per_block(int dtype, int group);
+hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
+                            hipStream_t st);
+
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int max_segs, hipStream_t st);
+bool decode_supported(int dtype, int D, int group);
+
+}  // namespace cpk

@@ -1,0 +1,573 @@
+// Chunk attention over a KV cache: flash-style tiled attention with online
+// softmax for gfx950.
+//
+// What is computed (per query row at causal position p, query head h, KV
+// head g = h / G): softmax(scale * q k_j) over the visible keys j, times v_j.
+// Visibility is the causal rule over absolute positions (ONNX GenAI Wiki
+// "Chunked Prefill", section 1.2), so a chunk sees exactly what one-shot
+// prefill sees; the rolling-cache form adds a lower bound or an additive
+// mask (Horizon developer blog "Chunk Prefill", section 4).
+//
+// bf16 / fp16 kernel (attn_mfma_kernel)
+// -------------------------------------
+// * Work item: 64 "query columns" = G query heads x (64/G) rows that share
+//   one KV head, so every K/V tile staged in LDS serves the whole GQA group.
+// * K/V tiles of 128 keys, double-buffered in LDS: K row-major [key][d],
+//   V transposed [d][key] so that both MFMA contractions read 16-byte
+//   fragments.  Tiles are aligned to absolute key 0, so a query row visits
+//   the same tile sequence whether its prompt runs in one pass or in chunks.
+// * Each of the 4 waves owns 32 keys of every tile and keeps its own online
+//   softmax state for all 64 query columns; the 4 states are merged once at
+//   the end through LDS (an in-workgroup split of the key range).
+// * Scores are computed transposed, S^T = K Q^T, with
+//   v_mfma_f32_32x32x16_{bf16,f16}: a lane then holds one query column and
+//   16 keys, so the row max is 15 in-lane max operations plus one
+//   permlane32 swap, and the probabilities are already in the B-operand
+//   layout of O^T = V^T P^T.
+// * Online softmax in the exp2 domain (scale * log2 e folded into one FMA).
+//   The running maximum is only raised when a tile's maximum exceeds it by
+//   more than 2^8; otherwise the stale maximum is kept (probabilities up to
+//   256, exact after the final normalisation).  This removes almost every
+//   rescale of the 128 accumulator registers.
+// * Keys at or past n_keys are zero-filled in LDS and never read from the
+//   cache, so stale or poisoned bytes beyond the valid length cannot leak.
+//
+// fp32 kernel (attn_f32_kernel): one query column per lane, VALU FMAs in
+// fp32 with an exact per-tile rescale.  Full precision, no reduced-precision
+// step; used where fp32 storage is requested.
+#include "cpk_internal.h"
+
+#include <hip/hip_bf16.h>
+#include <math.h>
+
+namespace cpk {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+struct Bf16 {
+    typedef bf16x8_t vec8;
+    static __device__ __forceinline__ f32x16_t mfma(uint4 a, uint4 b, f32x16_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(vec8, a),
+                                                       __builtin_bit_cast(vec8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float to_f32(uint32_t bits16)
+    {
+        return __uint_as_float(bits16 << 16);
+    }
+    static __device__ __forceinline__ uint32_t from_f32(float x)
+    {
+        return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+    }
+};
+
+struct F16 {
+    typedef f16x8_t vec8;
+    static __device__ __forceinline__ f32x16_t mfma(uint4 a, uint4 b, f32x16_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(vec8, a),
+                                                      __builtin_bit_cast(vec8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float to_f32(uint32_t bits16)
+    {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+    }
+    static __device__ __forceinline__ uint32_t from_f32(float x)
+    {
+        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+    }
+};
+
+constexpr int kQC = 64;         // query columns per workgroup
+constexpr int kBK = 128;        // keys per LDS tile
+constexpr int kThreads = 256;   // 4 waves
+constexpr float kLazyLog2 = 8.0f;
+
+// v_permlane32_swap exchanges the two 32-lane halves between its operands;
+// with the same value in both, {r[0], r[1]} is {own, partner} in some order
+// in every lane, so max() and + of the two are the pair max / pair sum, and
+// both halves obtain bit-identical results.
+__device__ __forceinline__ float pair_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                                    __builtin_bit_cast(int, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                                    __builtin_bit_cast(int, x), false, false);
+    return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+}
+
+__device__ __forceinline__ uint32_t dword(const uint4 &v, int j)
+{
+    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+// Position of key k inside a 16-key group of the transposed V tile: bits 2
+// and 3 swapped.  With it, the 8 probabilities a lane holds for one PV
+// k-step and the 8 V^T values it reads for that step are the same keys in
+// the same order (see the S^T accumulator layout below).
+__device__ __forceinline__ int swap23(int k)
+{
+    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+template <int D>
+struct Tile {
+    static constexpr int KS = D + 8;        // K row stride, elements (16-byte aligned rows)
+    static constexpr int VS = kBK + 8;      // V^T row stride
+    static constexpr int STAGE = kBK * KS + D * VS;   // uint16 elements per buffer
+    static constexpr int KPT = kBK * D / 8 / kThreads;   // keys staged per thread
+    static constexpr int NKG = kBK / KPT;   // key groups
+    static constexpr int OS = D + 4;        // epilogue row stride (floats)
+    static constexpr int LOOP_BYTES = 2 * STAGE * 2;
+    static constexpr int EPI_BYTES = (4 * kQC * OS + 2 * 4 * kQC) * 4;
+    static constexpr int BYTES = LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES;
+};
+
+struct SeqView {
+    int slot, q_row0, out_row0, rows, q_src_rows, out_rows, n_keys, key_lo, causal_base;
+};
+
+__device__ __forceinline__ bool resolve_seq(const AttnArgs &a, int z, SeqView &s)
+{
+    if (!a.varlen) {
+        s.slot = a.slot; s.q_row0 = a.q_row0; s.out_row0 = a.out_row0; s.rows = a.rows;
+        s.q_src_rows = a.q_src_rows; s.out_rows = a.out_rows; s.n_keys = a.n_keys;
+        s.key_lo = a.key_lo; s.causal_base = a.causal_base;
+        return true;
+    }
+    const int r0 = a.cu_rows[z], r1 = a.cu_rows[z + 1];
+    const int rows = r1 - r0;
+    if (rows < a.min_rows || rows <= 0) return false;
+    const int past = a.past_lens[z];
+    s.slot = a.slots[z]; s.q_row0 = r0; s.out_row0 = r0; s.rows = rows; s.q_src_rows = rows;
+    s.out_rows = rows; s.n_keys = past + rows; s.key_lo = 0; s.causal_base = past;
+    return true;
+}
+
+template <typename TR, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_mfma_kernel(AttnArgs a)
+{
+    using TL = Tile<D>;
+    constexpr int KPT = TL::KPT;
+    constexpr int NKG = TL::NKG;
+    constexpr int KS = TL::KS;
+    constexpr int VS = TL::VS;
+    constexpr int NS = D / 16;      // k-steps of the QK^T contraction
+    constexpr int NDB = D / 32;     // 32-wide d blocks of O^T
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[TL::BYTES / 2];
+
+    SeqView sv;
+    if (!resolve_seq(a, blockIdx.z, sv)) return;
+    const int G = a.Hq / a.Hkv;
+    const int BR = kQC / G;                 // rows per workgroup
+    const int r0 = blockIdx.x * BR;
+    if (r0 >= sv.rows) return;
+    const int g = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int c32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const uint16_t *qg = (const uint16_t *)a.q;
+    const uint16_t *kc = (const uint16_t *)a.k + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
+    const uint16_t *vc = (const uint16_t *)a.v + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
+
+    // ---- query fragments (B operand of S^T = K Q^T), one column per lane
+    uint4 qf[2][NS];
+    int lim[2];            // last visible key of this lane's column
+    int qrow[2];
+    bool qvalid[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qc = qb * 32 + c32;
+        const int row = r0 + qc / G;
+        const bool ok = (qc < BR * G) && (row < sv.rows);
+        const int rr = ok ? row : r0;
+        const int srow = rr < sv.q_src_rows ? rr : sv.q_src_rows - 1;
+        const int head = g * G + (ok ? qc % G : 0);
+        qrow[qb] = rr;
+        qvalid[qb] = ok;
+        lim[qb] = sv.causal_base + rr;
+        const uint16_t *qp = qg + ((int64_t)(sv.q_row0 + srow) * a.Hq + head) * D + 8 * hi;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qf[qb][s] = *(const uint4 *)(qp + 16 * s);
+    }
+
+    // ---- key range of this workgroup
+    const int last_row = min(r0 + BR, sv.rows) - 1;
+    const int key_end = min(sv.n_keys, sv.causal_base + last_row + 1);   // exclusive
+    const int t_first = sv.key_lo / kBK;
+    const int t_last = (key_end - 1) / kBK;
+
+    // ---- staging assignment: thread -> (key group, 8-element d chunk)
+    const int kg = tid % NKG;
+    const int dc = tid / NKG;
+    uint4 kreg[KPT], vreg[KPT];
+
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int key = kt * kBK + swap23(kg * KPT + i);
+            if (key < sv.n_keys) {
+                kreg[i] = *(const uint4 *)(kc + (int64_t)key * D + dc * 8);
+                vreg[i] = *(const uint4 *)(vc + (int64_t)key * D + dc * 8);
+            } else {
+                kreg[i] = make_uint4(0, 0, 0, 0);
+                vreg[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        uint16_t *Ks = smem + buf * TL::STAGE;
+        uint16_t *Vt = Ks + kBK * KS;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+            *(uint4 *)(Ks + swap23(kg * KPT + i) * KS + dc * 8) = kreg[i];
+        // transpose 8 d x KPT keys into V^T rows d = dc*8 + e
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint32_t w[KPT / 2];
+#pragma unroll
+            for (int i = 0; i < KPT / 2; ++i) {
+                const uint32_t a0 = (dword(vreg[2 * i], e >> 1) >> (16 * (e & 1))) & 0xffffu;
+                const uint32_t a1 = (dword(vreg[2 * i + 1], e >> 1) >> (16 * (e & 1))) & 0xffffu;
+                w[i] = a0 | (a1 << 16);
+            }
+            uint16_t *dst = Vt + (dc * 8 + e) * VS + kg * KPT;
+            if constexpr (KPT == 8)
+                *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
+            else
+                *(uint2 *)dst = make_uint2(w[0], w[1]);
+        }
+    };
+
+    // ---- accumulators
+    f32x16_t oacc[2][NDB];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[qb][db][j] = 0.f;
+    float m_run[2] = {-INFINITY, -INFINITY};
+    float l_run[2] = {0.f, 0.f};
+    const float c = a.scale_log2;
+    const float inv_scale = 1.0f / a.scale;
+    const uint16_t *maskp = (const uint16_t *)a.mask;
+
+    if (t_last >= t_first) {
+        load_tile(t_first);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int kt = t_first; kt <= t_last; ++kt) {
+        const int buf = (kt - t_first) & 1;
+        const bool more = kt < t_last;
+        if (more) load_tile(kt + 1);
+
+        const uint16_t *Ks = smem + buf * TL::STAGE;
+        const uint16_t *Vt = Ks + kBK * KS;
+
+        // S^T[32 keys x 64 cols] for this wave's keys
+        f32x16_t sacc[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) sacc[qb][j] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint4 ka = *(const uint4 *)(Ks + (wave * 32 + c32) * KS + 16 * s + 8 * hi);
+            sacc[0] = TR::mfma(ka, qf[0][s], sacc[0]);
+            sacc[1] = TR::mfma(ka, qf[1][s], sacc[1]);
+        }
+
+        // Accumulator register j of lane (c32, hi) holds key
+        // kbase + 8*(j/4) + 4*hi + (j%4) for query column c32 (+32*qb).
+        const int kbase = kt * kBK + wave * 32;
+        const bool full = (kt * kBK >= sv.key_lo) && ((kt + 1) * kBK <= sv.n_keys) &&
+                          ((kt + 1) * kBK - 1 <= sv.causal_base + r0);
+        if (maskp) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const uint16_t *mrow = maskp + (int64_t)qrow[qb] * a.mask_ld;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
+                    const float mv = key < sv.n_keys ? TR::to_f32(mrow[key]) : 0.f;
+                    const bool vis = key >= sv.key_lo && key < sv.n_keys;
+                    sacc[qb][j] = vis ? sacc[qb][j] + mv * inv_scale : -INFINITY;
+                }
+            }
+        } else if (!full) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
+                    const bool vis = key >= sv.key_lo && key <= lim[qb] && key < sv.n_keys;
+                    sacc[qb][j] = vis ? sacc[qb][j] : -INFINITY;
+                }
+        }
+
+        // online softmax (exp2 domain), lazy maximum
+        uint4 pb[2][2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float mx = sacc[qb][0];
+#pragma unroll
+            for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[qb][j]);
+            mx = pair_max(mx);
+            const float mt = mx * c;
+            const bool need = mt > m_run[qb] + kLazyLog2;
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                const float alpha = need ? exp2f(m_run[qb] - mt) : 1.0f;
+                m_run[qb] = need ? mt : m_run[qb];
+                l_run[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) oacc[qb][db][j] *= alpha;
+            }
+            const float mu = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+            float p[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][j], c, -mu));
+                l_run[qb] += p[j];
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    w[i] = TR::from_f32(p[8 * s2 + 2 * i]) |
+                           (TR::from_f32(p[8 * s2 + 2 * i + 1]) << 16);
+                pb[qb][s2] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+
+        // O^T[d x cols] += V^T[d x 32 keys] P^T[32 keys x cols]
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const uint4 va =
+                    *(const uint4 *)(Vt + (db * 32 + c32) * VS + wave * 32 + 16 * s2 + 8 * hi);
+                oacc[0][db] = TR::mfma(va, pb[0][s2], oacc[0][db]);
+                oacc[1][db] = TR::mfma(va, pb[1][s2], oacc[1][db]);
+            }
+
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- merge the four waves' partial states, normalise, write rows
+    float *Ms = (float *)smem;
+    float *Ls = Ms + 4 * kQC;
+    float *Os = Ls + 4 * kQC;
+    constexpr int OS = TL::OS;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const float lt = pair_sum(l_run[qb]);
+        if (hi == 0) {
+            Ms[wave * kQC + qb * 32 + c32] = m_run[qb];
+            Ls[wave * kQC + qb * 32 + c32] = lt;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qc = qb * 32 + c32;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, Ms[w * kQC + qc]);
+        float den = 0.f, mine = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float mw = Ms[w * kQC + qc];
+            const float e = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+            den += e * Ls[w * kQC + qc];
+            if (w == wave) mine = e;
+        }
+        const float f = den > 0.f ? mine / den : 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const int d = db * 32 + 8 * j4 + 4 * hi;
+                float4 v4 = make_float4(oacc[qb][db][4 * j4] * f, oacc[qb][db][4 * j4 + 1] * f,
+                                        oacc[qb][db][4 * j4 + 2] * f, oacc[qb][db][4 * j4 + 3] * f);
+                *(float4 *)(Os + (wave * kQC + qc) * OS + d) = v4;
+            }
+    }
+    __syncthreads();
+    {
+        const int qc = tid >> 2;
+        const int part = tid & 3;
+        const int row = r0 + qc / G;
+        if (qc < BR * G && row < sv.out_rows) {
+            const int head = g * G + qc % G;
+            uint16_t *op = (uint16_t *)a.out + ((int64_t)(sv.out_row0 + row) * a.Hq + head) * D +
+                           part * (D / 4);
+#pragma unroll
+            for (int d8 = 0; d8 < D / 4; d8 += 8) {
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x0 = 0.f, x1 = 0.f;
+                    const int d = part * (D / 4) + d8 + 2 * i;
+#pragma unroll
+                    for (int w4 = 0; w4 < 4; ++w4) {
+                        x0 += Os[(w4 * kQC + qc) * OS + d];
+                        x1 += Os[(w4 * kQC + qc) * OS + d + 1];
+                    }
+                    w[i] = TR::from_f32(x0) | (TR::from_f32(x1) << 16);
+                }
+                *(uint4 *)(op + d8) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ fp32
+
+constexpr int kF32Keys = 32;
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a)
+{
+    __shared__ float Ks[kF32Keys][D];
+    __shared__ float Vs[kF32Keys][D];
+    __shared__ float Qs[kQC][D + 1];
+
+    SeqView sv;
+    if (!resolve_seq(a, blockIdx.z, sv)) return;
+    const int G = a.Hq / a.Hkv;
+    const int BR = kQC / G;
+    const int r0 = blockIdx.x * BR;
+    if (r0 >= sv.rows) return;
+    const int g = blockIdx.y;
+    const int t = threadIdx.x;
+
+    const int row = r0 + t / G;
+    const bool ok = (t < BR * G) && (row < sv.rows);
+    const int rr = ok ? row : r0;
+    const int srow = rr < sv.q_src_rows ? rr : sv.q_src_rows - 1;
+    const int head = g * G + (ok ? t % G : 0);
+    const int lim = sv.causal_base + rr;
+    const float *qp = (const float *)a.q + ((int64_t)(sv.q_row0 + srow) * a.Hq + head) * D;
+    for (int d = 0; d < D; ++d) Qs[t][d] = qp[d];
+
+    const float *kc = (const float *)a.k + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
+    const float *vc = (const float *)a.v + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
+    const float *maskp = (const float *)a.mask;
+
+    const int last_row = min(r0 + BR, sv.rows) - 1;
+    const int key_end = min(sv.n_keys, sv.causal_base + last_row + 1);
+    const int t_first = sv.key_lo / kF32Keys;
+    const int t_last = (key_end - 1) / kF32Keys;
+
+    float acc[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = 0.f;
+    float m = -INFINITY, l = 0.f;
+
+    for (int kt = t_first; kt <= t_last; ++kt) {
+        __syncthreads();
+        for (int i = t; i < kF32Keys * D / 4; i += 64) {
+            const int kk = i / (D / 4), d4 = i % (D / 4);
+            const int key = kt * kF32Keys + kk;
+            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+            if (key < sv.n_keys) {
+                kv = *(const float4 *)(kc + (int64_t)key * D + 4 * d4);
+                vv = *(const float4 *)(vc + (int64_t)key * D + 4 * d4);
+            }
+            *(float4 *)&Ks[kk][4 * d4] = kv;
+            *(float4 *)&Vs[kk][4 * d4] = vv;
+        }
+        __syncthreads();
+        float s[kF32Keys];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kk = 0; kk < kF32Keys; ++kk) {
+            const int key = kt * kF32Keys + kk;
+            bool vis = key >= sv.key_lo && key < sv.n_keys && (maskp || key <= lim);
+            float dot = 0.f;
+            for (int d = 0; d < D; ++d) dot = fmaf(Qs[t][d], Ks[kk][d], dot);
+            float sc = dot * a.scale;
+            if (maskp && vis) sc += maskp[(int64_t)rr * a.mask_ld + key];
+            s[kk] = vis ? sc : -INFINITY;
+            tmax = fmaxf(tmax, s[kk]);
+        }
+        const float mn = fmaxf(m, tmax);
+        if (mn != -INFINITY) {
+            const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
+            if (alpha != 1.f) {
+                l *= alpha;
+#pragma unroll
+                for (int d = 0; d < D; ++d) acc[d] *= alpha;
+            }
+            m = mn;
+#pragma unroll
+            for (int kk = 0; kk < kF32Keys; ++kk) {
+                const float p = (s[kk] == -INFINITY) ? 0.f : expf(s[kk] - m);
+                l += p;
+#pragma unroll
+                for (int d = 0; d < D; ++d) acc[d] = fmaf(p, Vs[kk][d], acc[d]);
+            }
+        }
+    }
+    if (ok && row < sv.out_rows) {
+        float *op = (float *)a.out + ((int64_t)(sv.out_row0 + row) * a.Hq + head) * D;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int d = 0; d < D; d += 4)
+            *(float4 *)(op + d) =
+                make_float4(acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv);
+    }
+}
+
+}  // namespace
+
+int attn_rows_per_block(int dtype, int group)
+{
+    (void)dtype;
+    return kQC / group;
+}
+
+hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
+                            hipStream_t st)
+{
+    const dim3 grid(row_blocks, a.Hkv, n_seq_grid);
+    if (dtype == 0) {
+        if (a.D == 64)
+            hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, st, a);
+        else
+            hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, st, a);
+    } else if (dtype == 1) {
+        if (a.D == 64)
+            hipLaunchKernelGGL((attn_mfma_kernel<F16, 64>), grid, dim3(kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((attn_mfma_kernel<F16, 128>), grid, dim3(kThreads), 0, st, a);
+    } else {
+        if (a.D == 64)
+            hipLaunchKernelGGL((attn_mfma_kernel<Bf16, 64>), grid, dim3(kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((attn_mfma_kernel<Bf16, 128>), grid, dim3(kThreads), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace cpk

@@ -1,0 +1,253 @@
+/*
+ * cpk.h -- C ABI of the chunked-prefill causal-attention library for AMD
+ * MI355X (gfx950).
+ *
+ * A chunk of `rows` query rows at absolute positions [past_len,
+ * past_len + rows) attends causally over every cached key/value in
+ * [0, past_len + rows); its own K/V are appended to a cache bound at
+ * physical capacity first.  Chunked prefill is exact: its visible set per
+ * query equals one-shot prefill's (ONNX GenAI Wiki "Chunked Prefill",
+ * section 1: 1.1 append-only cache, 1.2 causal mask, 1.3 capacity kept
+ * apart from length).
+ *
+ * Conventions shared by every call:
+ *  - Return value: CPK_OK (0) or a negative CPK_E* status.  No exception or
+ *    abort crosses the ABI.  cpk_last_error() gives a message for the last
+ *    failing call on the calling thread.
+ *  - Validation runs on the host before anything is launched; on error no
+ *    device memory is written.
+ *  - Ownership: the caller owns every device buffer (cache, seqlens_k,
+ *    inputs, outputs, workspace).  The library allocates no device memory.
+ *  - Streams: every device call is asynchronous on the caller's stream
+ *    (`stream` is a hipStream_t passed as void*; NULL is the default
+ *    stream).  No call synchronises the host.
+ *  - Layouts: token-major q / out / new K/V rows are [rows, heads, D]
+ *    contiguous; caches are [batch, kv_heads, capacity, D] contiguous.
+ *    Device pointers must be 16-byte aligned.
+ *  - Dtypes: CPK_F32, CPK_F16, CPK_BF16; q, K/V, masks and outputs of one
+ *    call share one dtype.  Accumulation is fp32.
+ *  - Head dims: 64 or 128.  q_heads must be a multiple of kv_heads
+ *    (grouped-query attention with contiguous groups: query head h reads
+ *    KV head h / (q_heads / kv_heads)), with q_heads / kv_heads <= 64.
+ */
+#ifndef CPK_H
+#define CPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum cpk_status {
+    CPK_OK = 0,
+    CPK_EINVAL = -1,      /* bad size, index, flag or NULL pointer          */
+    CPK_EDTYPE = -2,      /* unsupported dtype / head-dim combination      */
+    CPK_ECAPACITY = -3,   /* positions past the cache's physical capacity  */
+    CPK_EALIGN = -4,      /* device pointer not 16-byte aligned            */
+    CPK_EWORKSPACE = -5,  /* workspace missing or too small                */
+    CPK_EHIP = -6,        /* the HIP runtime reported an error             */
+};
+
+enum cpk_dtype { CPK_F32 = 0, CPK_F16 = 1, CPK_BF16 = 2 };
+
+/*
+ * A KV cache bound at physical capacity, with the true number of valid
+ * positions per sequence carried beside it in seqlens_k (ONNX GenAI Wiki
+ * "Chunked Prefill", section 1.3).
+ *   k, v       device, [batch][kv_heads][capacity][head_dim] of dtype
+ *   seqlens_k  device, int32[batch]: valid positions (a count, not count-1)
+ */
+typedef struct cpk_kv_cache {
+    void *k;
+    void *v;
+    int32_t *seqlens_k;
+    int32_t batch;
+    int32_t kv_heads;
+    int32_t capacity;
+    int32_t head_dim;
+    int32_t dtype;
+} cpk_kv_cache;
+
+/* ------------------------------------------------------------ host logic */
+
+/*
+ * Query-axis padding ladder (ONNX GenAI Wiki "Chunked Prefill", sections 4
+ * and 6): three equally spaced widths at or below the chunk width W, the
+ * step rounded up so that the top rung is W itself -- {171, 342, 512} for
+ * W = 512.  Writes the distinct rungs in increasing order to out[0..*n).
+ * out must hold 3 ints.  CPK_EINVAL if W < 1 or a pointer is NULL.
+ */
+int cpk_ladder_rungs(int W, int *out, int *n);
+
+/*
+ * Smallest rung of the ladder of W that holds `rows` real rows; rows equal
+ * to a rung are not padded.  CPK_EINVAL if W < 1, rows < 1 or rows > W.
+ */
+int cpk_ladder_width(int W, int rows, int *width);
+
+/*
+ * Split an L-token prompt into W-row chunks, the last one taking the
+ * remainder (same page, sections 2 and 3): chunk i starts at past[i] and
+ * holds rows[i] rows.  max is the capacity of past/rows; *n receives the
+ * chunk count.  CPK_EINVAL if L < 0, W < 1 or max is too small.
+ */
+int cpk_split_chunks(int L, int W, int32_t *past, int32_t *rows, int max, int *n);
+
+/*
+ * Token-budget step rule (Ultralytics glossary "Chunked Prefill", section
+ * on how chunked prefill works): every running decode gets one row first,
+ * the waiting prompt fills what is left:
+ *   *prompt_rows = max(0, min(budget - n_decode, prompt_remaining)).
+ * CPK_EINVAL if an argument is negative or n_decode > budget.
+ */
+int cpk_plan_step(int budget, int n_decode, int prompt_remaining, int *prompt_rows);
+
+/* -------------------------------------------------------- device calls */
+
+/*
+ * Append `rows` positions to sequence b at [past_len, past_len + rows) from
+ * the token-major rows k_new/v_new [real_rows][kv_heads][head_dim], then set
+ * seqlens_k[b] = past_len + rows.  Positions past real_rows repeat the last
+ * real row (query-axis padding, ONNX GenAI Wiki "Chunked Prefill", section
+ * 4); real_rows == rows is a plain append.  Earlier positions are never
+ * touched (same page, section 1.1).  A byte copy.
+ * CPK_ECAPACITY if past_len + rows > capacity (a cache with no room left
+ * can be read but not written); CPK_EINVAL if real_rows < 1,
+ * real_rows > rows or b is out of range.
+ */
+int cpk_kv_append(const cpk_kv_cache *cache, int b, const void *k_new,
+                  const void *v_new, int past_len, int rows, int real_rows,
+                  void *stream);
+
+/*
+ * Causal attention of one chunk over sequence b's cache, which must already
+ * hold the chunk's own K/V (append first).
+ *   q    [real_rows][q_heads][head_dim].  `rows` rows are computed: row i
+ *        sits at absolute position past_len + i and sees keys
+ *        [0, past_len + i]; rows past real_rows repeat q's last row (the
+ *        padded rows of ONNX GenAI Wiki "Chunked Prefill", section 4).
+ *   out  [real_rows][q_heads][head_dim]: only the real rows are written
+ *        (truncation, same section); padded rows are discarded.
+ *   scale <= 0 selects 1/sqrt(head_dim).
+ * CPK_EINVAL if real_rows > rows, real_rows < 1 or q_heads is not a
+ * multiple of kv_heads; CPK_ECAPACITY if past_len + rows > capacity.
+ */
+int cpk_chunk_attention(const void *q, const cpk_kv_cache *cache, int b,
+                        int q_heads, int past_len, int rows, int real_rows,
+                        float scale, void *out, void *stream);
+
+/*
+ * Roll sequence b's logical length back to new_len (ONNX GenAI Wiki
+ * "Chunked Prefill", section 4): seqlens_k[b] = new_len.  Bytes past it
+ * are not cleared; the next append overwrites them.  cur_len is the
+ * caller's host copy of the current length.  CPK_EINVAL if new_len < 0 or
+ * new_len > cur_len.
+ */
+int cpk_rewind(const cpk_kv_cache *cache, int b, int new_len, int cur_len,
+               void *stream);
+
+/*
+ * One padded prefill forward in a single call (ONNX GenAI Wiki "Chunked
+ * Prefill", section 4): round real_rows up the ladder of W (pad != 0) or
+ * not (pad == 0, the page's switch that turns padding off); widen q, k and
+ * v by repeating their last real row; append every padded row; attend
+ * every padded row; write the real rows to out; rewind the cache to
+ * past_len + real_rows.  q [real_rows][q_heads][D], k/v
+ * [real_rows][kv_heads][D], out [real_rows][q_heads][D].  Equivalent to
+ * cpk_kv_append(rows = width) + cpk_chunk_attention(rows = width) +
+ * cpk_rewind(past_len + real_rows); the padding is an index clamp inside
+ * the kernels, so no scratch memory is used.
+ * *issued_rows (may be NULL) receives the padded width.
+ * CPK_EINVAL if real_rows < 1 or real_rows > W; CPK_ECAPACITY if the
+ * padded rows do not fit.
+ */
+int cpk_prefill_chunk(const void *q, const void *k, const void *v,
+                      const cpk_kv_cache *cache, int b, int q_heads,
+                      int past_len, int real_rows, int W, int pad, float scale,
+                      void *out, int *issued_rows, void *stream);
+
+/*
+ * Device workspace bytes cpk_varlen_step needs for a step of n_seqs
+ * sequences whose longest decode context (keys a one-row sequence reads)
+ * is max_ctx.
+ */
+size_t cpk_varlen_workspace_size(int n_seqs, int q_heads, int max_ctx,
+                                 int head_dim);
+
+/*
+ * One packed mixed step under a token budget (Ultralytics glossary
+ * "Chunked Prefill", section on how chunked prefill works): sequence s owns
+ * packed rows [cu_rows[s], cu_rows[s+1]) of q [total_rows][q_heads][D] and
+ * k_new/v_new [total_rows][kv_heads][D], sits in cache slot slots[s] and
+ * has past_lens[s] positions cached.  Every sequence appends its rows and
+ * attends them causally; a one-row sequence (a decode row) is computed by
+ * the split-KV decode path.  out is [total_rows][q_heads][D].
+ *   slots, cu_rows, past_lens   device int32 arrays (drive the kernels)
+ *   h_cu_rows, h_past_lens      host copies (validation, launch geometry)
+ *   ws / ws_bytes               device workspace, at least
+ *                               cpk_varlen_workspace_size(...) bytes
+ * Slots must be distinct.  CPK_ECAPACITY if a sequence's rows do not fit;
+ * CPK_EWORKSPACE if the workspace is too small.
+ */
+int cpk_varlen_step(const void *q, const void *k_new, const void *v_new,
+                    const cpk_kv_cache *cache, const int32_t *slots,
+                    const int32_t *cu_rows, const int32_t *past_lens,
+                    const int32_t *h_slots, const int32_t *h_cu_rows,
+                    const int32_t *h_past_lens, int n_seqs, int total_rows,
+                    int q_heads, float scale, void *out, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/*
+ * Rolling fixed-capacity cache step (Horizon developer blog "Chunk
+ * Prefill", section 3): new = cat(old, chunk)[c:] along positions, for K
+ * and V.  Out of place: k_new/v_new must not overlap k_old/v_old (the
+ * caller swaps buffers between chunks).
+ *   k_old, v_old, k_new, v_new   [B][H][C][D]
+ *   k_chunk, v_chunk             [B][c][H][D] token-major
+ * CPK_EINVAL if c < 1, c > C or the buffers overlap.
+ */
+int cpk_roll_append(const void *k_old, const void *v_old, const void *k_chunk,
+                    const void *v_chunk, void *k_new, void *v_new, int B,
+                    int H, int C, int c, int D, int dtype, void *stream);
+
+/*
+ * Attention of one chunk over a right-aligned rolling cache (Horizon
+ * developer blog "Chunk Prefill", section 4).  k, v [Hkv][C][D] hold
+ * absolute positions [abs_end - C, abs_end) right-aligned (slot s holds
+ * position abs_end - C + s); q [c][Hq][D] holds positions
+ * [abs_end - c, abs_end).  Slot s is visible to query row i iff its
+ * position a satisfies n_leftpad <= a <= abs_end - c + i.
+ *   mask  NULL: the rule above is evaluated in the kernel (masked slots
+ *         are skipped); or a (c, C) additive mask of the call's dtype
+ *         (0 visible, -32768 masked) added to the scaled scores.  For
+ *         every row that sees at least one slot both forms give the same
+ *         bits.
+ *   out   [c][Hq][D]
+ * CPK_EINVAL if c > C, abs_end < c or the sizes are inconsistent.
+ */
+int cpk_roll_attention(const void *q, const void *k, const void *v,
+                       const void *mask, int abs_end, int n_leftpad, int Hq,
+                       int Hkv, int C, int c, int D, int dtype, float scale,
+                       void *out, void *stream);
+
+/* ------------------------------------------------------------ diagnostics */
+
+/* Message for the last failing call on this thread ("" if none). */
+const char *cpk_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int cpk_version(void);
+
+/*
+ * Name and compute-unit count of the current HIP device.  name receives at
+ * most name_len bytes including the terminator.  CPK_EHIP if no device.
+ */
+int cpk_device_info(char *name, int name_len, int *compute_units);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPK_H */

@@ -79,6 +79,8 @@ def _load():
     if _lib is None:
         lib = ctypes.CDLL(build())
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.orc_num_threads.argtypes = []
+        lib.orc_num_threads.restype = I
         lib.orc_widen.argtypes = [P, I, I64, P]
         lib.orc_widen.restype = I
         lib.orc_attention.argtypes = [P, I, I, P, P, I, I, I, P, P, P, D, P]
@@ -89,6 +91,11 @@ def _load():
         lib.orc_roll_append.restype = I
         _lib = lib
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's loops use on this host."""
+    return int(_load().orc_num_threads())
 
 
 def _ptr(a: np.ndarray):

@@ -25,11 +25,15 @@
  * Parity pins for every function live in tests/test_oracle_pins.py.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+
+/* Threads the OpenMP loops use (reported beside the oracle's timings). */
+int orc_num_threads(void) { return omp_get_max_threads(); }
 
 /* IEEE binary16 -> double, exact (subnormals, inf and NaN included). */
 static double orc_half_to_double(uint16_t h)

@@ -1,0 +1,358 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Cache contents are compared byte for byte; outputs element by element
+within the stated tolerances (fp32 max-abs 1e-5, bf16 and fp16 max-abs
+2e-2), at sizes the oracle finishes in seconds and, at the workloads' full
+sizes, on sampled rows.  Bitwise self-checks of the GPU path (chunked ==
+one-shot, padded == unpadded, explicit mask == computed mask) guard the
+properties the pages state exactly.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import chunked_prefill_causal_kv_amd as cpk  # noqa: E402
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2, torch.float16: 2e-2}
+ODT = {torch.float32: oracle.F32, torch.bfloat16: oracle.BF16, torch.float16: oracle.F16}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+def check(gpu: torch.Tensor, ref: np.ndarray, tol: float, what: str):
+    g = f64(gpu)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    err = float(np.max(np.abs(g - ref))) if g.size else 0.0
+    say(f"  {what}: max-abs err {err:.3e} (tol {tol:g})")
+    assert err <= tol, f"{what}: max-abs {err} > {tol}"
+
+
+def bitwise(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.view(torch.int16) if a.element_size() == 2 else a.view(torch.int32),
+                       b.view(torch.int16) if b.element_size() == 2 else b.view(torch.int32))
+
+
+def sample_rows(L, chunks, every=13):
+    rows = set(range(0, L, every))
+    for past, r in chunks:
+        rows.update(range(past, min(past + 4, L)))
+        rows.update(range(max(past, past + r - 4), past + r))
+    return np.array(sorted(rows))
+
+
+def oracle_rows(q, k, v, rows_idx, dtype):
+    """One-shot causal oracle at selected absolute rows (token-major raw
+    storage arrays of the whole prompt)."""
+    L, Hq, D = q.shape
+    n_keys = int(rows_idx.max()) + 1
+    qq = oracle.widen(np.ascontiguousarray(q[rows_idx]), dtype)
+    kk = oracle.widen(np.ascontiguousarray(k[:n_keys].transpose(1, 0, 2)), dtype)
+    vv = oracle.widen(np.ascontiguousarray(v[:n_keys].transpose(1, 0, 2)), dtype)
+    lo = np.zeros(len(rows_idx), np.int32)
+    return oracle.attention(qq, kk, vv, lo, rows_idx.astype(np.int32), 1.0 / math.sqrt(D))
+
+
+def poison(cache: cpk.KVCache):
+    """Fill every cache byte with NaN (valid positions get written by
+    appends; a read past the valid length would surface as NaN)."""
+    cache.k.fill_(float("nan"))
+    cache.v.fill_(float("nan"))
+
+
+# -------------------------------------------------------------- append
+
+def test_kv_append_bit_exact():
+    say("case: kv_append bf16 [2,8,1024,128], 700 rows in 3 chunks at b=1")
+    q, k, v = si.gqa_prompt(L=700, Hq=32, Hkv=8, D=128, seed=101)
+    cache = cpk.KVCache(2, 8, 1024, 128, torch.bfloat16)
+    poison(cache)
+    ref = oracle.Cache(oracle.BF16, 2, 8, 1024, 128)
+    kd, vd = k.cuda(), v.cuda()
+    ks, vs = si.storage(k), si.storage(v)
+    for past, rows in cpk.cpk_split_chunks(700, 256):
+        cpk.cpk_kv_append(cache, 1, kd[past:past + rows], vd[past:past + rows], past)
+        ref.append(1, ks[past:past + rows], vs[past:past + rows], past)
+    torch.cuda.synchronize()
+    assert int(cache.seqlens_k[1]) == 700 and int(cache.seqlens_k[0]) == 0
+    gk = si.storage(cache.k[1, :, :700])
+    gv = si.storage(cache.v[1, :, :700])
+    assert np.array_equal(gk, ref.k[1, :, :700]) and np.array_equal(gv, ref.v[1, :, :700])
+    # the other sequence was not touched (still the NaN poison)
+    assert torch.isnan(cache.k[0]).all()
+
+
+# ------------------------------------------------------ workload 1: fp32 demo
+
+def test_fp32_demo_chunked_and_one_shot():
+    say("case: fp32 demo L=1000 H=8 D=64 chunk 256, cap 1024")
+    _, (qt, kt, vt) = si.demo_qkv()
+    qs, ks, vs = (si.storage(x) for x in (qt, kt, vt))
+    ref = oracle.prefill_one_shot(oracle.Cache(oracle.F32, 1, 8, 1024, 64), 0, qs, ks, vs)
+    q, k, v = qt.cuda(), kt.cuda(), vt.cuda()
+    c1 = cpk.KVCache(1, 8, 1024, 64, torch.float32)
+    poison(c1)
+    out_c, widths = cpk.prefill_chunked(c1, 0, q, k, v, 256, pad=False)
+    assert widths == [256, 256, 256, 232]
+    c2 = cpk.KVCache(1, 8, 1024, 64, torch.float32)
+    cpk.cpk_kv_append(c2, 0, k, v, 0)
+    out_1 = cpk.cpk_chunk_attention(q, c2, 0, 0)
+    c3 = cpk.KVCache(1, 8, 1024, 64, torch.float32)
+    out_p, widths_p = cpk.prefill_chunked(c3, 0, q, k, v, 256, pad=True)
+    torch.cuda.synchronize()
+    assert widths_p == [256, 256, 256, 256]
+    check(out_c, ref, 1e-5, "chunked vs oracle")
+    check(out_1, ref, 1e-5, "one-shot vs oracle")
+    assert bitwise(out_c, out_1), "chunked != one-shot (bitwise)"
+    assert bitwise(out_c, out_p), "padded != unpadded (bitwise)"
+    assert int(c3.seqlens_k[0]) == 1000
+    assert np.array_equal(si.storage(c1.k[0, :, :1000]), ks.transpose(1, 0, 2))
+
+
+# ----------------------------------------------- GQA shapes, full compare
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,L,W", [
+    (torch.bfloat16, 8, 2, 128, 700, 256),
+    (torch.bfloat16, 16, 2, 64, 333, 128),
+    (torch.bfloat16, 4, 4, 128, 300, 200),
+    (torch.float16, 8, 2, 128, 450, 256),
+    (torch.bfloat16, 24, 8, 128, 260, 100),
+])
+def test_chunked_prefill_full_compare(dtype, Hq, Hkv, D, L, W):
+    say(f"case: chunked prefill {dtype} Hq={Hq} Hkv={Hkv} D={D} L={L} W={W}")
+    dn = {torch.bfloat16: "bf16", torch.float16: "f16"}[dtype]
+    q, k, v = si.gqa_prompt(L=L, Hq=Hq, Hkv=Hkv, D=D, dtype=dn, seed=7 + L)
+    qs, ks, vs = (si.storage(x) for x in (q, k, v))
+    cap = L + 64
+    ref = oracle.prefill_one_shot(oracle.Cache(ODT[dtype], 1, Hkv, cap, D), 0, qs, ks, vs)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    c1 = cpk.KVCache(1, Hkv, cap, D, dtype)
+    poison(c1)
+    out_c, widths = cpk.prefill_chunked(c1, 0, qd, kd, vd, W, pad=True)
+    c2 = cpk.KVCache(1, Hkv, cap, D, dtype)
+    poison(c2)
+    cpk.cpk_kv_append(c2, 0, kd, vd, 0)
+    out_1 = cpk.cpk_chunk_attention(qd, c2, 0, 0)
+    torch.cuda.synchronize()
+    say(f"  widths {widths}")
+    check(out_c, ref, TOL[dtype], "chunked vs oracle")
+    check(out_1, ref, TOL[dtype], "one-shot vs oracle")
+    same = bitwise(out_c, out_1)
+    say(f"  chunked == one-shot bitwise: {same}")
+    assert same
+    assert np.array_equal(si.storage(c1.k[0, :, :L]), ks.transpose(1, 0, 2))
+    assert np.array_equal(si.storage(c1.v[0, :, :L]), vs.transpose(1, 0, 2))
+
+
+# ---------------------------------------------- workload 2: GQA bf16 W=512
+
+def test_workload2_gqa_bf16_full_size():
+    say("case: workload 2 L=4000 Hq=32 Hkv=8 D=128 cap 8192 W=512 (sampled rows)")
+    q, k, v = si.gqa_prompt()
+    qs, ks, vs = (si.storage(x) for x in (q, k, v))
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    cache = cpk.KVCache(1, 8, 8192, 128, torch.bfloat16)
+    poison(cache)
+    out_c, widths = cpk.prefill_chunked(cache, 0, qd, kd, vd, 512, pad=True)
+    one = cpk.KVCache(1, 8, 8192, 128, torch.bfloat16)
+    cpk.cpk_kv_append(one, 0, kd, vd, 0)
+    out_1 = cpk.cpk_chunk_attention(qd, one, 0, 0)
+    torch.cuda.synchronize()
+    assert widths == [512] * 8    # 7 x 512 + 416 padded to 512: eight M=512 forwards
+    chunks = cpk.cpk_split_chunks(4000, 512)
+    rows = sample_rows(4000, chunks)
+    ref = oracle_rows(qs, ks, vs, rows, oracle.BF16)
+    check(out_c[torch.from_numpy(rows).cuda()], ref, 2e-2, f"chunked vs oracle ({len(rows)} rows)")
+    assert bitwise(out_c, out_1), "chunked != one-shot"
+    assert int(cache.seqlens_k[0]) == 4000
+    assert np.array_equal(si.storage(cache.k[0, :, :4000]), ks.transpose(1, 0, 2))
+    assert np.array_equal(si.storage(cache.v[0, :, :4000]), vs.transpose(1, 0, 2))
+
+
+# ------------------------------------------------- workload 3: padding ladder
+
+def test_workload3_ladder_twice_on_dirty_cache():
+    lengths = si.ladder_prompt_lengths()
+    say(f"case: workload 3 ladder prompts {lengths}, each twice, NaN-poisoned tail")
+    cache = cpk.KVCache(1, 8, 8192, 128, torch.bfloat16)
+    poison(cache)
+    plain = cpk.KVCache(1, 8, 8192, 128, torch.bfloat16)
+    for i, L in enumerate(lengths):
+        q, k, v = si.gqa_prompt(L=L, seed=200 + i)
+        qs, ks, vs = (si.storage(x) for x in (q, k, v))
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        outs = []
+        for rep in range(2):
+            if cache.lens[0]:
+                cpk.cpk_rewind(cache, 0, 0)
+            out, widths = cpk.prefill_chunked(cache, 0, qd, kd, vd, 512, pad=True)
+            outs.append(out)
+        if plain.lens[0]:
+            cpk.cpk_rewind(plain, 0, 0)
+        out_np, _ = cpk.prefill_chunked(plain, 0, qd, kd, vd, 512, pad=False)
+        torch.cuda.synchronize()
+        tail = L % 512
+        exp_tail = cpk.cpk_ladder_width(512, tail) if tail else 512
+        assert widths[-1] == exp_tail
+        if L == 1137:
+            assert widths == [512, 512, 171]
+        if L == 1200:
+            assert widths == [512, 512, 342]
+        assert bitwise(outs[0], outs[1]), "second run differs"
+        assert bitwise(outs[0], out_np), "padded != unpadded"
+        assert int(cache.seqlens_k[0]) == L
+        assert np.array_equal(si.storage(cache.k[0, :, :L]), ks.transpose(1, 0, 2))
+        rows = sample_rows(L, cpk.cpk_split_chunks(L, 512), every=97)
+        ref = oracle_rows(qs, ks, vs, rows, oracle.BF16)
+        check(outs[0][torch.from_numpy(rows).cuda()], ref, 2e-2, f"L={L} widths={widths}")
+
+
+def test_rows_equal_capacity_and_single_row_chunks():
+    say("case: W=1 chunks and a prompt filling the cache exactly")
+    q, k, v = si.gqa_prompt(L=40, Hq=8, Hkv=2, D=128, seed=300)
+    qs, ks, vs = (si.storage(x) for x in (q, k, v))
+    ref = oracle.prefill_one_shot(oracle.Cache(oracle.BF16, 1, 2, 40, 128), 0, qs, ks, vs)
+    c = cpk.KVCache(1, 2, 40, 128, torch.bfloat16)
+    out, widths = cpk.prefill_chunked(c, 0, q.cuda(), k.cuda(), v.cuda(), 1, pad=True)
+    c2 = cpk.KVCache(1, 2, 40, 128, torch.bfloat16)
+    out2, widths2 = cpk.prefill_chunked(c2, 0, q.cuda(), k.cuda(), v.cuda(), 40, pad=True)
+    torch.cuda.synchronize()
+    assert widths == [1] * 40 and widths2 == [40]
+    check(out, ref, 2e-2, "W=1")
+    check(out2, ref, 2e-2, "W=L=capacity")
+    assert bitwise(out, out2)
+    with pytest.raises(cpk.CpkError):
+        cpk.cpk_kv_append(c2, 0, k[:1].cuda(), v[:1].cuda(), 40)
+
+
+# -------------------------------------------------- workload 4: rolling fp16
+
+def test_rolling_small_with_left_pad_full_compare():
+    L, C, c, H, D = 1000, 512, 128, 4, 128
+    say(f"case: rolling fp16 L={L} C={C} c={c} H={H} (24 left-pad rows)")
+    q, k, v = si.rolling_inputs(L=L, H=H, D=D, seed=401)
+    qs, ks, vs = (si.storage(x) for x in (q, k, v))
+    ref, n_left, rk, rv, masks = oracle.roll_prefill(qs, ks, vs, C, c, oracle.F16)
+    assert n_left == 24
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out_a, nl, gk, gv = cpk.roll_prefill(qd, kd, vd, C, c)
+    mk = [torch.from_numpy(m.astype(np.float16)).cuda() for m in masks]
+    out_m, _, gk2, gv2 = cpk.roll_prefill(qd, kd, vd, C, c, masks=mk)
+    torch.cuda.synchronize()
+    assert nl == 24
+    assert np.array_equal(si.storage(gk), rk) and np.array_equal(si.storage(gv), rv)
+    assert np.array_equal(si.storage(gk2), rk)
+    check(out_a[n_left:], ref[n_left:], 2e-2, "computed mask vs oracle (real rows)")
+    check(out_m[n_left:], ref[n_left:], 2e-2, "explicit mask vs oracle (real rows)")
+    assert bitwise(out_a[n_left:], out_m[n_left:]), "explicit != computed mask"
+
+
+def test_workload4_rolling_full_size():
+    L, C, c, H, D = 4096, 2048, 256, 16, 128
+    say(f"case: workload 4 rolling fp16 L={L} C={C} c={c} H={H} (sampled rows)")
+    q, k, v = si.rolling_inputs()
+    qs, ks, vs = (si.storage(x) for x in (q, k, v))
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out, nl, gk, gv = cpk.roll_prefill(qd, kd, vd, C, c)
+    masks = [torch.from_numpy(oracle.chunk_mask(L, 0, j, c, C).astype(np.float16)).cuda()
+             for j in range(L // c)]
+    out_m, _, _, _ = cpk.roll_prefill(qd, kd, vd, C, c, masks=masks)
+    torch.cuda.synchronize()
+    assert nl == 0
+    # final cache: the last C positions, right-aligned
+    assert np.array_equal(si.storage(gk), ks[L - C:].transpose(1, 0, 2))
+    assert np.array_equal(si.storage(gv), vs[L - C:].transpose(1, 0, 2))
+    assert bitwise(out, out_m), "explicit != computed mask"
+    rows = np.array(sorted(set(range(0, L, 37)) | set(range(L - 8, L)) | {255, 256, 2047, 2048, 2303}))
+    qq = oracle.widen(np.ascontiguousarray(qs[rows]), oracle.F16)
+    kk = oracle.widen(np.ascontiguousarray(ks.transpose(1, 0, 2)), oracle.F16)
+    vv = oracle.widen(np.ascontiguousarray(vs.transpose(1, 0, 2)), oracle.F16)
+    lo = np.maximum(0, (rows // c + 1) * c - C).astype(np.int32)
+    ref = oracle.attention(qq, kk, vv, lo, rows.astype(np.int32), 1.0 / math.sqrt(D))
+    check(out[torch.from_numpy(rows).cuda()], ref, 2e-2, f"sliding window ({len(rows)} rows)")
+
+
+# ------------------------------------------------ workload 5: mixed varlen
+
+def _run_mixed(n_dec, ctx_lo, ctx_hi, prompt, budget, Hq, Hkv, D, seed, cap, check_steps, every):
+    ctxs = si.mixed_contexts(n_dec, ctx_lo, ctx_hi, seed=seed)
+    B = n_dec + 1
+    cache = cpk.KVCache(B, Hkv, cap, D, torch.bfloat16)
+    si.fill_seeded(cache.k, seed + 1)
+    si.fill_seeded(cache.v, seed + 2)
+    cache.lens = ctxs + [0]
+    pq, pk, pv = si.gqa_prompt(L=prompt, Hq=Hq, Hkv=Hkv, D=D, seed=seed + 3)
+    pqd, pkd, pvd = pq.cuda(), pk.cuda(), pv.cuda()
+    g = si.generator(seed + 4)
+    done, step, lens = 0, 0, list(ctxs)
+    prompt_out = torch.empty_like(pqd)
+    while done < prompt:
+        rows = cpk.cpk_plan_step(budget, n_dec, prompt - done)
+        dq = si.randn((n_dec, Hq, D), "bf16", g).cuda()
+        dk = si.randn((n_dec, Hkv, D), "bf16", g).cuda()
+        dv = si.randn((n_dec, Hkv, D), "bf16", g).cuda()
+        q = torch.cat([dq, pqd[done:done + rows]])
+        kn = torch.cat([dk, pkd[done:done + rows]])
+        vn = torch.cat([dv, pvd[done:done + rows]])
+        slots = list(range(B))
+        cu = list(range(n_dec + 1)) + [n_dec + rows]
+        past = lens + [done]
+        out = cpk.cpk_varlen_step(q, kn, vn, cache, slots, cu, past)
+        prompt_out[done:done + rows] = out[n_dec:]
+        torch.cuda.synchronize()
+        if step in check_steps:
+            # decode rows: every one, against the oracle over the sequence's cache
+            for s in range(n_dec):
+                n = lens[s] + 1
+                kk = oracle.widen(si.storage(cache.k[s, :, :n]), oracle.BF16)
+                vv = oracle.widen(si.storage(cache.v[s, :, :n]), oracle.BF16)
+                qq = oracle.widen(si.storage(dq[s:s + 1]), oracle.BF16)
+                ref = oracle.attention(qq, kk, vv, np.zeros(1, np.int32),
+                                       np.array([n - 1], np.int32), 1.0 / math.sqrt(D))
+                assert np.array_equal(si.storage(cache.k[s, :, n - 1]), si.storage(dk[s]))
+                err = float(np.max(np.abs(f64(out[s:s + 1]) - ref)))
+                assert err <= 2e-2, f"decode seq {s} ctx {n}: {err}"
+            say(f"  step {step}: {n_dec} decode rows ok, prompt rows {done}..{done + rows}")
+        lens = [x + 1 for x in lens]
+        done += rows
+        step += 1
+    torch.cuda.synchronize()
+    qs, ks, vs = (si.storage(x) for x in (pq, pk, pv))
+    rows_idx = sample_rows(prompt, [(0, prompt)], every=every)
+    ref = oracle_rows(qs, ks, vs, rows_idx, oracle.BF16)
+    check(prompt_out[torch.from_numpy(rows_idx).cuda()], ref, 2e-2,
+          f"prompt rows across {step} budgeted steps")
+    assert np.array_equal(si.storage(cache.k[n_dec, :, :prompt]), ks.transpose(1, 0, 2))
+    return step
+
+
+def test_mixed_step_small_full_compare():
+    say("case: mixed step small: 5 decodes ctx 20..300, prompt 700, budget 128, G=4")
+    steps = _run_mixed(5, 20, 300, 700, 128, 8, 2, 128, seed=500, cap=1024,
+                       check_steps=set(range(10)), every=1)
+    assert steps == 6
+
+
+def test_workload5_mixed_full_size_budget_2048():
+    say("case: workload 5: 64 decodes ctx U[512,16384], 20000-token prompt, budget 2048")
+    steps = _run_mixed(64, 512, 16384, 20000, 2048, 32, 8, 128, seed=si.SEEDS["mixed"],
+                       cap=20480, check_steps={0, 10}, every=211)
+    assert steps == 11

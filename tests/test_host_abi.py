@@ -1,0 +1,181 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every symbol the
+header declares, its host logic (ladder, split, planner) agrees with the
+oracle and the pages' printed values, and invalid arguments are rejected on
+the host before any launch (no GPU is touched by these tests)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpk.h")
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_values.json")))
+
+cpk = pytest.importorskip("chunked_prefill_causal_kv_amd")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(cpk.LIB_PATH)
+    names = _declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_covers_every_declared_symbol():
+    for n in _declared_functions():
+        assert callable(getattr(cpk, n)), n
+
+
+def test_ladder_matches_oracle_and_pages():
+    assert cpk.cpk_ladder_rungs(GOLD["ladder"]["W"]) == GOLD["ladder"]["rungs"]
+    for W in list(range(1, 600)) + [1024, 2048, 4096, 8192]:
+        assert cpk.cpk_ladder_rungs(W) == oracle.ladder_rungs(W)
+    for W in (1, 2, 3, 4, 5, 7, 64, 255, 256, 512, 1000):
+        for r in range(1, W + 1):
+            assert cpk.cpk_ladder_width(W, r) == oracle.ladder_width(W, r)
+
+
+def test_split_matches_oracle_and_pages():
+    for L, rows in GOLD["split_examples"]["cases"].items():
+        assert [r for _, r in cpk.cpk_split_chunks(int(L), 512)] == rows
+    assert [r for _, r in cpk.cpk_split_chunks(1000, 256)] == GOLD["demo_split"]["chunk_rows"]
+    for L in (0, 1, 255, 256, 257, 4000, 20000):
+        for W in (1, 7, 256, 512):
+            assert cpk.cpk_split_chunks(L, W) == oracle.split_chunks(L, W)
+
+
+def test_planner_matches_oracle():
+    for budget in (0, 1, 64, 65, 2048, 8192):
+        for n_dec in (0, 1, 64):
+            if n_dec > budget:
+                with pytest.raises(cpk.CpkError):
+                    cpk.cpk_plan_step(budget, n_dec, 100)
+                continue
+            for rem in (0, 1, 100, 20000):
+                assert cpk.cpk_plan_step(budget, n_dec, rem) == oracle.plan_step(budget, n_dec, rem)
+
+
+def test_host_logic_rejects_bad_arguments():
+    for args in ((0, 1), (512, 0), (512, 513)):
+        with pytest.raises(cpk.CpkError) as e:
+            cpk.cpk_ladder_width(*args)
+        assert e.value.status == cpk.CPK_EINVAL
+    with pytest.raises(cpk.CpkError):
+        cpk.cpk_ladder_rungs(0)
+    with pytest.raises(cpk.CpkError):
+        cpk.cpk_split_chunks(-1, 4)
+
+
+# Validation of device calls: each of these must fail on the host before
+# any launch.  The device addresses are fake, so the tests only run where no
+# GPU is visible: a validation gap then shows up as CPK_EHIP (no device)
+# instead of a launch on bogus pointers.
+
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced
+no_gpu = pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                            reason="fake device pointers: host-only machines")
+
+
+def _desc(**kw):
+    d = dict(k=FAKE, v=FAKE * 2, seqlens_k=FAKE * 3, batch=2, kv_heads=8, capacity=1024,
+             head_dim=128, dtype=cpk.CPK_BF16)
+    d.update(kw)
+    return cpk.cpk_kv_cache(d["k"], d["v"], d["seqlens_k"], d["batch"], d["kv_heads"],
+                            d["capacity"], d["head_dim"], d["dtype"])
+
+
+def _append(desc, b=0, past=0, rows=4, kn=FAKE, vn=FAKE, real=None):
+    return cpk._lib.cpk_kv_append(ctypes.byref(desc), b, kn, vn, past, rows,
+                                  rows if real is None else real, None)
+
+
+@no_gpu
+def test_append_validation():
+    assert _append(_desc(), past=1020, rows=5) == cpk.CPK_ECAPACITY
+    assert _append(_desc(), b=2) == cpk.CPK_EINVAL
+    assert _append(_desc(), rows=0) == cpk.CPK_EINVAL
+    assert _append(_desc(), rows=4, real=5) == cpk.CPK_EINVAL
+    assert _append(_desc(), rows=4, real=0) == cpk.CPK_EINVAL
+    assert _append(_desc(), kn=FAKE + 2) == cpk.CPK_EALIGN
+    assert _append(_desc(head_dim=96)) == cpk.CPK_EDTYPE
+    assert _append(_desc(dtype=7)) == cpk.CPK_EDTYPE
+    assert _append(_desc(k=0)) == cpk.CPK_EINVAL
+    assert "capacity" in (_append(_desc(), past=1024, rows=1) and cpk.cpk_last_error())
+
+
+def _attn(desc, Hq=32, past=0, rows=8, real=8, q=FAKE, out=FAKE):
+    return cpk._lib.cpk_chunk_attention(q, ctypes.byref(desc), 0, Hq, past, rows, real, 0.0,
+                                        out, None)
+
+
+@no_gpu
+def test_attention_validation():
+    assert _attn(_desc(), real=9) == cpk.CPK_EINVAL
+    assert _attn(_desc(), Hq=30) == cpk.CPK_EINVAL
+    assert _attn(_desc(kv_heads=1), Hq=128) == cpk.CPK_EINVAL       # group 128 > 64
+    assert _attn(_desc(), past=1020, rows=8) == cpk.CPK_ECAPACITY
+    assert _attn(_desc(), q=FAKE + 8) == cpk.CPK_EALIGN
+    assert _attn(_desc(), rows=0, real=0) == cpk.CPK_EINVAL
+
+
+@no_gpu
+def test_rewind_and_prefill_validation():
+    d = _desc()
+    assert cpk._lib.cpk_rewind(ctypes.byref(d), 0, 5, 4, None) == cpk.CPK_EINVAL
+    assert cpk._lib.cpk_rewind(ctypes.byref(d), 0, -1, 4, None) == cpk.CPK_EINVAL
+    w = ctypes.c_int(0)
+    f = cpk._lib.cpk_prefill_chunk
+    # real rows above the chunk width
+    assert f(FAKE, FAKE, FAKE, ctypes.byref(d), 0, 32, 0, 513, 512, 1, 0.0, FAKE, ctypes.byref(w), None) == cpk.CPK_EINVAL
+    # padding 113 -> 171 rows does not fit 1024 - 900
+    assert f(FAKE, FAKE, FAKE, ctypes.byref(d), 0, 32, 900, 113, 512, 1, 0.0, FAKE, ctypes.byref(w), None) == cpk.CPK_ECAPACITY
+    # without padding it would fit: then the failure must come from elsewhere
+    assert f(FAKE, FAKE, FAKE, ctypes.byref(d), 0, 30, 900, 113, 512, 0, 0.0, FAKE, ctypes.byref(w), None) == cpk.CPK_EINVAL
+
+
+@no_gpu
+def test_varlen_validation():
+    d = _desc()
+    A = ctypes.c_int32
+    slots = (A * 2)(0, 0)
+    cu = (A * 3)(0, 1, 3)
+    past = (A * 2)(10, 20)
+    f = cpk._lib.cpk_varlen_step
+    # slot used twice
+    assert f(FAKE, FAKE, FAKE, ctypes.byref(d), FAKE, FAKE, FAKE, slots, cu, past, 2, 3, 32, 0.0,
+             FAKE, FAKE, 1 << 30, None) == cpk.CPK_EINVAL
+    slots = (A * 2)(0, 1)
+    # cu_rows not ending at total_rows
+    assert f(FAKE, FAKE, FAKE, ctypes.byref(d), FAKE, FAKE, FAKE, slots, cu, past, 2, 4, 32, 0.0,
+             FAKE, FAKE, 1 << 30, None) == cpk.CPK_EINVAL
+    # workspace too small for the decode row
+    assert f(FAKE, FAKE, FAKE, ctypes.byref(d), FAKE, FAKE, FAKE, slots, cu, past, 2, 3, 32, 0.0,
+             FAKE, FAKE, 16, None) == cpk.CPK_EWORKSPACE
+    # capacity
+    past = (A * 2)(1024, 20)
+    assert f(FAKE, FAKE, FAKE, ctypes.byref(d), FAKE, FAKE, FAKE, slots, cu, past, 2, 3, 32, 0.0,
+             FAKE, FAKE, 1 << 30, None) == cpk.CPK_ECAPACITY
+    assert cpk.cpk_varlen_workspace_size(64, 32, 16385, 128) == 64 * 32 * 65 * 132 * 4
+
+
+@no_gpu
+def test_roll_validation():
+    f = cpk._lib.cpk_roll_append
+    # c > C
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, FAKE * 6, 1, 2, 8, 9, 64, cpk.CPK_F16, None) == cpk.CPK_EINVAL
+    # output overlaps input
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE, FAKE * 6, 1, 2, 8, 4, 64, cpk.CPK_F16, None) == cpk.CPK_EINVAL
+    g = cpk._lib.cpk_roll_attention
+    assert g(FAKE, FAKE, FAKE, None, 100, 0, 16, 16, 64, 128, 128, cpk.CPK_F16, 0.0, FAKE, None) == cpk.CPK_EINVAL
+    assert g(FAKE, FAKE, FAKE, None, 10, 0, 16, 16, 64, 32, 128, cpk.CPK_F16, 0.0, FAKE, None) == cpk.CPK_EINVAL
