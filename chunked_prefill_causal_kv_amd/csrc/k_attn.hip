@@ -22,7 +22,7 @@
 // * Scores are computed transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_{bf16,f16}: a lane then holds one query column and
 //   16 keys, so the row max is 15 in-lane max operations plus one
-//   permlane32 swap, and the probabilities are already in the B-operand
+//   cross-half exchange, and the probabilities are already in the B-operand
 //   layout of O^T = V^T P^T.
 // * Online softmax in the exp2 domain (scale * log2 e folded into one FMA).
 //   The running maximum is only raised when a tile's maximum exceeds it by
@@ -86,22 +86,17 @@ constexpr int kBK = 128;        // keys per LDS tile
 constexpr int kThreads = 256;   // 4 waves
 constexpr float kLazyLog2 = 8.0f;
 
-// v_permlane32_swap exchanges the two 32-lane halves between its operands;
-// with the same value in both, {r[0], r[1]} is {own, partner} in some order
-// in every lane, so max() and + of the two are the pair max / pair sum, and
-// both halves obtain bit-identical results.
+// The two 32-lane halves of a wave hold the same query column (different
+// keys).  Exchange through ds_bpermute (__shfl_xor across 32 lanes); max and
+// + are commutative, so both halves obtain bit-identical results.
 __device__ __forceinline__ float pair_max(float x)
 {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
-                                                    __builtin_bit_cast(int, x), false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+    return fmaxf(x, __shfl_xor(x, 32));
 }
 
 __device__ __forceinline__ float pair_sum(float x)
 {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
-                                                    __builtin_bit_cast(int, x), false, false);
-    return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+    return x + __shfl_xor(x, 32);
 }
 
 __device__ __forceinline__ uint32_t dword(const uint4 &v, int j)

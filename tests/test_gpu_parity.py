@@ -141,7 +141,7 @@ def test_chunked_prefill_full_compare(dtype, Hq, Hkv, D, L, W):
     dn = {torch.bfloat16: "bf16", torch.float16: "f16"}[dtype]
     q, k, v = si.gqa_prompt(L=L, Hq=Hq, Hkv=Hkv, D=D, dtype=dn, seed=7 + L)
     qs, ks, vs = (si.storage(x) for x in (q, k, v))
-    cap = L + 64
+    cap = L + W   # room for the padded tail chunk
     ref = oracle.prefill_one_shot(oracle.Cache(ODT[dtype], 1, Hkv, cap, D), 0, qs, ks, vs)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     c1 = cpk.KVCache(1, Hkv, cap, D, dtype)
