@@ -180,9 +180,25 @@ def bench_decode(cpk, si, torch, reps=10):
             "note": "whole packed step (append + split-KV decode + combine)"}
 
 
+def calibrate_copy(cpk, torch, reps=3):
+    """A plain copy of known size for scaling HBM counters: roll_append with
+    c = 1 reads K and V caches of 32 heads x 16384 x 128 bf16 (2 x 128 MiB)
+    and writes the same amount."""
+    H, C, D = 32, 16384, 128
+    bufs = [torch.ones((1, H, C, D), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    chunk = [torch.ones((1, 1, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    for _ in range(reps):
+        cpk.cpk_roll_append(bufs[0], bufs[1], chunk[0], chunk[1], bufs[2], bufs[3])
+    torch.cuda.synchronize()
+    nbytes = 2 * H * C * D * 2
+    log(f"calibration copy: {nbytes} bytes read and {nbytes} bytes written per launch")
+    return nbytes
+
+
 def cpu_baseline(si, budget_s=10.0):
-    """The fp64 oracle on rows of the last chunk (past_len 3584, 416 real
-    rows), sampled until about budget_s seconds of CPU work."""
+    """The fp64 oracle on rows of the 4000-token prompt drawn in a seeded
+    random order, until all rows are done or about budget_s seconds of CPU
+    work have been spent."""
     import numpy as np
 
     import oracle
@@ -191,11 +207,11 @@ def cpu_baseline(si, budget_s=10.0):
     qs, ks, vs = (si.storage(x) for x in (q, k, v))
     kk = oracle.widen(np.ascontiguousarray(ks.transpose(1, 0, 2)), oracle.BF16)
     vv = oracle.widen(np.ascontiguousarray(vs.transpose(1, 0, 2)), oracle.BF16)
-    rows_all = np.arange(3584, 4000)
+    rows_all = np.arange(0, L)
     rng = np.random.default_rng(0)
     rows_all = rng.permutation(rows_all)
     done_rows, flops, t_total = 0, 0, 0.0
-    batch = 16
+    batch = 64
     while done_rows < len(rows_all) and t_total < budget_s:
         rows = np.sort(rows_all[done_rows:done_rows + batch])
         qq = oracle.widen(np.ascontiguousarray(qs[rows]), oracle.BF16)
@@ -207,8 +223,8 @@ def cpu_baseline(si, budget_s=10.0):
         done_rows += len(rows)
     return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s",
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{done_rows} of the 416 rows of the last W=512 chunk (past_len 3584) "
-                      f"of the 4000-token prompt, all 32 heads, fp64; {t_total:.1f} s"}
+            "sample": f"{done_rows} of the 4000 query rows of the prompt (seeded random order), "
+                      f"all 32 heads, causal over the cache, fp64; {t_total:.1f} s"}
 
 
 def main():
@@ -218,6 +234,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain copy of known size (for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -231,6 +249,8 @@ def main():
     import synth_inputs as si
 
     torch.cuda.set_device(0)
+    if args.calibrate:
+        calibrate_copy(cpk, torch)
     log("bench: chunked prefill 4000 tokens, W=512, GQA 32/8, D=128, bf16")
     r = bench_chunked(cpk, si, torch, args.steps, args.warmup)
     log(f"bench: {r['ms_step']:.3f} ms/step, attention {r['achieved']:.1f} TFLOP/s")

@@ -80,7 +80,7 @@ hipError_t launch_roll_append(const void *k_old, const void *v_old, const void *
                               const void *v_chunk, void *k_new, void *v_new, int B, int H,
                               int C, int c, int row_bytes, hipStream_t st);
 
-// Attention: grid.x = row blocks, grid.y = KV heads, grid.z = sequences.
+// Attention: grid.x = row blocks x KV heads (KV head fastest), grid.z = sequences.
 int attn_rows_per_block(int dtype, int group);
 hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
                             hipStream_t st);

@@ -12,10 +12,15 @@
 // -------------------------------------
 // * Work item: 64 "query columns" = G query heads x (64/G) rows that share
 //   one KV head, so every K/V tile staged in LDS serves the whole GQA group.
-// * K/V tiles of 128 keys, double-buffered in LDS: K row-major [key][d],
-//   V transposed [d][key] so that both MFMA contractions read 16-byte
-//   fragments.  Tiles are aligned to absolute key 0, so a query row visits
-//   the same tile sequence whether its prompt runs in one pass or in chunks.
+//   Workgroups are numbered KV head fastest, so with 8 KV heads each XCD
+//   (and its L2) serves a single KV head.
+// * K/V tiles of 128 keys, double-buffered in LDS and filled by direct
+//   global->LDS 16-byte loads (no register staging).  Both tiles stay
+//   row-major [key][d]; the 16-byte chunks of each row are XOR-swizzled
+//   (by choosing which global chunk each lane fetches) so that the MFMA
+//   fragment reads below are free of bank conflicts.  Tiles are aligned to
+//   absolute key 0, so a query row visits the same tile sequence whether its
+//   prompt runs in one pass or in chunks.
 // * Each of the 4 waves owns 32 keys of every tile and keeps its own online
 //   softmax state for all 64 query columns; the 4 states are merged once at
 //   the end through LDS (an in-workgroup split of the key range).
@@ -23,14 +28,18 @@
 //   v_mfma_f32_32x32x16_{bf16,f16}: a lane then holds one query column and
 //   16 keys, so the row max is 15 in-lane max operations plus one
 //   cross-half exchange, and the probabilities are already in the B-operand
-//   layout of O^T = V^T P^T.
+//   layout of O^T = V^T P^T.  V^T fragments come straight from the
+//   row-major V tile through the LDS transpose read (ds_read_b64_tr_b16).
 // * Online softmax in the exp2 domain (scale * log2 e folded into one FMA).
 //   The running maximum is only raised when a tile's maximum exceeds it by
 //   more than 2^8; otherwise the stale maximum is kept (probabilities up to
 //   256, exact after the final normalisation).  This removes almost every
-//   rescale of the 128 accumulator registers.
-// * Keys at or past n_keys are zero-filled in LDS and never read from the
-//   cache, so stale or poisoned bytes beyond the valid length cannot leak.
+//   rescale of the 128 accumulator registers.  The row sum accumulates the
+//   rounded probabilities with packed dot products, so numerator and
+//   denominator use the same weights.
+// * Key indices at or past n_keys are clamped to the last valid key for the
+//   load and masked out of the softmax, so bytes beyond the valid length
+//   (stale pads, poison) are never read.
 //
 // fp32 kernel (attn_f32_kernel): one query column per lane, VALU FMAs in
 // fp32 with an exact per-tile rescale.  Full precision, no reduced-precision
@@ -45,14 +54,24 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 struct Bf16 {
     typedef bf16x8_t vec8;
+    static constexpr uint32_t kOnes = 0x3f803f80u;   // (1.0, 1.0)
     static __device__ __forceinline__ f32x16_t mfma(uint4 a, uint4 b, f32x16_t c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(vec8, a),
                                                        __builtin_bit_cast(vec8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+    {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                               __builtin_bit_cast(bf16x2_t, b), c, false);
     }
     static __device__ __forceinline__ float to_f32(uint32_t bits16)
     {
@@ -66,10 +85,16 @@ struct Bf16 {
 
 struct F16 {
     typedef f16x8_t vec8;
+    static constexpr uint32_t kOnes = 0x3c003c00u;   // (1.0, 1.0)
     static __device__ __forceinline__ f32x16_t mfma(uint4 a, uint4 b, f32x16_t c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(vec8, a),
                                                       __builtin_bit_cast(vec8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+    {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a),
+                                      __builtin_bit_cast(f16x2_t, b), c, false);
     }
     static __device__ __forceinline__ float to_f32(uint32_t bits16)
     {
@@ -99,31 +124,18 @@ __device__ __forceinline__ float pair_sum(float x)
     return x + __shfl_xor(x, 32);
 }
 
-__device__ __forceinline__ uint32_t dword(const uint4 &v, int j)
-{
-    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
-}
-
-// Position of key k inside a 16-key group of the transposed V tile: bits 2
-// and 3 swapped.  With it, the 8 probabilities a lane holds for one PV
-// k-step and the 8 V^T values it reads for that step are the same keys in
-// the same order (see the S^T accumulator layout below).
-__device__ __forceinline__ int swap23(int k)
-{
-    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-
 template <int D>
 struct Tile {
-    static constexpr int KS = D + 8;        // K row stride, elements (16-byte aligned rows)
-    static constexpr int VS = kBK + 8;      // V^T row stride
-    static constexpr int STAGE = kBK * KS + D * VS;   // uint16 elements per buffer
-    static constexpr int KPT = kBK * D / 8 / kThreads;   // keys staged per thread
-    static constexpr int NKG = kBK / KPT;   // key groups
-    static constexpr int OS = D + 4;        // epilogue row stride (floats)
+    static constexpr int NCH = D / 8;                 // 16-byte chunks per key row
+    static constexpr int STAGE = 2 * kBK * D;         // K then V, uint16 elements
+    static constexpr int LOADS = kBK * NCH / kThreads;   // 16-byte loads per thread per tensor
+    static constexpr int OS = D + 4;                  // epilogue row stride (floats)
     static constexpr int LOOP_BYTES = 2 * STAGE * 2;
     static constexpr int EPI_BYTES = (4 * kQC * OS + 2 * 4 * kQC) * 4;
     static constexpr int BYTES = LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES;
+    // chunk swizzles: stored position = chunk ^ swizzle(row)
+    static __device__ __forceinline__ int swz_k(int row) { return row % NCH; }
+    static __device__ __forceinline__ int swz_v(int row) { return (row % (NCH / 4)) << 2; }
 };
 
 struct SeqView {
@@ -152,10 +164,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void attn_mfma_kernel(AttnArgs a)
 {
     using TL = Tile<D>;
-    constexpr int KPT = TL::KPT;
-    constexpr int NKG = TL::NKG;
-    constexpr int KS = TL::KS;
-    constexpr int VS = TL::VS;
+    constexpr int NCH = TL::NCH;
     constexpr int NS = D / 16;      // k-steps of the QK^T contraction
     constexpr int NDB = D / 32;     // 32-wide d blocks of O^T
 
@@ -165,9 +174,12 @@ void attn_mfma_kernel(AttnArgs a)
     if (!resolve_seq(a, blockIdx.z, sv)) return;
     const int G = a.Hq / a.Hkv;
     const int BR = kQC / G;                 // rows per workgroup
-    const int r0 = blockIdx.x * BR;
+    // blockIdx.x = row_block * Hkv + kv_head: consecutive workgroups go to
+    // consecutive XCDs, so with 8 KV heads each XCD serves one KV head and
+    // its L2 holds that head's K/V for all of the XCD's row blocks.
+    const int g = blockIdx.x % a.Hkv;
+    const int r0 = (blockIdx.x / a.Hkv) * BR;
     if (r0 >= sv.rows) return;
-    const int g = blockIdx.y;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -182,7 +194,6 @@ void attn_mfma_kernel(AttnArgs a)
     uint4 qf[2][NS];
     int lim[2];            // last visible key of this lane's column
     int qrow[2];
-    bool qvalid[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const int qc = qb * 32 + c32;
@@ -192,7 +203,6 @@ void attn_mfma_kernel(AttnArgs a)
         const int srow = rr < sv.q_src_rows ? rr : sv.q_src_rows - 1;
         const int head = g * G + (ok ? qc % G : 0);
         qrow[qb] = rr;
-        qvalid[qb] = ok;
         lim[qb] = sv.causal_base + rr;
         const uint16_t *qp = qg + ((int64_t)(sv.q_row0 + srow) * a.Hq + head) * D + 8 * hi;
 #pragma unroll
@@ -205,45 +215,26 @@ void attn_mfma_kernel(AttnArgs a)
     const int t_first = sv.key_lo / kBK;
     const int t_last = (key_end - 1) / kBK;
 
-    // ---- staging assignment: thread -> (key group, 8-element d chunk)
-    const int kg = tid % NKG;
-    const int dc = tid / NKG;
-    uint4 kreg[KPT], vreg[KPT];
-
-    auto load_tile = [&](int kt) {
+    // ---- direct global->LDS tile loads: load i of this wave fills LDS
+    // chunks [(i*4 + wave)*64, +64) of the tile, one 16-byte chunk per lane
+    auto issue_tile = [&](int kt, int buf) {
+        uint16_t *Kb = smem + buf * TL::STAGE;
+        uint16_t *Vb = Kb + kBK * D;
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int key = kt * kBK + swap23(kg * KPT + i);
-            if (key < sv.n_keys) {
-                kreg[i] = *(const uint4 *)(kc + (int64_t)key * D + dc * 8);
-                vreg[i] = *(const uint4 *)(vc + (int64_t)key * D + dc * 8);
-            } else {
-                kreg[i] = make_uint4(0, 0, 0, 0);
-                vreg[i] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        uint16_t *Ks = smem + buf * TL::STAGE;
-        uint16_t *Vt = Ks + kBK * KS;
-#pragma unroll
-        for (int i = 0; i < KPT; ++i)
-            *(uint4 *)(Ks + swap23(kg * KPT + i) * KS + dc * 8) = kreg[i];
-        // transpose 8 d x KPT keys into V^T rows d = dc*8 + e
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint32_t w[KPT / 2];
-#pragma unroll
-            for (int i = 0; i < KPT / 2; ++i) {
-                const uint32_t a0 = (dword(vreg[2 * i], e >> 1) >> (16 * (e & 1))) & 0xffffu;
-                const uint32_t a1 = (dword(vreg[2 * i + 1], e >> 1) >> (16 * (e & 1))) & 0xffffu;
-                w[i] = a0 | (a1 << 16);
-            }
-            uint16_t *dst = Vt + (dc * 8 + e) * VS + kg * KPT;
-            if constexpr (KPT == 8)
-                *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
-            else
-                *(uint2 *)dst = make_uint2(w[0], w[1]);
+        for (int i = 0; i < TL::LOADS; ++i) {
+            const int blk = i * 4 + wave;
+            const int t = blk * 64 + lane;
+            const int row = t / NCH;
+            const int pos = t % NCH;
+            const int key = min(kt * kBK + row, sv.n_keys - 1);
+            const uint16_t *ks = kc + (int64_t)key * D + (pos ^ TL::swz_k(row)) * 8;
+            const uint16_t *vs = vc + (int64_t)key * D + (pos ^ TL::swz_v(row)) * 8;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)ks,
+                (__attribute__((address_space(3))) void *)(Kb + blk * 64 * 8), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)vs,
+                (__attribute__((address_space(3))) void *)(Vb + blk * 64 * 8), 16, 0, 0);
         }
     };
 
@@ -261,19 +252,27 @@ void attn_mfma_kernel(AttnArgs a)
     const float inv_scale = 1.0f / a.scale;
     const uint16_t *maskp = (const uint16_t *)a.mask;
 
-    if (t_last >= t_first) {
-        load_tile(t_first);
-        store_tile(0);
-    }
-    __syncthreads();
+    // V^T fragment addressing for the LDS transpose read: in each 16-lane
+    // group, lane s supplies 4 elements of row (s/4); lane i receives
+    // element i of the 4 rows.  Row j of half-read j2 is key
+    // 16*s2 + 8*j2 + 4*hi + j of this wave's 32 keys, columns
+    // d = 32*db + 16*g16 .. +16, so the lane receives V[key][d] for the same
+    // keys, in the same order, as its probabilities for that k-step.
+    const int g16 = (lane >> 4) & 1;
+    const int si = lane & 15;
+    const int vrow_off = 4 * hi + (si >> 2);          // + 16*s2 + 8*j2 + 32*wave
+    const int vcol = 16 * g16 + 4 * (si & 3);         // + 32*db
+
+    if (t_last >= t_first) issue_tile(t_first, 0);
 
     for (int kt = t_first; kt <= t_last; ++kt) {
         const int buf = (kt - t_first) & 1;
-        const bool more = kt < t_last;
-        if (more) load_tile(kt + 1);
+        __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of tile kt have landed
+        __syncthreads();                   // ... and every wave's; buf^1 is free again
+        if (kt < t_last) issue_tile(kt + 1, buf ^ 1);
 
-        const uint16_t *Ks = smem + buf * TL::STAGE;
-        const uint16_t *Vt = Ks + kBK * KS;
+        const uint16_t *Kb = smem + buf * TL::STAGE;
+        const uint16_t *Vb = Kb + kBK * D;
 
         // S^T[32 keys x 64 cols] for this wave's keys
         f32x16_t sacc[2];
@@ -281,11 +280,16 @@ void attn_mfma_kernel(AttnArgs a)
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) sacc[qb][j] = 0.f;
+        {
+            const int krow = wave * 32 + c32;
+            const uint16_t *kr = Kb + krow * D;
+            const int sk = TL::swz_k(krow);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const uint4 ka = *(const uint4 *)(Ks + (wave * 32 + c32) * KS + 16 * s + 8 * hi);
-            sacc[0] = TR::mfma(ka, qf[0][s], sacc[0]);
-            sacc[1] = TR::mfma(ka, qf[1][s], sacc[1]);
+            for (int s = 0; s < NS; ++s) {
+                const uint4 ka = *(const uint4 *)(kr + ((2 * s + hi) ^ sk) * 8);
+                sacc[0] = TR::mfma(ka, qf[0][s], sacc[0]);
+                sacc[1] = TR::mfma(ka, qf[1][s], sacc[1]);
+            }
         }
 
         // Accumulator register j of lane (c32, hi) holds key
@@ -336,19 +340,18 @@ void attn_mfma_kernel(AttnArgs a)
                     for (int j = 0; j < 16; ++j) oacc[qb][db][j] *= alpha;
             }
             const float mu = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-            float p[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][j], c, -mu));
-                l_run[qb] += p[j];
-            }
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 uint32_t w[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    w[i] = TR::from_f32(p[8 * s2 + 2 * i]) |
-                           (TR::from_f32(p[8 * s2 + 2 * i + 1]) << 16);
+                for (int i = 0; i < 4; ++i) {
+                    const float p0 =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][8 * s2 + 2 * i], c, -mu));
+                    const float p1 =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][8 * s2 + 2 * i + 1], c, -mu));
+                    w[i] = TR::from_f32(p0) | (TR::from_f32(p1) << 16);
+                    l_run[qb] = TR::dot2(w[i], TR::kOnes, l_run[qb]);
+                }
                 pb[qb][s2] = make_uint4(w[0], w[1], w[2], w[3]);
             }
         }
@@ -358,15 +361,22 @@ void attn_mfma_kernel(AttnArgs a)
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const uint4 va =
-                    *(const uint4 *)(Vt + (db * 32 + c32) * VS + wave * 32 + 16 * s2 + 8 * hi);
+                uint2 half[2];
+#pragma unroll
+                for (int j2 = 0; j2 < 2; ++j2) {
+                    const int vrow = wave * 32 + 16 * s2 + 8 * j2 + vrow_off;
+                    const int dd = 32 * db + vcol;
+                    const uint16_t *vp =
+                        Vb + vrow * D + (((dd >> 3) ^ TL::swz_v(vrow)) << 3) + (dd & 7);
+                    const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)vp);
+                    half[j2] = __builtin_bit_cast(uint2, r);
+                }
+                const uint4 va = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
                 oacc[0][db] = TR::mfma(va, pb[0][s2], oacc[0][db]);
                 oacc[1][db] = TR::mfma(va, pb[1][s2], oacc[1][db]);
             }
-
-        if (more) store_tile(buf ^ 1);
-        __syncthreads();
     }
+    __syncthreads();   // all waves are done with the tiles: reuse LDS below
 
     // ---- merge the four waves' partial states, normalise, write rows
     float *Ms = (float *)smem;
@@ -451,9 +461,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a)
     if (!resolve_seq(a, blockIdx.z, sv)) return;
     const int G = a.Hq / a.Hkv;
     const int BR = kQC / G;
-    const int r0 = blockIdx.x * BR;
+    const int g = blockIdx.x % a.Hkv;
+    const int r0 = (blockIdx.x / a.Hkv) * BR;
     if (r0 >= sv.rows) return;
-    const int g = blockIdx.y;
     const int t = threadIdx.x;
 
     const int row = r0 + t / G;
@@ -545,7 +555,7 @@ int attn_rows_per_block(int dtype, int group)
 hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
                             hipStream_t st)
 {
-    const dim3 grid(row_blocks, a.Hkv, n_seq_grid);
+    const dim3 grid(row_blocks * a.Hkv, 1, n_seq_grid);
     if (dtype == 0) {
         if (a.D == 64)
             hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, st, a);
