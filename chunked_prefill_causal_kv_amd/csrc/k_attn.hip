@@ -21,9 +21,11 @@
 //   fragment reads below are free of bank conflicts.  Tiles are aligned to
 //   absolute key 0, so a query row visits the same tile sequence whether its
 //   prompt runs in one pass or in chunks.
-// * Each of the 4 waves owns 32 keys of every tile and keeps its own online
-//   softmax state for all 64 query columns; the 4 states are merged once at
-//   the end through LDS (an in-workgroup split of the key range).
+// * 8 waves: 2 groups of 32 query columns x 4 slices of 32 keys of every
+//   tile.  Each wave keeps its own online-softmax state for its 32 columns;
+//   the 4 key slices are merged once at the end through LDS (an
+//   in-workgroup split of the key range).  Two waves per SIMD let one
+//   wave's softmax (VALU) overlap the other's matrix work.
 // * Scores are computed transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_{bf16,f16}: a lane then holds one query column and
 //   16 keys, so the row max is 15 in-lane max operations plus one
@@ -81,6 +83,11 @@ struct Bf16 {
     {
         return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
     }
+    static __device__ __forceinline__ uint32_t pack(float lo, float hi)
+    {
+        const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
 };
 
 struct F16 {
@@ -104,11 +111,16 @@ struct F16 {
     {
         return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
     }
+    static __device__ __forceinline__ uint32_t pack(float lo, float hi)
+    {
+        const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
 };
 
-constexpr int kQC = 64;         // query columns per workgroup
-constexpr int kBK = 128;        // keys per LDS tile
-constexpr int kThreads = 256;   // 4 waves
+constexpr int kQC = 64;         // query columns per workgroup (2 groups of 32)
+constexpr int kBK = 128;        // keys per LDS tile (4 slices of 32)
+constexpr int kThreads = 512;   // 8 waves = 2 column groups x 4 key slices
 constexpr float kLazyLog2 = 8.0f;
 
 // The two 32-lane halves of a wave hold the same query column (different
@@ -129,6 +141,7 @@ struct Tile {
     static constexpr int NCH = D / 8;                 // 16-byte chunks per key row
     static constexpr int STAGE = 2 * kBK * D;         // K then V, uint16 elements
     static constexpr int LOADS = kBK * NCH / kThreads;   // 16-byte loads per thread per tensor
+    static constexpr int WAVES = kThreads / 64;
     static constexpr int OS = D + 4;                  // epilogue row stride (floats)
     static constexpr int LOOP_BYTES = 2 * STAGE * 2;
     static constexpr int EPI_BYTES = (4 * kQC * OS + 2 * 4 * kQC) * 4;
@@ -160,7 +173,7 @@ __device__ __forceinline__ bool resolve_seq(const AttnArgs &a, int z, SeqView &s
 }
 
 template <typename TR, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_mfma_kernel(AttnArgs a)
 {
     using TL = Tile<D>;
@@ -185,28 +198,28 @@ void attn_mfma_kernel(AttnArgs a)
     const int lane = tid & 63;
     const int c32 = lane & 31;
     const int hi = lane >> 5;
+    const int qg = wave >> 2;               // query-column group: columns 32*qg .. +32
+    const int ks = wave & 3;                // key slice: keys 32*ks .. +32 of each tile
+    const int qc = qg * 32 + c32;           // this lane's query column
 
-    const uint16_t *qg = (const uint16_t *)a.q;
     const uint16_t *kc = (const uint16_t *)a.k + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
     const uint16_t *vc = (const uint16_t *)a.v + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
 
-    // ---- query fragments (B operand of S^T = K Q^T), one column per lane
-    uint4 qf[2][NS];
-    int lim[2];            // last visible key of this lane's column
-    int qrow[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int qc = qb * 32 + c32;
+    // ---- query fragment (B operand of S^T = K Q^T): column qc
+    uint4 qf[NS];
+    int lim, qrow;
+    {
         const int row = r0 + qc / G;
         const bool ok = (qc < BR * G) && (row < sv.rows);
         const int rr = ok ? row : r0;
         const int srow = rr < sv.q_src_rows ? rr : sv.q_src_rows - 1;
         const int head = g * G + (ok ? qc % G : 0);
-        qrow[qb] = rr;
-        lim[qb] = sv.causal_base + rr;
-        const uint16_t *qp = qg + ((int64_t)(sv.q_row0 + srow) * a.Hq + head) * D + 8 * hi;
+        qrow = rr;
+        lim = sv.causal_base + rr;
+        const uint16_t *qp =
+            (const uint16_t *)a.q + ((int64_t)(sv.q_row0 + srow) * a.Hq + head) * D + 8 * hi;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) qf[qb][s] = *(const uint4 *)(qp + 16 * s);
+        for (int s = 0; s < NS; ++s) qf[s] = *(const uint4 *)(qp + 16 * s);
     }
 
     // ---- key range of this workgroup
@@ -216,38 +229,36 @@ void attn_mfma_kernel(AttnArgs a)
     const int t_last = (key_end - 1) / kBK;
 
     // ---- direct global->LDS tile loads: load i of this wave fills LDS
-    // chunks [(i*4 + wave)*64, +64) of the tile, one 16-byte chunk per lane
+    // chunks [(i*WAVES + wave)*64, +64) of the tile, one 16-byte chunk per lane
     auto issue_tile = [&](int kt, int buf) {
         uint16_t *Kb = smem + buf * TL::STAGE;
         uint16_t *Vb = Kb + kBK * D;
 #pragma unroll
         for (int i = 0; i < TL::LOADS; ++i) {
-            const int blk = i * 4 + wave;
+            const int blk = i * TL::WAVES + wave;
             const int t = blk * 64 + lane;
             const int row = t / NCH;
             const int pos = t % NCH;
             const int key = min(kt * kBK + row, sv.n_keys - 1);
-            const uint16_t *ks = kc + (int64_t)key * D + (pos ^ TL::swz_k(row)) * 8;
-            const uint16_t *vs = vc + (int64_t)key * D + (pos ^ TL::swz_v(row)) * 8;
+            const uint16_t *ksrc = kc + (int64_t)key * D + (pos ^ TL::swz_k(row)) * 8;
+            const uint16_t *vsrc = vc + (int64_t)key * D + (pos ^ TL::swz_v(row)) * 8;
             __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)ks,
+                (const __attribute__((address_space(1))) void *)ksrc,
                 (__attribute__((address_space(3))) void *)(Kb + blk * 64 * 8), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)vs,
+                (const __attribute__((address_space(1))) void *)vsrc,
                 (__attribute__((address_space(3))) void *)(Vb + blk * 64 * 8), 16, 0, 0);
         }
     };
 
     // ---- accumulators
-    f32x16_t oacc[2][NDB];
+    f32x16_t oacc[NDB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[qb][db][j] = 0.f;
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
+        for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
     const float c = a.scale_log2;
     const float inv_scale = 1.0f / a.scale;
     const uint16_t *maskp = (const uint16_t *)a.mask;
@@ -260,8 +271,9 @@ void attn_mfma_kernel(AttnArgs a)
     // keys, in the same order, as its probabilities for that k-step.
     const int g16 = (lane >> 4) & 1;
     const int si = lane & 15;
-    const int vrow_off = 4 * hi + (si >> 2);          // + 16*s2 + 8*j2 + 32*wave
-    const int vcol = 16 * g16 + 4 * (si & 3);         // + 32*db
+    const int vrow_off = ks * 32 + 4 * hi + (si >> 2);   // + 16*s2 + 8*j2
+    const int vcol = 16 * g16 + 4 * (si & 3);            // + 32*db
+    const int krow = ks * 32 + c32;
 
     if (t_last >= t_first) issue_tile(t_first, 0);
 
@@ -274,86 +286,74 @@ void attn_mfma_kernel(AttnArgs a)
         const uint16_t *Kb = smem + buf * TL::STAGE;
         const uint16_t *Vb = Kb + kBK * D;
 
-        // S^T[32 keys x 64 cols] for this wave's keys
-        f32x16_t sacc[2];
+        // S^T[32 keys x 32 cols] for this wave's key slice and column group
+        f32x16_t sacc;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) sacc[qb][j] = 0.f;
+        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
         {
-            const int krow = wave * 32 + c32;
             const uint16_t *kr = Kb + krow * D;
             const int sk = TL::swz_k(krow);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const uint4 ka = *(const uint4 *)(kr + ((2 * s + hi) ^ sk) * 8);
-                sacc[0] = TR::mfma(ka, qf[0][s], sacc[0]);
-                sacc[1] = TR::mfma(ka, qf[1][s], sacc[1]);
+                sacc = TR::mfma(ka, qf[s], sacc);
             }
         }
 
         // Accumulator register j of lane (c32, hi) holds key
-        // kbase + 8*(j/4) + 4*hi + (j%4) for query column c32 (+32*qb).
-        const int kbase = kt * kBK + wave * 32;
+        // kbase + 8*(j/4) + 4*hi + (j%4) for query column qc.
+        const int kbase = kt * kBK + ks * 32;
         const bool full = (kt * kBK >= sv.key_lo) && ((kt + 1) * kBK <= sv.n_keys) &&
                           ((kt + 1) * kBK - 1 <= sv.causal_base + r0);
         if (maskp) {
+            const uint16_t *mrow = maskp + (int64_t)qrow * a.mask_ld;
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const uint16_t *mrow = maskp + (int64_t)qrow[qb] * a.mask_ld;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
-                    const float mv = key < sv.n_keys ? TR::to_f32(mrow[key]) : 0.f;
-                    const bool vis = key >= sv.key_lo && key < sv.n_keys;
-                    sacc[qb][j] = vis ? sacc[qb][j] + mv * inv_scale : -INFINITY;
-                }
+            for (int j = 0; j < 16; ++j) {
+                const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
+                const int mk = key < sv.n_keys ? key : sv.n_keys - 1;
+                const float mv = TR::to_f32(mrow[mk]);
+                const bool vis = key >= sv.key_lo && key < sv.n_keys;
+                sacc[j] = vis ? sacc[j] + mv * inv_scale : -INFINITY;
             }
         } else if (!full) {
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
-                    const bool vis = key >= sv.key_lo && key <= lim[qb] && key < sv.n_keys;
-                    sacc[qb][j] = vis ? sacc[qb][j] : -INFINITY;
-                }
+            for (int j = 0; j < 16; ++j) {
+                const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
+                const bool vis = key >= sv.key_lo && key <= lim && key < sv.n_keys;
+                sacc[j] = vis ? sacc[j] : -INFINITY;
+            }
         }
 
         // online softmax (exp2 domain), lazy maximum
-        uint4 pb[2][2];
+        float mx = sacc[0];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float mx = sacc[qb][0];
+        for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[j]);
+        mx = pair_max(mx);
+        const float mt = mx * c;
+        const bool need = mt > m_run + kLazyLog2;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            const float alpha = need ? exp2f(m_run - mt) : 1.0f;
+            m_run = need ? mt : m_run;
+            l_run *= alpha;
 #pragma unroll
-            for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[qb][j]);
-            mx = pair_max(mx);
-            const float mt = mx * c;
-            const bool need = mt > m_run[qb] + kLazyLog2;
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                const float alpha = need ? exp2f(m_run[qb] - mt) : 1.0f;
-                m_run[qb] = need ? mt : m_run[qb];
-                l_run[qb] *= alpha;
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+                for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+        }
+        const float mu = m_run == -INFINITY ? 0.f : m_run;
+        uint4 pb[2];
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) oacc[qb][db][j] *= alpha;
+        for (int s2 = 0; s2 < 2; ++s2) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * s2 + 2 * i], c, -mu));
+                const float p1 =
+                    __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * s2 + 2 * i + 1], c, -mu));
+                w[i] = TR::pack(p0, p1);
+                l_run = TR::dot2(w[i], TR::kOnes, l_run);
             }
-            const float mu = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                uint32_t w[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p0 =
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][8 * s2 + 2 * i], c, -mu));
-                    const float p1 =
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][8 * s2 + 2 * i + 1], c, -mu));
-                    w[i] = TR::from_f32(p0) | (TR::from_f32(p1) << 16);
-                    l_run[qb] = TR::dot2(w[i], TR::kOnes, l_run[qb]);
-                }
-                pb[qb][s2] = make_uint4(w[0], w[1], w[2], w[3]);
-            }
+            pb[s2] = make_uint4(w[0], w[1], w[2], w[3]);
         }
 
         // O^T[d x cols] += V^T[d x 32 keys] P^T[32 keys x cols]
@@ -364,7 +364,7 @@ void attn_mfma_kernel(AttnArgs a)
                 uint2 half[2];
 #pragma unroll
                 for (int j2 = 0; j2 < 2; ++j2) {
-                    const int vrow = wave * 32 + 16 * s2 + 8 * j2 + vrow_off;
+                    const int vrow = vrow_off + 16 * s2 + 8 * j2;
                     const int dd = 32 * db + vcol;
                     const uint16_t *vp =
                         Vb + vrow * D + (((dd >> 3) ^ TL::swz_v(vrow)) << 3) + (dd & 7);
@@ -372,29 +372,25 @@ void attn_mfma_kernel(AttnArgs a)
                     half[j2] = __builtin_bit_cast(uint2, r);
                 }
                 const uint4 va = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
-                oacc[0][db] = TR::mfma(va, pb[0][s2], oacc[0][db]);
-                oacc[1][db] = TR::mfma(va, pb[1][s2], oacc[1][db]);
+                oacc[db] = TR::mfma(va, pb[s2], oacc[db]);
             }
     }
     __syncthreads();   // all waves are done with the tiles: reuse LDS below
 
-    // ---- merge the four waves' partial states, normalise, write rows
+    // ---- merge the four key slices' partial states, normalise, write rows
     float *Ms = (float *)smem;
     float *Ls = Ms + 4 * kQC;
     float *Os = Ls + 4 * kQC;
     constexpr int OS = TL::OS;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const float lt = pair_sum(l_run[qb]);
+    {
+        const float lt = pair_sum(l_run);
         if (hi == 0) {
-            Ms[wave * kQC + qb * 32 + c32] = m_run[qb];
-            Ls[wave * kQC + qb * 32 + c32] = lt;
+            Ms[ks * kQC + qc] = m_run;
+            Ls[ks * kQC + qc] = lt;
         }
     }
     __syncthreads();
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int qc = qb * 32 + c32;
+    {
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < 4; ++w) M = fmaxf(M, Ms[w * kQC + qc]);
@@ -404,7 +400,7 @@ void attn_mfma_kernel(AttnArgs a)
             const float mw = Ms[w * kQC + qc];
             const float e = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
             den += e * Ls[w * kQC + qc];
-            if (w == wave) mine = e;
+            if (w == ks) mine = e;
         }
         const float f = den > 0.f ? mine / den : 0.f;
 #pragma unroll
@@ -412,33 +408,35 @@ void attn_mfma_kernel(AttnArgs a)
 #pragma unroll
             for (int j4 = 0; j4 < 4; ++j4) {
                 const int d = db * 32 + 8 * j4 + 4 * hi;
-                float4 v4 = make_float4(oacc[qb][db][4 * j4] * f, oacc[qb][db][4 * j4 + 1] * f,
-                                        oacc[qb][db][4 * j4 + 2] * f, oacc[qb][db][4 * j4 + 3] * f);
-                *(float4 *)(Os + (wave * kQC + qc) * OS + d) = v4;
+                float4 v4 = make_float4(oacc[db][4 * j4] * f, oacc[db][4 * j4 + 1] * f,
+                                        oacc[db][4 * j4 + 2] * f, oacc[db][4 * j4 + 3] * f);
+                *(float4 *)(Os + (ks * kQC + qc) * OS + d) = v4;
             }
     }
     __syncthreads();
     {
-        const int qc = tid >> 2;
-        const int part = tid & 3;
-        const int row = r0 + qc / G;
-        if (qc < BR * G && row < sv.out_rows) {
-            const int head = g * G + qc % G;
+        constexpr int PARTS = kThreads / kQC;    // threads per query column
+        constexpr int DP = D / PARTS;            // output elements per thread
+        const int oc = tid / PARTS;
+        const int part = tid % PARTS;
+        const int row = r0 + oc / G;
+        if (oc < BR * G && row < sv.out_rows) {
+            const int head = g * G + oc % G;
             uint16_t *op = (uint16_t *)a.out + ((int64_t)(sv.out_row0 + row) * a.Hq + head) * D +
-                           part * (D / 4);
+                           part * DP;
 #pragma unroll
-            for (int d8 = 0; d8 < D / 4; d8 += 8) {
+            for (int d8 = 0; d8 < DP; d8 += 8) {
                 uint32_t w[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float x0 = 0.f, x1 = 0.f;
-                    const int d = part * (D / 4) + d8 + 2 * i;
+                    const int d = part * DP + d8 + 2 * i;
 #pragma unroll
                     for (int w4 = 0; w4 < 4; ++w4) {
-                        x0 += Os[(w4 * kQC + qc) * OS + d];
-                        x1 += Os[(w4 * kQC + qc) * OS + d + 1];
+                        x0 += Os[(w4 * kQC + oc) * OS + d];
+                        x1 += Os[(w4 * kQC + oc) * OS + d + 1];
                     }
-                    w[i] = TR::from_f32(x0) | (TR::from_f32(x1) << 16);
+                    w[i] = TR::pack(x0, x1);
                 }
                 *(uint4 *)(op + d8) = make_uint4(w[0], w[1], w[2], w[3]);
             }
