@@ -139,16 +139,16 @@ __device__ __forceinline__ float pair_sum(float x)
 template <int D>
 struct Tile {
     static constexpr int NCH = D / 8;                 // 16-byte chunks per key row
-    static constexpr int STAGE = 2 * kBK * D;         // K then V, uint16 elements
+    static constexpr int STAGE = 2 * kBK * D;         // one buffer: K then V, uint16 elements
     static constexpr int LOADS = kBK * NCH / kThreads;   // 16-byte loads per thread per tensor
     static constexpr int WAVES = kThreads / 64;
-    static constexpr int OS = D + 4;                  // epilogue row stride (floats)
-    static constexpr int LOOP_BYTES = 2 * STAGE * 2;
-    static constexpr int EPI_BYTES = (4 * kQC * OS + 2 * 4 * kQC) * 4;
-    static constexpr int BYTES = LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES;
+    static constexpr int D4 = D / 4;                  // float4 columns of an epilogue row
     // chunk swizzles: stored position = chunk ^ swizzle(row)
     static __device__ __forceinline__ int swz_k(int row) { return row % NCH; }
     static __device__ __forceinline__ int swz_v(int row) { return (row % (NCH / 4)) << 2; }
+    // epilogue rows (one query column of one key slice, D floats) are
+    // float4-swizzled by the column index instead of padded
+    static __device__ __forceinline__ int swz_o(int col) { return col & (D4 - 1); }
 };
 
 struct SeqView {
@@ -181,7 +181,12 @@ void attn_mfma_kernel(AttnArgs a)
     constexpr int NS = D / 16;      // k-steps of the QK^T contraction
     constexpr int NDB = D / 32;     // 32-wide d blocks of O^T
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[TL::BYTES / 2];
+    // Two separately declared tile buffers (K then V in each): the compiler
+    // can then tell that reading one while the other is being filled by
+    // direct loads needs no wait for those loads.
+    __shared__ __attribute__((aligned(16))) uint16_t buf0[TL::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t buf1[TL::STAGE];
+    __shared__ float ml[2 * 4 * kQC];
 
     SeqView sv;
     if (!resolve_seq(a, blockIdx.z, sv)) return;
@@ -194,7 +199,7 @@ void attn_mfma_kernel(AttnArgs a)
     const int r0 = (blockIdx.x / a.Hkv) * BR;
     if (r0 >= sv.rows) return;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int lane = tid & 63;
     const int c32 = lane & 31;
     const int hi = lane >> 5;
@@ -229,25 +234,47 @@ void attn_mfma_kernel(AttnArgs a)
     const int t_last = (key_end - 1) / kBK;
 
     // ---- direct global->LDS tile loads: load i of this wave fills LDS
-    // chunks [(i*WAVES + wave)*64, +64) of the tile, one 16-byte chunk per lane
-    auto issue_tile = [&](int kt, int buf) {
-        uint16_t *Kb = smem + buf * TL::STAGE;
-        uint16_t *Vb = Kb + kBK * D;
+    // chunks [(i*WAVES + wave)*64, +64) of the tile, one 16-byte chunk per
+    // lane.  The per-lane element offsets inside a tile are loop invariant;
+    // each tile adds one uniform base, and only a tile that runs past the
+    // last valid key clamps its rows (to re-read the last valid key).
+    uint32_t koff[TL::LOADS], voff[TL::LOADS];   // byte offsets inside a tile
+    int lrow[TL::LOADS];
 #pragma unroll
-        for (int i = 0; i < TL::LOADS; ++i) {
-            const int blk = i * TL::WAVES + wave;
-            const int t = blk * 64 + lane;
-            const int row = t / NCH;
-            const int pos = t % NCH;
-            const int key = min(kt * kBK + row, sv.n_keys - 1);
-            const uint16_t *ksrc = kc + (int64_t)key * D + (pos ^ TL::swz_k(row)) * 8;
-            const uint16_t *vsrc = vc + (int64_t)key * D + (pos ^ TL::swz_v(row)) * 8;
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)ksrc,
-                (__attribute__((address_space(3))) void *)(Kb + blk * 64 * 8), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)vsrc,
-                (__attribute__((address_space(3))) void *)(Vb + blk * 64 * 8), 16, 0, 0);
+    for (int i = 0; i < TL::LOADS; ++i) {
+        const int t = (i * TL::WAVES + wave) * 64 + lane;
+        const int row = t / NCH;
+        const int pos = t % NCH;
+        lrow[i] = row;
+        koff[i] = (uint32_t)(row * D + (pos ^ TL::swz_k(row)) * 8) * 2u;
+        voff[i] = (uint32_t)(row * D + (pos ^ TL::swz_v(row)) * 8) * 2u;
+    }
+    auto load16 = [](const char *src, uint16_t *dst) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    };
+    auto issue_tile = [&](int kt, uint16_t *Kb) {
+        uint16_t *Vb = Kb + kBK * D;
+        const int key0 = kt * kBK;
+        const char *kt_base = (const char *)(kc + (int64_t)key0 * D);
+        const char *vt_base = (const char *)(vc + (int64_t)key0 * D);
+        if (key0 + kBK <= sv.n_keys) {
+#pragma unroll
+            for (int i = 0; i < TL::LOADS; ++i) {
+                const int blk = i * TL::WAVES + wave;
+                load16(kt_base + koff[i], Kb + blk * 64 * 8);
+                load16(vt_base + voff[i], Vb + blk * 64 * 8);
+            }
+        } else {
+            // the tile runs past the last valid key: those rows re-read it
+#pragma unroll
+            for (int i = 0; i < TL::LOADS; ++i) {
+                const int blk = i * TL::WAVES + wave;
+                const uint32_t back =
+                    (uint32_t)max(0, key0 + lrow[i] - (sv.n_keys - 1)) * (uint32_t)(D * 2);
+                load16(kt_base + (koff[i] - back), Kb + blk * 64 * 8);
+                load16(vt_base + (voff[i] - back), Vb + blk * 64 * 8);
+            }
         }
     };
 
@@ -275,15 +302,24 @@ void attn_mfma_kernel(AttnArgs a)
     const int vcol = 16 * g16 + 4 * (si & 3);            // + 32*db
     const int krow = ks * 32 + c32;
 
-    if (t_last >= t_first) issue_tile(t_first, 0);
-
-    for (int kt = t_first; kt <= t_last; ++kt) {
-        const int buf = (kt - t_first) & 1;
+    // one tile: wait for its loads, start the next tile's loads into the
+    // other buffer, then compute on this one
+    auto tile_step = [&](int kt, const uint16_t *Kb, uint16_t *next) {
         __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of tile kt have landed
-        __syncthreads();                   // ... and every wave's; buf^1 is free again
-        if (kt < t_last) issue_tile(kt + 1, buf ^ 1);
-
-        const uint16_t *Kb = smem + buf * TL::STAGE;
+        __syncthreads();                   // ... and every wave's; `next` is free again
+        // explicit additive mask values of this tile (loaded before the next
+        // tile's loads, so waiting for them does not wait for those)
+        const int kbase = kt * kBK + ks * 32;
+        float mvals[16];
+        if (maskp) {
+            const uint16_t *mrow = maskp + (int64_t)qrow * a.mask_ld;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
+                mvals[j] = TR::to_f32(mrow[key < sv.n_keys ? key : sv.n_keys - 1]);
+            }
+        }
+        if (kt < t_last) issue_tile(kt + 1, next);
         const uint16_t *Vb = Kb + kBK * D;
 
         // S^T[32 keys x 32 cols] for this wave's key slice and column group
@@ -302,18 +338,17 @@ void attn_mfma_kernel(AttnArgs a)
 
         // Accumulator register j of lane (c32, hi) holds key
         // kbase + 8*(j/4) + 4*hi + (j%4) for query column qc.
-        const int kbase = kt * kBK + ks * 32;
         const bool full = (kt * kBK >= sv.key_lo) && ((kt + 1) * kBK <= sv.n_keys) &&
                           ((kt + 1) * kBK - 1 <= sv.causal_base + r0);
         if (maskp) {
-            const uint16_t *mrow = maskp + (int64_t)qrow * a.mask_ld;
+            // additive mask; entries at or below the fill value (-32768)
+            // exclude the slot (their weight underflows to exactly 0
+            // whenever the row sees any slot)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
-                const int mk = key < sv.n_keys ? key : sv.n_keys - 1;
-                const float mv = TR::to_f32(mrow[mk]);
-                const bool vis = key >= sv.key_lo && key < sv.n_keys;
-                sacc[j] = vis ? sacc[j] + mv * inv_scale : -INFINITY;
+                const bool vis = key >= sv.key_lo && key < sv.n_keys && mvals[j] > -32768.0f;
+                sacc[j] = vis ? sacc[j] + mvals[j] * inv_scale : -INFINITY;
             }
         } else if (!full) {
 #pragma unroll
@@ -374,14 +409,23 @@ void attn_mfma_kernel(AttnArgs a)
                 const uint4 va = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
                 oacc[db] = TR::mfma(va, pb[s2], oacc[db]);
             }
+    };
+
+    if (t_last >= t_first) issue_tile(t_first, buf0);
+    for (int kt = t_first; kt <= t_last; kt += 2) {
+        tile_step(kt, buf0, buf1);
+        if (kt + 1 <= t_last) tile_step(kt + 1, buf1, buf0);
     }
     __syncthreads();   // all waves are done with the tiles: reuse LDS below
 
     // ---- merge the four key slices' partial states, normalise, write rows
-    float *Ms = (float *)smem;
-    float *Ls = Ms + 4 * kQC;
-    float *Os = Ls + 4 * kQC;
-    constexpr int OS = TL::OS;
+    // (slices 0-1 stage their rows in buf0, slices 2-3 in buf1)
+    float *Ms = ml;
+    float *Ls = ml + 4 * kQC;
+    auto orow = [&](int slice, int col) -> float * {
+        float *base = (float *)(slice < 2 ? buf0 : buf1);
+        return base + ((slice & 1) * kQC + col) * D;
+    };
     {
         const float lt = pair_sum(l_run);
         if (hi == 0) {
@@ -403,14 +447,16 @@ void attn_mfma_kernel(AttnArgs a)
             if (w == ks) mine = e;
         }
         const float f = den > 0.f ? mine / den : 0.f;
+        float *dst = orow(ks, qc);
+        const int sw = TL::swz_o(qc);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int j4 = 0; j4 < 4; ++j4) {
-                const int d = db * 32 + 8 * j4 + 4 * hi;
+                const int d4 = db * 8 + 2 * j4 + hi;     // float4 column of d = 4*d4
                 float4 v4 = make_float4(oacc[db][4 * j4] * f, oacc[db][4 * j4 + 1] * f,
                                         oacc[db][4 * j4 + 2] * f, oacc[db][4 * j4 + 3] * f);
-                *(float4 *)(Os + (ks * kQC + qc) * OS + d) = v4;
+                *(float4 *)(dst + 4 * (d4 ^ sw)) = v4;
             }
     }
     __syncthreads();
@@ -424,6 +470,7 @@ void attn_mfma_kernel(AttnArgs a)
             const int head = g * G + oc % G;
             uint16_t *op = (uint16_t *)a.out + ((int64_t)(sv.out_row0 + row) * a.Hq + head) * D +
                            part * DP;
+            const int sw = TL::swz_o(oc);
 #pragma unroll
             for (int d8 = 0; d8 < DP; d8 += 8) {
                 uint32_t w[4];
@@ -431,10 +478,12 @@ void attn_mfma_kernel(AttnArgs a)
                 for (int i = 0; i < 4; ++i) {
                     float x0 = 0.f, x1 = 0.f;
                     const int d = part * DP + d8 + 2 * i;
+                    const int off = 4 * ((d >> 2) ^ sw) + (d & 3);
 #pragma unroll
                     for (int w4 = 0; w4 < 4; ++w4) {
-                        x0 += Os[(w4 * kQC + oc) * OS + d];
-                        x1 += Os[(w4 * kQC + oc) * OS + d + 1];
+                        const float *src = orow(w4, oc);
+                        x0 += src[off];
+                        x1 += src[off + 1];
                     }
                     w[i] = TR::pack(x0, x1);
                 }
