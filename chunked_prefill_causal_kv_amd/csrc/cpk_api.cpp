@@ -296,7 +296,7 @@ int cpk_varlen_step(const void *q, const void *k_new, const void *v_new,
     std::vector<char> used((size_t)cache->batch, 0);
     int max_ctx = 0, max_rows = 0, n_dec = 0, n_pre = 0;
     const int G = q_heads / cache->kv_heads;
-    const bool dec_ok = cpk::decode_supported(cache->dtype, cache->head_dim, G);
+    const bool dec_ok = cpk::decode_supported(cache->dtype, cache->head_dim, G, cache->capacity);
     for (int s = 0; s < n_seqs; ++s) {
         const int rows = h_cu_rows[s + 1] - h_cu_rows[s];
         if (rows < 1) return fail(CPK_EINVAL, "varlen: sequence %d has %d rows", s, rows);

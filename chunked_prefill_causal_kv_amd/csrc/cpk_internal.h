@@ -53,7 +53,7 @@ struct DecodeArgs {
     const void *k;      // cache
     const void *v;
     void *out;
-    float *ws;          // partials [n_seqs][Hq][max_segs][D + 2] (m, l, acc[D])
+    float *ws;          // partials [n_seqs][Hq][max_segs][D + 4] (m, l, pad, pad, acc[D])
     int Hq, Hkv, D, cap;
     float scale_log2;
     int max_segs;       // segments allocated per (seq, head) in ws
@@ -64,7 +64,7 @@ struct DecodeArgs {
     int n_seqs;
 };
 
-constexpr int kDecodeSeg = 256;   // keys per decode work item
+constexpr int kDecodeSeg = 256;   // keys per decode work item (4 waves x 64)
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_kv_append(const void *k_new, const void *v_new, void *ck, void *cv,
@@ -86,6 +86,6 @@ hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_
                             hipStream_t st);
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int max_segs, hipStream_t st);
-bool decode_supported(int dtype, int D, int group);
+bool decode_supported(int dtype, int D, int group, int capacity);
 
 }  // namespace cpk

@@ -7,15 +7,22 @@
 //
 // * Split-KV: a work item is (sequence, KV head, 256-key segment), so a
 //   batch of sequences with contexts from hundreds to tens of thousands of
-//   keys turns into thousands of equal-sized items that fill all CUs.
+//   keys turns into thousands of short, equal-sized items; the dispatcher's
+//   tail at the end of the grid is then a small part of the step.
 // * GQA packing: the G query heads of one KV head are computed together,
 //   so each K/V byte is read from HBM once per KV head, not once per query
 //   head.
-// * Each key row is read by 8 lanes; lane j reads bytes [16j, 16j+16) and
-//   [128+16j, 128+16j+16) of the row, so every load instruction of a wave
-//   covers whole 128-byte lines of 8 consecutive keys.  QK^T uses packed
-//   2-element dot products (v_dot2_f32_{bf16,f16}) in fp32, reduced across
-//   the 8 lanes with butterflies; PV accumulates in fp32.
+// * A key row is spread over D/8 lanes, 16 bytes (8 elements) per lane, so
+//   a wave's load instruction covers whole 128-byte lines of consecutive
+//   keys.  Each of the 4 waves streams 64 keys in steps of 4 keys per lane
+//   group, with the next step's K/V loads in flight while the current step
+//   computes (double buffering in registers, non-temporal loads).
+// * QK^T: packed 2-element dot products (v_dot2_f32_{bf16,f16}) in fp32,
+//   summed over the lane group with DPP butterflies that leave identical
+//   bits in every lane.  Softmax is online per query head with a lazy
+//   running maximum.  P is rounded to the storage type in pairs of keys, so
+//   PV is again packed dot products, over two keys at a time, accumulated
+//   in fp32; the running sum adds the same rounded P.
 // * Keys at or past the sequence's length are never loaded.
 //
 // decode_combine merges the per-segment (max, sum, acc) partials of every
@@ -36,12 +43,16 @@ struct DBf16 {
         return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                                __builtin_bit_cast(bf16x2_t, b), c, false);
     }
-    static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
-    static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
     static __device__ __forceinline__ uint32_t from_f32(float x)
     {
         return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
     }
+    static __device__ __forceinline__ uint32_t pack(float lo, float hi)
+    {
+        const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    static constexpr uint32_t kOnes = 0x3F803F80u;   // (1.0, 1.0)
 };
 
 struct DF16 {
@@ -50,37 +61,81 @@ struct DF16 {
         return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a),
                                       __builtin_bit_cast(f16x2_t, b), c, false);
     }
-    static __device__ __forceinline__ float lo(uint32_t x)
-    {
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
-    }
-    static __device__ __forceinline__ float hi(uint32_t x)
-    {
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
-    }
     static __device__ __forceinline__ uint32_t from_f32(float x)
     {
         return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
     }
+    static __device__ __forceinline__ uint32_t pack(float lo, float hi)
+    {
+        const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    static constexpr uint32_t kOnes = 0x3C003C00u;   // (1.0, 1.0)
 };
 
-constexpr int kThreadsDec = 256;
-constexpr int kGroups = kThreadsDec / 8;            // 32 key lanes-groups per item
-constexpr int kKeysPerGroup = kDecodeSeg / kGroups; // 8
+constexpr int kThreadsDec = 256;                               // 4 waves
+constexpr int kKeysPerWave = kDecodeSeg / (kThreadsDec / 64);   // 64
+constexpr int kKK = 4;              // keys per lane group per streaming step
+constexpr float kLazyLog2Dec = 8.0f;
 
 __device__ __forceinline__ uint32_t dw(const uint4 &v, int j)
 {
     return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
-template <typename TR, int D, int G>
-__global__ __launch_bounds__(kThreadsDec) void decode_kernel(DecodeArgs a)
+// Sum over the LPK lanes (8 or 16) of an aligned lane group, returned in all
+// of them with identical bits: xor-1 and xor-2 exchanges (quad permutes), a
+// half-row mirror (lane i <-> 7 - i) and, for 16 lanes, a row mirror
+// (lane i <-> 15 - i).  Each step adds two operands in both orders, so all
+// lanes of the group end with the same value.  All are DPP register moves.
+template <int LPK>
+__device__ __forceinline__ float group_sum(float x)
 {
-    constexpr int NCH = D / 64;              // 16-byte chunks per lane per row
-    constexpr int WS = D + 4;                // workspace record: m, l, pad, pad, acc[D]
-    __shared__ float Mg[kGroups][G];
-    __shared__ float Lg[kGroups][G];
-    __shared__ __attribute__((aligned(16))) float Ag[kGroups][G][D];
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0xB1, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x4E, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x141, 0xF, 0xF, false));
+    if constexpr (LPK == 16)
+        x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                   0x140, 0xF, 0xF, false));
+    return x;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Cache rows are read once per decode step: non-temporal loads keep them from
+// displacing reusable lines in the caches.
+__device__ __forceinline__ uint4 load_stream(const char *base, uint32_t off)
+{
+    const u32x4 t = __builtin_nontemporal_load((const u32x4 *)(base + off));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+struct KVStep {
+    uint4 k[kKK];
+    uint4 v[kKK];
+};
+
+// waves per SIMD the register budget is held to (G = 8 keeps 2: its
+// accumulators alone need 64 VGPRs)
+template <int G>
+constexpr int decode_waves() { return G <= 4 ? 3 : 2; }
+
+template <typename TR, int D, int G>
+__global__ __launch_bounds__(kThreadsDec)
+__attribute__((amdgpu_waves_per_eu(decode_waves<G>())))
+void decode_kernel(DecodeArgs a)
+{
+    constexpr int LPK = D / 8;                 // lanes per key row, 16 bytes each
+    constexpr int GPW = 64 / LPK;              // lane groups per wave
+    constexpr int NG = GPW * (kThreadsDec / 64);   // lane groups per workgroup
+    constexpr int STEP = GPW * kKK;            // keys per wave per step
+    constexpr int WS = D + 4;                  // workspace record: m, l, pad, pad, acc[D]
+    __shared__ float Mg[NG][G];
+    __shared__ float Lg[NG][G];
+    __shared__ __attribute__((aligned(16))) float Ag[NG][G][D];
 
     const int z = blockIdx.z;
     const int row0 = a.cu_rows[z];
@@ -92,90 +147,133 @@ __global__ __launch_bounds__(kThreadsDec) void decode_kernel(DecodeArgs a)
     const int g = blockIdx.y;
     const int slot = a.slots[z];
     const int tid = threadIdx.x;
-    const int gi = tid >> 3;
-    const int j = tid & 7;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int gq = lane / LPK;                 // lane group inside the wave
+    const int gi = wave * GPW + gq;            // lane group inside the workgroup
+    const int j = lane % LPK;                  // this lane's 8 elements: [8j, 8j + 8)
 
-    const uint16_t *kc = (const uint16_t *)a.k + ((int64_t)slot * a.Hkv + g) * a.cap * D;
-    const uint16_t *vc = (const uint16_t *)a.v + ((int64_t)slot * a.Hkv + g) * a.cap * D;
+    // uniform bases of this (slot, KV head); per-lane 32-bit byte offsets
+    const int64_t head_off = ((int64_t)slot * a.Hkv + g) * a.cap * D * 2;
+    const char *kbase = (const char *)a.k + head_off;
+    const char *vbase = (const char *)a.v + head_off;
 
-    // query slices of the G heads of this KV head
-    uint4 qv[G][NCH];
-    const uint16_t *qp = (const uint16_t *)a.q + ((int64_t)row0 * a.Hq + g * G) * D;
+    uint4 qv[G];
+    const uint16_t *qp = (const uint16_t *)a.q + ((int64_t)row0 * a.Hq + g * G) * D + 8 * j;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
-            qv[h][ch] = *(const uint4 *)(qp + (int64_t)h * D + ch * 64 + 8 * j);
+    for (int h = 0; h < G; ++h) qv[h] = *(const uint4 *)(qp + (int64_t)h * D);
 
-    uint4 kr[kKeysPerGroup][NCH], vr[kKeysPerGroup][NCH];
+    // the wave streams keys [wbase, wlast]; in step st, lane group gq takes
+    // keys wbase + st*STEP + kKK*gq + (0 .. kKK-1).  Keys are clamped to
+    // wlast, so a step past the end re-reads only that row.
+    const int wbase = sb + wave * kKeysPerWave;
+    const int wlast = min(n_keys, wbase + kKeysPerWave) - 1;
+    auto load_step = [&](int st, KVStep &b) __attribute__((always_inline)) {
+        const int key0 = wbase + st * STEP + kKK * gq;
 #pragma unroll
-    for (int it = 0; it < kKeysPerGroup; ++it) {
-        const int key = sb + gi + kGroups * it;
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-            if (key < n_keys) {
-                kr[it][ch] = *(const uint4 *)(kc + (int64_t)key * D + ch * 64 + 8 * j);
-                vr[it][ch] = *(const uint4 *)(vc + (int64_t)key * D + ch * 64 + 8 * j);
-            } else {
-                kr[it][ch] = make_uint4(0, 0, 0, 0);
-                vr[it][ch] = make_uint4(0, 0, 0, 0);
-            }
+        for (int kk = 0; kk < kKK; ++kk) {
+            const uint32_t off = (uint32_t)min(key0 + kk, wlast) * (D * 2) + 16u * j;
+            b.k[kk] = load_stream(kbase, off);
+            b.v[kk] = load_stream(vbase, off);
         }
-    }
+    };
 
-    // scores in the exp2 domain
-    float s[kKeysPerGroup][G];
-#pragma unroll
-    for (int it = 0; it < kKeysPerGroup; ++it) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float acc = 0.f;
-#pragma unroll
-            for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) acc = TR::dot2(dw(qv[h][ch], w), dw(kr[it][ch], w), acc);
-            acc += __shfl_xor(acc, 1, 8);
-            acc += __shfl_xor(acc, 2, 8);
-            acc += __shfl_xor(acc, 4, 8);
-            const int key = sb + gi + kGroups * it;
-            s[it][h] = key < n_keys ? acc * a.scale_log2 : -INFINITY;
-        }
-    }
-
-    // per-group softmax over its keys, then P V
-    float m[G], l[G], o[G][NCH * 8];
+    float m[G], l[G], o[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        m[h] = s[0][h];
-#pragma unroll
-        for (int it = 1; it < kKeysPerGroup; ++it) m[h] = fmaxf(m[h], s[it][h]);
+        m[h] = -INFINITY;
         l[h] = 0.f;
 #pragma unroll
-        for (int e = 0; e < NCH * 8; ++e) o[h][e] = 0.f;
-    }
-#pragma unroll
-    for (int it = 0; it < kKeysPerGroup; ++it) {
-        float p[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            p[h] = (m[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[it][h] - m[h]);
-            l[h] += p[h];
-        }
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t x = dw(vr[it][ch], w);
-                const float v0 = TR::lo(x), v1 = TR::hi(x);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    o[h][ch * 8 + 2 * w] = __builtin_fmaf(p[h], v0, o[h][ch * 8 + 2 * w]);
-                    o[h][ch * 8 + 2 * w + 1] = __builtin_fmaf(p[h], v1, o[h][ch * 8 + 2 * w + 1]);
-                }
-            }
+        for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
     }
 
-    // merge the 32 groups of this item
+    const float c = a.scale_log2;   // > 0: the maximum of raw scores is the maximum of scaled ones
+    auto compute_step = [&](int st, const KVStep &b) __attribute__((always_inline)) {
+        const int key0 = wbase + st * STEP + kKK * gq;
+        float s[kKK][G];
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk)
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float acc = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) acc = TR::dot2(dw(qv[h], w), dw(b.k[kk], w), acc);
+                s[kk][h] = group_sum<LPK>(acc);
+            }
+        if (wbase + (st + 1) * STEP - 1 > wlast) {   // wave-uniform: the step has keys past wlast
+#pragma unroll
+            for (int kk = 0; kk < kKK; ++kk)
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                    if (key0 + kk > wlast) s[kk][h] = -INFINITY;
+        }
+        // online softmax per head with a lazy maximum: the reference m (log2
+        // domain) is raised only when a step's maximum exceeds it by more
+        // than 2^8.  p is rounded to the storage type in pairs of keys, and l
+        // sums the rounded values, so the normalisation matches what PV uses.
+        uint32_t pp[kKK / 2][G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float mx = s[0][h];
+#pragma unroll
+            for (int kk = 1; kk < kKK; ++kk) mx = fmaxf(mx, s[kk][h]);
+            mx *= c;
+            if (mx > m[h] + kLazyLog2Dec) {
+                const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
+                m[h] = mx;
+                l[h] *= alpha;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+            }
+            const float mu = m[h] == -INFINITY ? 0.f : m[h];
+#pragma unroll
+            for (int t = 0; t < kKK / 2; ++t) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * t][h], c, -mu));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * t + 1][h], c, -mu));
+                pp[t][h] = TR::pack(p0, p1);
+                l[h] = TR::dot2(pp[t][h], TR::kOnes, l[h]);
+            }
+        }
+        // PV over key pairs: (v_k0[d], v_k1[d]) . (p_k0, p_k1) with packed dots
+#pragma unroll
+        for (int t = 0; t < kKK / 2; ++t)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x0 = dw(b.v[2 * t], w), x1 = dw(b.v[2 * t + 1], w);
+                const uint32_t ev = __builtin_amdgcn_perm(x1, x0, 0x05040100u);   // element 2w
+                const uint32_t od = __builtin_amdgcn_perm(x1, x0, 0x07060302u);   // element 2w+1
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    o[h][2 * w] = TR::dot2(pp[t][h], ev, o[h][2 * w]);
+                    o[h][2 * w + 1] = TR::dot2(pp[t][h], od, o[h][2 * w + 1]);
+                }
+            }
+    };
+
+    // stream the wave's keys: step st + 1 is in flight while step st
+    // computes.  The step loop is unrolled in full (its length is fixed) so
+    // that no buffer is carried around a loop back edge: the compiler then
+    // keeps each prefetch in place and its wait counts exact.  The step count
+    // is rounded up to even: a step past wlast scores all its keys -inf
+    // (weight 0), and the prefetch after the last pair is a clamped re-read.
+    constexpr int kSteps = kKeysPerWave / STEP;
+    const int steps = wlast >= wbase ? (wlast - wbase + STEP) / STEP : 0;
+    if (steps > 0) {
+        KVStep b0, b1;
+        load_step(0, b0);
+#pragma unroll
+        for (int st = 0; st < kSteps; st += 2) {
+            if (st >= steps) break;   // wave-uniform
+            load_step(st + 1, b1);
+            __builtin_amdgcn_sched_barrier(0);   // issue the prefetch before any wait
+            compute_step(st, b0);
+            if (st + 2 < kSteps) load_step(st + 2, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(st + 1, b1);
+        }
+    }
+
+    // merge the lane groups of this work item
     if (j == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -184,24 +282,22 @@ __global__ __launch_bounds__(kThreadsDec) void decode_kernel(DecodeArgs a)
         }
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-            float *dst = &Ag[gi][h][ch * 64 + 8 * j];
-            *(float4 *)dst = make_float4(o[h][ch * 8], o[h][ch * 8 + 1], o[h][ch * 8 + 2],
-                                         o[h][ch * 8 + 3]);
-            *(float4 *)(dst + 4) = make_float4(o[h][ch * 8 + 4], o[h][ch * 8 + 5],
-                                               o[h][ch * 8 + 6], o[h][ch * 8 + 7]);
-        }
+    for (int h = 0; h < G; ++h) {
+        float *dst = &Ag[gi][h][8 * j];
+        *(float4 *)dst = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+        *(float4 *)(dst + 4) = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+    }
     __syncthreads();
 
     for (int idx = tid; idx < G * D; idx += kThreadsDec) {
         const int h = idx / D;
         const int d = idx % D;
         float M = -INFINITY;
-        for (int q = 0; q < kGroups; ++q) M = fmaxf(M, Mg[q][h]);
+#pragma unroll
+        for (int q = 0; q < NG; ++q) M = fmaxf(M, Mg[q][h]);
         float acc = 0.f, lsum = 0.f;
-        for (int q = 0; q < kGroups; ++q) {
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
             const float mq = Mg[q][h];
             const float e = (mq == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mq - M);
             acc = __builtin_fmaf(e, Ag[q][h][d], acc);
@@ -216,10 +312,21 @@ __global__ __launch_bounds__(kThreadsDec) void decode_kernel(DecodeArgs a)
     }
 }
 
+// Merge the segment partials of one (sequence, query head).  One thread per
+// output column d.  The maximum over all segments is found with a block
+// reduction; segment weights exp2(m_s - M) and sums l_s are then staged in
+// LDS, kCombineChunk segments at a time, and every thread accumulates its
+// column over the segments in increasing order (deterministic, no atomics).
+constexpr int kCombineChunk = 256;
+
 template <typename TR, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a)
 {
     constexpr int WS = D + 4;
+    constexpr int NW = D / 64;
+    __shared__ float we[kCombineChunk];
+    __shared__ float wl[kCombineChunk];
+    __shared__ float wmax[NW];
     const int z = blockIdx.y;
     const int row0 = a.cu_rows[z];
     if (a.cu_rows[z + 1] - row0 != 1) return;
@@ -228,14 +335,34 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a)
     const int head = blockIdx.x;
     const int d = threadIdx.x;
     const float *rec = a.ws + ((int64_t)z * a.Hq + head) * a.max_segs * WS;
+
     float M = -INFINITY;
-    for (int s = 0; s < n_segs; ++s) M = fmaxf(M, rec[s * WS]);
+    for (int s = d; s < n_segs; s += D) M = fmaxf(M, rec[(int64_t)s * WS]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if ((d & 63) == 0) wmax[d >> 6] = M;
+    __syncthreads();
+    M = wmax[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, wmax[w]);
+
     float acc = 0.f, lsum = 0.f;
-    for (int s = 0; s < n_segs; ++s) {
-        const float ms = rec[s * WS];
-        const float e = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-        acc = __builtin_fmaf(e, rec[s * WS + 4 + d], acc);
-        lsum = __builtin_fmaf(e, rec[s * WS + 1], lsum);
+    for (int s0 = 0; s0 < n_segs; s0 += kCombineChunk) {
+        const int cnt = min(kCombineChunk, n_segs - s0);
+        __syncthreads();
+        for (int s = d; s < cnt; s += D) {
+            const float *r = rec + (int64_t)(s0 + s) * WS;
+            const float ms = r[0];
+            we[s] = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+            wl[s] = r[1];
+        }
+        __syncthreads();
+        const float *col = rec + (int64_t)s0 * WS + 4 + d;
+#pragma unroll 4
+        for (int s = 0; s < cnt; ++s) {
+            acc = __builtin_fmaf(we[s], col[(int64_t)s * WS], acc);
+            lsum = __builtin_fmaf(we[s], wl[s], lsum);
+        }
     }
     const float r = lsum > 0.f ? acc / lsum : 0.f;
     uint16_t *op = (uint16_t *)a.out + ((int64_t)row0 * a.Hq + head) * D;
@@ -260,10 +387,12 @@ hipError_t launch_decode_t(const DecodeArgs &a, int G, int max_segs, hipStream_t
 
 }  // namespace
 
-bool decode_supported(int dtype, int D, int group)
+bool decode_supported(int dtype, int D, int group, int capacity)
 {
+    // key rows are addressed with 32-bit byte offsets inside one (slot, head)
     return (dtype == 1 || dtype == 2) && (D == 64 || D == 128) &&
-           (group == 1 || group == 2 || group == 4 || group == 8);
+           (group == 1 || group == 2 || group == 4 || group == 8) &&
+           (int64_t)capacity * D * 2 <= (int64_t)UINT32_MAX;
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int max_segs, hipStream_t st)

@@ -171,7 +171,9 @@ int cpk_prefill_chunk(const void *q, const void *k, const void *v,
 /*
  * Device workspace bytes cpk_varlen_step needs for a step of n_seqs
  * sequences whose longest decode context (keys a one-row sequence reads)
- * is max_ctx.
+ * is max_ctx: n_seqs * q_heads * ceil(max_ctx / 256) * (head_dim + 4) * 4,
+ * one fp32 record (running max, sum, partial output) per query head and
+ * 256-key slice of a decode row's context.
  */
 size_t cpk_varlen_workspace_size(int n_seqs, int q_heads, int max_ctx,
                                  int head_dim);

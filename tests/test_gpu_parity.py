@@ -356,3 +356,59 @@ def test_workload5_mixed_full_size_budget_2048():
     steps = _run_mixed(64, 512, 16384, 20000, 2048, 32, 8, 128, seed=si.SEEDS["mixed"],
                        cap=20480, check_steps={0, 10}, every=211)
     assert steps == 11
+
+
+# ------------------------------------------------ decode rows, every variant
+
+# past lengths around the decode kernel's boundaries: 16/32-key streaming
+# steps, 64-key waves, 256-key work items, and many work items
+DECODE_PAST = [0, 1, 14, 15, 16, 31, 32, 255, 256, 511, 1022, 1023, 1024, 2047, 2500, 4095]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_rows_every_variant(dtype, D, G):
+    """Decode-only varlen step (one row per sequence) against the oracle for
+    every (dtype, head_dim, group) the decode kernel is built for.  The
+    cache is NaN past each sequence's length, and every third query is
+    scaled by 8 so its scores span far more than the lazy maximum's 2^8
+    window (the running reference must be raised mid-stream)."""
+    Hkv, n, cap = 2, len(DECODE_PAST), 4096
+    Hq = G * Hkv
+    sdt = "bf16" if dtype == torch.bfloat16 else "f16"
+    odt = ODT[dtype]
+    seed = 900 + 10 * D + G + (0 if dtype == torch.bfloat16 else 5)
+    say(f"case: decode rows {sdt} D={D} G={G} Hkv={Hkv} past {DECODE_PAST[0]}..{DECODE_PAST[-1]}")
+    cache = cpk.KVCache(n, Hkv, cap, D, dtype)
+    poison(cache)
+    full_k = si.fill_seeded(torch.empty_like(cache.k), seed)
+    full_v = si.fill_seeded(torch.empty_like(cache.v), seed + 1)
+    for s, p in enumerate(DECODE_PAST):
+        cache.k[s, :, :p] = full_k[s, :, :p]
+        cache.v[s, :, :p] = full_v[s, :, :p]
+    del full_k, full_v
+    cache.lens = list(DECODE_PAST)
+    g = si.generator(seed + 2)
+    q = si.randn((n, Hq, D), sdt, g).cuda()
+    q[::3] *= 8
+    kn = si.randn((n, Hkv, D), sdt, g).cuda()
+    vn = si.randn((n, Hkv, D), sdt, g).cuda()
+    out = cpk.cpk_varlen_step(q, kn, vn, cache, list(range(n)), list(range(n + 1)), DECODE_PAST)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for s, p in enumerate(DECODE_PAST):
+        nk = p + 1
+        assert np.array_equal(si.storage(cache.k[s, :, p]), si.storage(kn[s]))
+        assert np.array_equal(si.storage(cache.v[s, :, p]), si.storage(vn[s]))
+        kk = oracle.widen(si.storage(cache.k[s, :, :nk]), odt)
+        vv = oracle.widen(si.storage(cache.v[s, :, :nk]), odt)
+        qq = oracle.widen(si.storage(q[s:s + 1]), odt)
+        ref = oracle.attention(qq, kk, vv, np.zeros(1, np.int32), np.array([p], np.int32),
+                               1.0 / math.sqrt(D))
+        g64 = f64(out[s:s + 1])
+        assert np.isfinite(g64).all(), f"past {p}: non-finite"
+        err = float(np.max(np.abs(g64 - ref)))
+        worst = max(worst, err)
+        assert err <= 2e-2, f"past {p}: max-abs {err}"
+    say(f"  {n} decode rows: worst max-abs err {worst:.3e} (tol 2e-2)")
