@@ -35,7 +35,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_w512_traffic.txt")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_64seq_traffic.txt")
 ATTN_SRC = os.path.join(ROOT, "chunked_prefill_causal_kv_amd", "csrc", "k_attn.hip")
+DECODE_SRC = os.path.join(ROOT, "chunked_prefill_causal_kv_amd", "csrc", "k_decode.hip")
 
 
 def log(*a):
@@ -49,18 +51,22 @@ def chunk_flops(past, real, Hq, D):
     return 4 * D * Hq * pairs
 
 
-def attn_src_sha():
-    with open(ATTN_SRC, "rb") as f:
+def src_sha(path=ATTN_SRC):
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(sha):
-    """Measured HBM bytes per attention launch from the committed counter
-    summary, or None if absent or taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def attn_src_sha():
+    return src_sha(ATTN_SRC)
+
+
+def read_traffic(sha, path=TRAFFIC_FILE):
+    """Measured HBM bytes per launch from a committed counter summary, or
+    None if absent or taken on a different kernel source."""
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
@@ -175,9 +181,15 @@ def bench_decode(cpk, si, torch, reps=10):
     kv_bytes = sum((c + 1) * Hkv * D * 2 * 2 for c in ctxs)
     io_bytes = n * Hq * D * 2 * 2 + n * Hkv * D * 2 * 2 * 2
     gbps = (kv_bytes + io_bytes) / (ms * 1e-3) / 1e9
+    sha = src_sha(DECODE_SRC)
     return {"sequences": n, "kv_gb": round(kv_bytes / 1e9, 3), "ms": round(ms, 4),
             "GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-            "note": "whole packed step (append + split-KV decode + combine)"}
+            "note": "whole packed step (append + split-KV decode + combine)",
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                         "traffic": read_traffic(sha, DECODE_TRAFFIC_FILE),
+                         "kernel": "decode_kernel<bf16,128,4> + decode_combine (whole step)",
+                         "kernel_source_sha": sha}}
 
 
 def calibrate_copy(cpk, torch, reps=3):
