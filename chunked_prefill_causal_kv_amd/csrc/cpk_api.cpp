@@ -183,7 +183,7 @@ int cpk_kv_append(const cpk_kv_cache *cache, int b, const void *k_new, const voi
     const int rb = cache->head_dim * elem_size(cache->dtype);
     return hip_status(cpk::launch_kv_append(k_new, v_new, cache->k, cache->v, cache->seqlens_k,
                                             cache->kv_heads, cache->capacity, rb, b, past_len,
-                                            rows, real_rows, (hipStream_t)stream),
+                                            rows, real_rows, past_len + rows, (hipStream_t)stream),
                       "kv_append launch");
 }
 
@@ -255,15 +255,15 @@ int cpk_prefill_chunk(const void *q, const void *k, const void *v, const cpk_kv_
                     past_len, width, cache->capacity);
     hipStream_t st = (hipStream_t)stream;
     const int rb = cache->head_dim * elem_size(cache->dtype);
+    // the append writes the padded rows but records the true length
+    // past_len + real_rows (the rewind of the padding, folded into the copy;
+    // attention takes its key range from its arguments, not from seqlens_k)
     r = hip_status(cpk::launch_kv_append(k, v, cache->k, cache->v, cache->seqlens_k,
                                          cache->kv_heads, cache->capacity, rb, b, past_len, width,
-                                         real_rows, st),
+                                         real_rows, past_len + real_rows, st),
                    "prefill_chunk append");
     if (r) return r;
     r = attention_common(q, cache, b, q_heads, past_len, width, real_rows, scale, out, st);
-    if (r) return r;
-    r = hip_status(cpk::launch_set_len(cache->seqlens_k, b, past_len + real_rows, st),
-                   "prefill_chunk rewind");
     if (r) return r;
     if (issued_rows) *issued_rows = width;
     return ok();

@@ -69,7 +69,7 @@ constexpr int kDecodeSeg = 256;   // keys per decode work item (4 waves x 64)
 // Launchers (return hipError_t of the launch).
 hipError_t launch_kv_append(const void *k_new, const void *v_new, void *ck, void *cv,
                             int32_t *seqlens, int Hkv, int cap, int row_bytes, int slot,
-                            int past, int rows, int src_rows, hipStream_t st);
+                            int past, int rows, int src_rows, int len_after, hipStream_t st);
 hipError_t launch_kv_append_varlen(const void *k_new, const void *v_new, void *ck, void *cv,
                                    int32_t *seqlens, int Hkv, int cap, int row_bytes,
                                    const int32_t *cu_rows, const int32_t *past_lens,

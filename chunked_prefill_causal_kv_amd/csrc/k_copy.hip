@@ -12,13 +12,14 @@ namespace {
 
 typedef uint4 vec16;  // 16 bytes
 
-// cache[slot][h][past + r][:] = new[min(r, src_rows - 1)][h][:]
-// Rows past src_rows repeat the last real row: the query-axis padding of the
-// ONNX GenAI Wiki "Chunked Prefill", section 4, done as an index clamp.
+// cache[slot][h][past + r][:] = new[min(r, src_rows - 1)][h][:], then
+// seqlens[slot] = len_after.  Rows past src_rows repeat the last real row:
+// the query-axis padding of the ONNX GenAI Wiki "Chunked Prefill", section
+// 4, done as an index clamp.
 __global__ void kv_append_kernel(const vec16 *__restrict__ kn, const vec16 *__restrict__ vn,
                                  vec16 *__restrict__ ck, vec16 *__restrict__ cv,
                                  int32_t *__restrict__ seqlens, int Hkv, int cap, int vpr,
-                                 int slot, int past, int rows, int src_rows)
+                                 int slot, int past, int rows, int src_rows, int len_after)
 {
     const int64_t total = (int64_t)rows * Hkv * vpr;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -33,7 +34,7 @@ __global__ void kv_append_kernel(const vec16 *__restrict__ kn, const vec16 *__re
         ck[dst] = kn[src];
         cv[dst] = vn[src];
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0 && seqlens) seqlens[slot] = past + rows;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && seqlens) seqlens[slot] = len_after;
 }
 
 // Packed step: row t of the packed k_new/v_new belongs to the sequence s with
@@ -118,13 +119,13 @@ int grid_for(int64_t items)
 
 hipError_t launch_kv_append(const void *k_new, const void *v_new, void *ck, void *cv,
                             int32_t *seqlens, int Hkv, int cap, int row_bytes, int slot,
-                            int past, int rows, int src_rows, hipStream_t st)
+                            int past, int rows, int src_rows, int len_after, hipStream_t st)
 {
     const int vpr = row_bytes / 16;
     const int64_t items = (int64_t)rows * Hkv * vpr;
     hipLaunchKernelGGL(kv_append_kernel, dim3(grid_for(items)), dim3(256), 0, st,
                        (const vec16 *)k_new, (const vec16 *)v_new, (vec16 *)ck, (vec16 *)cv,
-                       seqlens, Hkv, cap, vpr, slot, past, rows, src_rows);
+                       seqlens, Hkv, cap, vpr, slot, past, rows, src_rows, len_after);
     return hipGetLastError();
 }
 

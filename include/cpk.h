@@ -155,10 +155,11 @@ int cpk_rewind(const cpk_kv_cache *cache, int b, int new_len, int cur_len,
  * v by repeating their last real row; append every padded row; attend
  * every padded row; write the real rows to out; rewind the cache to
  * past_len + real_rows.  q [real_rows][q_heads][D], k/v
- * [real_rows][kv_heads][D], out [real_rows][q_heads][D].  Equivalent to
+ * [real_rows][kv_heads][D], out [real_rows][q_heads][D].  Same result as
  * cpk_kv_append(rows = width) + cpk_chunk_attention(rows = width) +
- * cpk_rewind(past_len + real_rows); the padding is an index clamp inside
- * the kernels, so no scratch memory is used.
+ * cpk_rewind(past_len + real_rows), in two launches (the append records the
+ * true length); the padding is an index clamp inside the kernels, so no
+ * scratch memory is used.
  * *issued_rows (may be NULL) receives the padded width.
  * CPK_EINVAL if real_rows < 1 or real_rows > W; CPK_ECAPACITY if the
  * padded rows do not fit.
