@@ -322,7 +322,11 @@ void attn_mfma_kernel(AttnArgs a)
         if (kt < t_last) issue_tile(kt + 1, next);
         const uint16_t *Vb = Kb + kBK * D;
 
-        // S^T[32 keys x 32 cols] for this wave's key slice and column group
+        // S^T[32 keys x 32 cols] for this wave's key slice and column group.
+        // Matrix sections run at raised wave priority: the wave that reaches
+        // them first keeps the matrix pipe while its SIMD partner does vector
+        // work, which de-phases the two waves of a SIMD.
+        __builtin_amdgcn_s_setprio(1);
         f32x16_t sacc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
@@ -335,6 +339,7 @@ void attn_mfma_kernel(AttnArgs a)
                 sacc = TR::mfma(ka, qf[s], sacc);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
 
         // Accumulator register j of lane (c32, hi) holds key
         // kbase + 8*(j/4) + 4*hi + (j%4) for query column qc.
@@ -392,6 +397,7 @@ void attn_mfma_kernel(AttnArgs a)
         }
 
         // O^T[d x cols] += V^T[d x 32 keys] P^T[32 keys x cols]
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -409,6 +415,7 @@ void attn_mfma_kernel(AttnArgs a)
                 const uint4 va = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
                 oacc[db] = TR::mfma(va, pb[s2], oacc[db]);
             }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     if (t_last >= t_first) issue_tile(t_first, buf0);

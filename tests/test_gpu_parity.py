@@ -290,6 +290,57 @@ def test_workload4_rolling_full_size():
     check(out[torch.from_numpy(rows).cuda()], ref, 2e-2, f"sliding window ({len(rows)} rows)")
 
 
+# ------------------------------------------------ HIP graph replay
+
+def test_graph_replay_of_chunked_prefill():
+    """A chunked prefill (rewind, then cpk_prefill_chunk per chunk with the
+    padded tail) captured once as a HIP graph: every replay, with eager work
+    between replays, matches the eager run bit for bit (output, cache rows,
+    seqlens_k)."""
+    say("case: HIP graph of rewind + padded chunked prefill (L=1300, W=512), 3 replays")
+    L, W, Hq, Hkv, D = 1300, 512, 16, 4, 128
+    q, k, v = si.gqa_prompt(L=L, Hq=Hq, Hkv=Hkv, D=D, seed=700)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    cache = cpk.KVCache(1, Hkv, 2048, D, torch.bfloat16)
+    out = torch.empty_like(qd)
+    chunks = cpk.cpk_split_chunks(L, W)
+
+    def run():
+        cpk.cpk_rewind(cache, 0, 0)
+        for past, rows in chunks:
+            sl = slice(past, past + rows)
+            cpk.cpk_prefill_chunk(qd[sl], kd[sl], vd[sl], cache, 0, past, W, pad=True,
+                                  out=out[sl])
+
+    run()
+    torch.cuda.synchronize()
+    ref_out, ref_k, ref_v = out.clone(), cache.k[:, :, :L].clone(), cache.v[:, :, :L].clone()
+    assert int(cache.seqlens_k[0]) == L
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        poison(cache)
+        cache.seqlens_k.fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert bitwise(out, ref_out), f"replay {rep}: output differs"
+        assert bitwise(cache.k[:, :, :L], ref_k) and bitwise(cache.v[:, :, :L], ref_v)
+        assert int(cache.seqlens_k[0]) == L
+        run()   # eager work between replays
+        torch.cuda.synchronize()
+        assert bitwise(out, ref_out)
+    say("  3 replays bit-identical to the eager run")
+
+
 # ------------------------------------------------ workload 5: mixed varlen
 
 def _run_mixed(n_dec, ctx_lo, ctx_hi, prompt, budget, Hq, Hkv, D, seed, cap, check_steps, every):
