@@ -17,8 +17,10 @@ roofline = the attention kernel alone: per-launch algorithmic flops over its
          the bf16 dense MFMA peak of 2.5 PFLOP/s.
 secondary = decode rows of the mixed-step workload (64 sequences, contexts
          uniform in [512, 16384]) as a decode-only packed step: KV bytes read
-         per second against the 8 TB/s HBM peak; plus a steady-state W=512
-         chunk at past_len 7680.
+         per second against the 8 TB/s HBM peak; a steady-state W=512 chunk
+         at past_len 7680; the ladder prompts (useful and issued TFLOP/s);
+         the rolling fp16 cache; the mixed decode + prefill step at budgets
+         2048 and 8192 against its sum and max bounds.
 cpu_baseline = the fp64 CPU oracle timed on this host on a bounded sample of
          the same workload (query rows of the prompt in seeded random order),
          same flop accounting.
@@ -248,6 +250,166 @@ def bench_decode(cpk, si, torch, reps=10):
                          "kernel_source_sha": sha}}
 
 
+def issued_pairs(past, width):
+    """(query, key) pairs of `width` rows at past: row i sees past + i + 1 keys."""
+    return width * past + width * (width + 1) // 2
+
+
+def bench_ladder(cpk, si, torch, reps=2):
+    """Ladder workload: seven prompts (five seeded lengths, 1137, 1200), each
+    prefilled twice on the same cache without clearing, through
+    cpk_prefill_chunk with padding on.  Useful flops count real rows only,
+    issued flops the padded widths."""
+    Hq, Hkv, D, W, CAP = 32, 8, 128, 512, 8192
+    lengths = si.ladder_prompt_lengths()
+    prompts = [tuple(x.cuda() for x in si.gqa_prompt(L=L, seed=200 + i))
+               for i, L in enumerate(lengths)]
+    cache = cpk.KVCache(1, Hkv, CAP, D, torch.bfloat16)
+    outs = [torch.empty_like(p[0]) for p in prompts]
+    useful = issued = 0
+    for L in lengths:
+        for past, rows in cpk.cpk_split_chunks(L, W):
+            useful += issued_pairs(past, rows)
+            issued += issued_pairs(past, cpk.cpk_ladder_width(W, rows))
+
+    def run():
+        for (q, k, v), out, L in zip(prompts, outs, lengths):
+            for _ in range(reps):
+                if cache.lens[0]:
+                    cpk.cpk_rewind(cache, 0, 0)
+                for past, rows in cpk.cpk_split_chunks(L, W):
+                    sl = slice(past, past + rows)
+                    cpk.cpk_prefill_chunk(q[sl], k[sl], v[sl], cache, 0, past, W, pad=True,
+                                          out=out[sl])
+
+    run()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    f_useful = 4 * D * Hq * useful * reps
+    f_issued = 4 * D * Hq * issued * reps
+    return {"prompts": lengths, "runs_each": reps, "ms": round(ms, 3),
+            "useful_gflop": round(f_useful / 1e9, 2), "issued_gflop": round(f_issued / 1e9, 2),
+            "useful_tflops": round(f_useful / (ms * 1e-3) / 1e12, 1),
+            "issued_tflops": round(f_issued / (ms * 1e-3) / 1e12, 1),
+            "note": "eager cpk_prefill_chunk calls (append + attention per chunk)"}
+
+
+def bench_rolling(cpk, si, torch, explicit_mask=True):
+    """Rolling right-aligned cache: 4096 fp16 tokens, 16 heads, C = 2048,
+    c = 256; per chunk roll_append (out of place, double-buffered) then
+    roll_attention with the explicit (c, C) additive mask (0 visible,
+    -32768 masked)."""
+    L, H, D, C, c = 4096, 16, 128, 2048, 256
+    q, k, v = (x.cuda() for x in si.rolling_inputs())
+    n = L // c
+    masks, pairs = [], 0
+    rows = torch.arange(c, device="cuda").unsqueeze(1)
+    slots = torch.arange(C, device="cuda").unsqueeze(0)
+    for j in range(n):
+        p = j * c + rows                       # absolute query positions
+        a = (j + 1) * c - C + slots            # absolute position held by each slot
+        vis = (a >= 0) & (a <= p)
+        masks.append(torch.where(vis, 0.0, -32768.0).to(torch.float16).contiguous())
+        pairs += int(vis.sum())
+    bufs = [torch.zeros((1, H, C, D), dtype=torch.float16, device="cuda") for _ in range(4)]
+    out = torch.empty_like(q)
+
+    def run():
+        cur = 0
+        for j in range(n):
+            sl = slice(j * c, (j + 1) * c)
+            ko, vo = bufs[2 * cur], bufs[2 * cur + 1]
+            kn, vn = bufs[2 * (1 - cur)], bufs[2 * (1 - cur) + 1]
+            cpk.cpk_roll_append(ko, vo, k[sl].unsqueeze(0), v[sl].unsqueeze(0), kn, vn)
+            cur = 1 - cur
+            cpk.cpk_roll_attention(q[sl], kn[0], vn[0], (j + 1) * c, 0,
+                                   mask=masks[j] if explicit_mask else None, out=out[sl])
+
+    run()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    f = 4 * D * H * pairs
+    how = "the explicit (c, C) mask" if explicit_mask else "visibility computed in the kernel"
+    return {"chunks": n, "gflop": round(f / 1e9, 2), "ms": round(ms, 4),
+            "tflops": round(f / (ms * 1e-3) / 1e12, 1), "dtype": "fp16",
+            "note": f"roll_append + roll_attention with {how}, per chunk"}
+
+
+def bench_mixed(cpk, si, torch, budget):
+    """Mixed step: 64 running decodes (contexts U[512, 16384]) plus a
+    20,000-token prompt under a token budget, one cpk_varlen_step per step
+    (packed inputs built before timing).  Each step is compared with
+    sum = bytes/HBM + flops/MFMA and max = max of the two (perfect overlap)."""
+    Hq, Hkv, D, CAP, P = 32, 8, 128, 20480, 20000
+    ctxs = si.mixed_contexts()
+    n_dec = len(ctxs)
+    cache = cpk.KVCache(n_dec + 1, Hkv, CAP, D, torch.bfloat16)
+    si.fill_seeded(cache.k, 31)
+    si.fill_seeded(cache.v, 32)
+    pq, pk, pv = (x.cuda() for x in si.gqa_prompt(L=P, seed=33))
+    g = si.generator(34)
+    steps, done, lens = [], 0, list(ctxs)
+    while done < P:
+        rows = cpk.cpk_plan_step(budget, n_dec, P - done)
+        dq = si.randn((n_dec, Hq, D), "bf16", g).cuda()
+        dk = si.randn((n_dec, Hkv, D), "bf16", g).cuda()
+        dv = si.randn((n_dec, Hkv, D), "bf16", g).cuda()
+        q = torch.cat([dq, pq[done:done + rows]])
+        kn = torch.cat([dk, pk[done:done + rows]])
+        vn = torch.cat([dv, pv[done:done + rows]])
+        slots = list(range(n_dec + 1))
+        cu = list(range(n_dec + 1)) + [n_dec + rows]
+        past = lens + [done]
+        meta = torch.tensor(slots + cu + past, dtype=torch.int32).cuda()
+        ws = torch.empty(cpk.cpk_varlen_workspace_size(n_dec + 1, Hq, max(lens) + 1, D) // 4 + 4,
+                         dtype=torch.float32, device="cuda")
+        kv_bytes = sum((x + 1) * Hkv * D * 2 * 2 for x in lens) + (done + rows) * Hkv * D * 2 * 2
+        flops = 4 * D * Hq * (issued_pairs(done, rows) + sum(x + 1 for x in lens))
+        steps.append((q, kn, vn, slots, cu, past, meta, ws, torch.empty_like(q), kv_bytes, flops))
+        lens = [x + 1 for x in lens]
+        done += rows
+
+    def run(events=None):
+        for i, (q, kn, vn, slots, cu, past, meta, ws, out, _, _) in enumerate(steps):
+            if events is not None:
+                events[i][0].record(torch.cuda.current_stream())
+            cpk.cpk_varlen_step(q, kn, vn, cache, slots, cu, past, out=out, ws=ws, dev_meta=meta)
+            if events is not None:
+                events[i][1].record(torch.cuda.current_stream())
+
+    run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in steps]
+    run(evs)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    table = []
+    for (*_, kv_bytes, flops), m in zip(steps, ms):
+        t_mem = kv_bytes / (PEAK_HBM_GBPS * 1e9) * 1e3
+        t_mma = flops / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+        table.append({"ms": round(m, 4), "sum_bound_ms": round(t_mem + t_mma, 4),
+                      "max_bound_ms": round(max(t_mem, t_mma), 4),
+                      "tflops": round(flops / (m * 1e-3) / 1e12, 1)})
+    tot = sum(ms)
+    return {"budget": budget, "steps": len(steps), "ms_total": round(tot, 3),
+            "ms_per_step": round(tot / len(steps), 4),
+            "sum_bound_ms_total": round(sum(t["sum_bound_ms"] for t in table), 3),
+            "max_bound_ms_total": round(sum(t["max_bound_ms"] for t in table), 3),
+            "per_step": table}
+
+
 def calibrate_copy(cpk, torch, reps=3):
     """A plain copy of known size for scaling HBM counters: roll_append with
     c = 1 reads K and V caches of 32 heads x 16384 x 128 bf16 (2 x 128 MiB)
@@ -331,6 +493,18 @@ def main():
         secondary["decode_rows"] = bench_decode(cpk, si, torch)
         log(f"bench: decode {secondary['decode_rows']}")
         secondary["per_chunk"] = r["table"]
+        secondary["ladder"] = bench_ladder(cpk, si, torch)
+        log(f"bench: ladder {secondary['ladder']}")
+        secondary["rolling_fp16"] = bench_rolling(cpk, si, torch)
+        log(f"bench: rolling {secondary['rolling_fp16']}")
+        secondary["rolling_fp16_computed_mask"] = bench_rolling(cpk, si, torch, False)
+        log(f"bench: rolling {secondary['rolling_fp16_computed_mask']}")
+        for budget in (2048, 8192):
+            mixed = bench_mixed(cpk, si, torch, budget)
+            secondary[f"mixed_budget_{budget}"] = mixed
+            log(f"bench: mixed budget {budget}: {mixed['ms_per_step']} ms/step over "
+                f"{mixed['steps']} steps (bounds: sum {mixed['sum_bound_ms_total']} ms, "
+                f"max {mixed['max_bound_ms_total']} ms in total)")
     sha = attn_src_sha()
     value = r["total_flops"] / (ms_graph * 1e-3) / 1e12
     line = {

@@ -313,10 +313,26 @@ void attn_mfma_kernel(AttnArgs a)
         float mvals[16];
         if (maskp) {
             const uint16_t *mrow = maskp + (int64_t)qrow * a.mask_ld;
+            if ((a.mask_ld & 3) == 0 && ((uintptr_t)maskp & 7u) == 0) {
+                // the lane's 16 keys are 4 runs of 4 consecutive keys: one
+                // 8-byte load per run (a run starting at or past the row's
+                // end is re-read from the row's last run; those keys are
+                // masked out below whatever the values)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
-                mvals[j] = TR::to_f32(mrow[key < sv.n_keys ? key : sv.n_keys - 1]);
+                for (int r = 0; r < 4; ++r) {
+                    const int key0 = min(kbase + 8 * r + 4 * hi, a.mask_ld - 4);
+                    const uint2 w = *(const uint2 *)(mrow + key0);
+                    mvals[4 * r + 0] = TR::to_f32(w.x & 0xffffu);
+                    mvals[4 * r + 1] = TR::to_f32(w.x >> 16);
+                    mvals[4 * r + 2] = TR::to_f32(w.y & 0xffffu);
+                    mvals[4 * r + 3] = TR::to_f32(w.y >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
+                    mvals[j] = TR::to_f32(mrow[key < sv.n_keys ? key : sv.n_keys - 1]);
+                }
             }
         }
         if (kt < t_last) issue_tile(kt + 1, next);
