@@ -32,6 +32,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -125,8 +126,9 @@ def bench_chunked(cpk, si, torch, steps, warmup):
     kern_ms = [sum(c) / len(c) for c in per_chunk_ms]
     achieved = (total_flops / len(chunks)) / (sum(kern_ms) / len(chunks) * 1e-3) / 1e12
     table = [{"past_len": p, "rows": r, "gflop": round(f / 1e9, 3),
-              "ms": round(m, 4), "tflops": round(f / (m * 1e-3) / 1e12, 1)}
-             for (p, r), f, m in zip(chunks, flops, kern_ms)]
+              "ms": round(m, 4), "ms_median": round(statistics.median(c), 4),
+              "ms_min": round(min(c), 4), "tflops": round(f / (m * 1e-3) / 1e12, 1)}
+             for (p, r), f, m, c in zip(chunks, flops, kern_ms, per_chunk_ms)]
     return dict(ms_step=ms_step, total_flops=total_flops, achieved=achieved,
                 kern_ms_avg=sum(kern_ms) / len(kern_ms), table=table, chunks=chunks,
                 q=q, k=k, v=v)
