@@ -44,7 +44,7 @@ class cpk_kv_cache(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run "
-                          "`python -m chunked_prefill_causal_kv_amd.build`")
+                          "`python chunked_prefill_causal_kv_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     IP = ctypes.POINTER(ctypes.c_int)
@@ -66,7 +66,8 @@ def _load() -> ctypes.CDLL:
         "cpk_varlen_workspace_size": ([I, I, I, I], Z),
         "cpk_varlen_step": ([P, P, P, CP, P, P, P, I32P, I32P, I32P, I, I, I, F, P, P, Z, P], I),
         "cpk_roll_append": ([P, P, P, P, P, P, I, I, I, I, I, I, P], I),
-        "cpk_roll_attention": ([P, P, P, P, I, I, I, I, I, I, I, I, F, P, P], I),
+        "cpk_roll_attention": ([P, P, P, P, I, I, I, I, I, I, I, I, F, P, P, Z, P], I),
+        "cpk_roll_workspace_size": ([I, I, I, I, I, I], Z),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -269,16 +270,41 @@ def cpk_roll_append(k_old, v_old, k_chunk, v_chunk, k_new, v_new, stream=None):
                                 DTYPE_CODE[k_old.dtype], _stream(stream)))
 
 
+def cpk_roll_workspace_size(Hq: int, Hkv: int, C: int, c: int, head_dim: int, dtype) -> int:
+    return int(_lib.cpk_roll_workspace_size(Hq, Hkv, C, c, head_dim, DTYPE_CODE[dtype]))
+
+
+_roll_ws = {}
+
+
+def _roll_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    """A reusable device workspace of at least nbytes (None for 0)."""
+    if nbytes == 0:
+        return None
+    key = torch.device(device)
+    ws = _roll_ws.get(key)
+    if ws is None or ws.numel() * 4 < nbytes:
+        ws = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=key)
+        _roll_ws[key] = ws
+    return ws
+
+
 def cpk_roll_attention(q, k, v, abs_end: int, n_leftpad: int, mask=None, scale: float = 0.0,
-                       out=None, stream=None):
-    """q [c, Hq, D] over a rolling cache k/v [Hkv, C, D]."""
+                       out=None, stream=None, split: bool = True):
+    """q [c, Hq, D] over a rolling cache k/v [Hkv, C, D].  split=True passes
+    a workspace (the key range is split across workgroups when the shapes
+    call for it); split=False runs the unsplit kernel alone."""
     c, Hq, D = q.shape
     Hkv, C, _ = k.shape
     if out is None:
         out = torch.empty_like(q)
+    ws = None
+    if split:
+        ws = _roll_workspace(cpk_roll_workspace_size(Hq, Hkv, C, c, D, q.dtype), q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * 4
     _check(_lib.cpk_roll_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(mask), abs_end, n_leftpad,
                                    Hq, Hkv, C, c, D, DTYPE_CODE[q.dtype], float(scale),
-                                   _ptr(out), _stream(stream)))
+                                   _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
     return out
 
 
@@ -300,7 +326,8 @@ def prefill_chunked(cache: KVCache, b: int, q, k, v, W: int, pad: bool = True,
     return out, widths
 
 
-def roll_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream=None):
+def roll_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream=None,
+                 split: bool = True):
     """Rolling fixed-capacity prefill of one sequence (batch 1).  q/k/v are
     token-major real tokens; the sequence is left-padded with zero rows to a
     multiple of c.  masks: optional list of per-chunk (c, C) additive masks;
@@ -325,5 +352,5 @@ def roll_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream
         cur = 1 - cur
         m = None if masks is None else masks[j]
         cpk_roll_attention(q[sl], kn[0], vn[0], (j + 1) * c, n_left, mask=m, scale=scale,
-                           out=out[sl], stream=stream)
+                           out=out[sl], stream=stream, split=split)
     return out, n_left, bufs[2 * cur][0], bufs[2 * cur + 1][0]

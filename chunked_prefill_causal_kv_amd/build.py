@@ -1,6 +1,6 @@
 """Build libcpk.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-    python -m chunked_prefill_causal_kv_amd.build
+    python chunked_prefill_causal_kv_amd/build.py
 
 Every HIP source is compiled with packed-fp32 instruction selection turned
 off (``-Xclang -target-feature -Xclang -packed-fp32-ops``).

@@ -384,9 +384,41 @@ int cpk_roll_append(const void *k_old, const void *v_old, const void *k_chunk,
                       "roll_append launch");
 }
 
+// Key-range split of a rolling attention: parts of whole key tiles so that
+// (row blocks x KV heads x parts) reaches about kSplitTarget workgroups.  A
+// function of the shapes only, so the explicit-mask and computed-visibility
+// forms of one call split identically.
+static const int kSplitTarget = 256;
+
+static void roll_split(int Hq, int Hkv, int C, int c, int dtype, int *n_parts, int *part_tiles)
+{
+    *n_parts = 1;
+    *part_tiles = 0;
+    if (dtype == CPK_F32 || Hkv < 1 || Hq < Hkv || Hq % Hkv) return;
+    const int br = cpk::attn_rows_per_block(dtype, Hq / Hkv);
+    const int base = ((c + br - 1) / br) * Hkv;
+    const int tiles = (C + cpk::kAttnTileKeys - 1) / cpk::kAttnTileKeys;
+    int s = kSplitTarget / (base > 0 ? base : 1);
+    if (s > tiles) s = tiles;
+    if (s <= 1) return;
+    const int pt = (tiles + s - 1) / s;
+    *part_tiles = pt;
+    *n_parts = (tiles + pt - 1) / pt;
+}
+
+size_t cpk_roll_workspace_size(int Hq, int Hkv, int C, int c, int head_dim, int dtype)
+{
+    if (Hq < 1 || Hkv < 1 || C < 1 || c < 1 || head_dim < 1) return 0;
+    int parts, pt;
+    roll_split(Hq, Hkv, C, c, dtype, &parts, &pt);
+    if (parts <= 1) return 0;
+    return (size_t)parts * (size_t)c * (size_t)Hq * (size_t)(head_dim + 4) * sizeof(float);
+}
+
 int cpk_roll_attention(const void *q, const void *k, const void *v, const void *mask,
                        int abs_end, int n_leftpad, int Hq, int Hkv, int C, int c, int D,
-                       int dtype, float scale, void *out, void *stream)
+                       int dtype, float scale, void *out, void *ws, size_t ws_bytes,
+                       void *stream)
 {
     int r = check_dtype_dim(dtype, D);
     if (r) return r;
@@ -415,9 +447,24 @@ int cpk_roll_attention(const void *q, const void *k, const void *v, const void *
         a.key_lo = lo < 0 ? 0 : (lo > C ? C : (int)lo);
         a.causal_base = C - c;
     }
+    int parts = 1, pt = 0;
+    if (ws) {
+        roll_split(Hq, Hkv, C, c, dtype, &parts, &pt);
+        const size_t need = cpk_roll_workspace_size(Hq, Hkv, C, c, D, dtype);
+        if (ws_bytes < need)
+            return fail(CPK_EWORKSPACE, "roll_attention: workspace %zu bytes, need %zu", ws_bytes,
+                        need);
+        if (!aligned16(ws)) return fail(CPK_EALIGN, "roll_attention: workspace not aligned");
+    }
+    a.n_parts = parts;
+    a.part_tiles = pt;
+    a.part_ws = (float *)ws;
     const int br = cpk::attn_rows_per_block(dtype, Hq / Hkv);
-    return hip_status(cpk::launch_attention(a, dtype, (c + br - 1) / br, 1, (hipStream_t)stream),
-                      "roll_attention launch");
+    r = hip_status(cpk::launch_attention(a, dtype, (c + br - 1) / br, 1, (hipStream_t)stream),
+                   "roll_attention launch");
+    if (r || parts <= 1) return r;
+    return hip_status(cpk::launch_attention_combine(a, dtype, (hipStream_t)stream),
+                      "roll_attention combine");
 }
 
 }  // extern "C"

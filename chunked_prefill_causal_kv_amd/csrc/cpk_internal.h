@@ -45,6 +45,17 @@ struct AttnArgs {
     const int32_t *slots;
     int n_seqs;
     int min_rows;
+
+    // key-range split (scalar mode, bf16/fp16 only): grid.y = n_parts and
+    // part p covers the absolute key tiles [p * part_tiles, (p + 1) *
+    // part_tiles).  With n_parts > 1 each workgroup writes fp32 partial
+    // records [M, den, pad, pad, O[D]] (running maximum in the exp2 domain,
+    // sum and unnormalised output) per (row, query head) to
+    // part_ws[p][row][head] instead of the output; launch_attention_combine
+    // merges them in part order.
+    int n_parts;        // 1: no split
+    int part_tiles;
+    float *part_ws;
 };
 
 // Split-KV decode: one query row per sequence.
@@ -86,6 +97,11 @@ hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_
                             hipStream_t st);
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int max_segs, hipStream_t st);
+
+// Key tile of the bf16/fp16 attention kernel, and the merge of split parts
+// (a.n_parts > 1) into a.out.
+constexpr int kAttnTileKeys = 128;
+hipError_t launch_attention_combine(const AttnArgs &a, int dtype, hipStream_t st);
 bool decode_supported(int dtype, int D, int group, int capacity);
 
 }  // namespace cpk

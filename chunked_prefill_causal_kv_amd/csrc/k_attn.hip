@@ -121,6 +121,7 @@ struct F16 {
 constexpr int kQC = 64;         // query columns per workgroup (2 groups of 32)
 constexpr int kBK = 128;        // keys per LDS tile (4 slices of 32)
 constexpr int kThreads = 512;   // 8 waves = 2 column groups x 4 key slices
+static_assert(kBK == kAttnTileKeys, "split parts are counted in key tiles");
 constexpr float kLazyLog2 = 8.0f;
 
 // The two 32-lane halves of a wave hold the same query column (different
@@ -230,8 +231,13 @@ void attn_mfma_kernel(AttnArgs a)
     // ---- key range of this workgroup
     const int last_row = min(r0 + BR, sv.rows) - 1;
     const int key_end = min(sv.n_keys, sv.causal_base + last_row + 1);   // exclusive
-    const int t_first = sv.key_lo / kBK;
-    const int t_last = (key_end - 1) / kBK;
+    int t_first = sv.key_lo / kBK;
+    int t_last = (key_end - 1) / kBK;
+    if (a.n_parts > 1) {
+        // this workgroup's part of the key range (absolute tiles), possibly empty
+        t_first = max(t_first, (int)blockIdx.y * a.part_tiles);
+        t_last = min(t_last, ((int)blockIdx.y + 1) * a.part_tiles - 1);
+    }
 
     // ---- direct global->LDS tile loads: load i of this wave fills LDS
     // chunks [(i*WAVES + wave)*64, +64) of the tile, one 16-byte chunk per
@@ -469,7 +475,9 @@ void attn_mfma_kernel(AttnArgs a)
             den += e * Ls[w * kQC + qc];
             if (w == ks) mine = e;
         }
-        const float f = den > 0.f ? mine / den : 0.f;
+        // split parts keep the slices' sum unnormalised (the combine
+        // normalises over all parts); otherwise normalise here
+        const float f = a.n_parts > 1 ? mine : (den > 0.f ? mine / den : 0.f);
         float *dst = orow(ks, qc);
         const int sw = TL::swz_o(qc);
 #pragma unroll
@@ -489,7 +497,37 @@ void attn_mfma_kernel(AttnArgs a)
         const int oc = tid / PARTS;
         const int part = tid % PARTS;
         const int row = r0 + oc / G;
-        if (oc < BR * G && row < sv.out_rows) {
+        if (oc < BR * G && row < sv.out_rows && a.n_parts > 1) {
+            // partial record of this part: [M, den, 0, 0, O[D]]
+            const int head = g * G + oc % G;
+            float *rec =
+                a.part_ws + (((int64_t)blockIdx.y * sv.out_rows + row) * a.Hq + head) * (D + 4);
+            if (part == 0) {
+                float M = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) M = fmaxf(M, Ms[w * kQC + oc]);
+                float den = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float mw = Ms[w * kQC + oc];
+                    den += ((mw == -INFINITY) ? 0.f : exp2f(mw - M)) * Ls[w * kQC + oc];
+                }
+                *(float4 *)rec = make_float4(M, den, 0.f, 0.f);
+            }
+            const int sw = TL::swz_o(oc);
+#pragma unroll
+            for (int d4 = 0; d4 < DP; d4 += 4) {
+                const int d = part * DP + d4;
+                const int off = 4 * ((d >> 2) ^ sw);
+                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) {
+                    const float4 y = *(const float4 *)(orow(w4, oc) + off);
+                    x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+                }
+                *(float4 *)(rec + 4 + d) = x;
+            }
+        } else if (oc < BR * G && row < sv.out_rows) {
             const int head = g * G + oc % G;
             uint16_t *op = (uint16_t *)a.out + ((int64_t)(sv.out_row0 + row) * a.Hq + head) * D +
                            part * DP;
@@ -514,6 +552,31 @@ void attn_mfma_kernel(AttnArgs a)
             }
         }
     }
+}
+
+// Merge of the split parts of a key range: for each (row, query head), in
+// part order, M = max_p M_p, f_p = 2^(M_p - M), out = sum_p f_p O_p /
+// sum_p f_p den_p.  One thread per output element d.
+template <typename TR, int D>
+__global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a)
+{
+    const int row = blockIdx.x;
+    const int head = blockIdx.y;
+    const int d = threadIdx.x;
+    const int64_t stride = (int64_t)a.out_rows * a.Hq * (D + 4);
+    const float *rec = a.part_ws + ((int64_t)row * a.Hq + head) * (D + 4);
+    float M = -INFINITY;
+    for (int p = 0; p < a.n_parts; ++p) M = fmaxf(M, rec[p * stride]);
+    float num = 0.f, den = 0.f;
+    for (int p = 0; p < a.n_parts; ++p) {
+        const float *r = rec + p * stride;
+        const float f = (r[0] == -INFINITY) ? 0.f : exp2f(r[0] - M);
+        num = __builtin_fmaf(f, r[4 + d], num);
+        den = __builtin_fmaf(f, r[1], den);
+    }
+    const float o = den > 0.f ? num / den : 0.f;
+    uint16_t *op = (uint16_t *)a.out + ((int64_t)(a.out_row0 + row) * a.Hq + head) * D;
+    op[d] = (uint16_t)TR::from_f32(o);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -625,7 +688,7 @@ int attn_rows_per_block(int dtype, int group)
 hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
                             hipStream_t st)
 {
-    const dim3 grid(row_blocks * a.Hkv, 1, n_seq_grid);
+    const dim3 grid(row_blocks * a.Hkv, a.n_parts > 1 ? a.n_parts : 1, n_seq_grid);
     if (dtype == 0) {
         if (a.D == 64)
             hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, st, a);
@@ -641,6 +704,19 @@ hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_
             hipLaunchKernelGGL((attn_mfma_kernel<Bf16, 64>), grid, dim3(kThreads), 0, st, a);
         else
             hipLaunchKernelGGL((attn_mfma_kernel<Bf16, 128>), grid, dim3(kThreads), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_combine(const AttnArgs &a, int dtype, hipStream_t st)
+{
+    const dim3 grid(a.out_rows, a.Hq);
+    if (dtype == 1) {
+        if (a.D == 64) hipLaunchKernelGGL((attn_combine_kernel<F16, 64>), grid, dim3(64), 0, st, a);
+        else hipLaunchKernelGGL((attn_combine_kernel<F16, 128>), grid, dim3(128), 0, st, a);
+    } else {
+        if (a.D == 64) hipLaunchKernelGGL((attn_combine_kernel<Bf16, 64>), grid, dim3(64), 0, st, a);
+        else hipLaunchKernelGGL((attn_combine_kernel<Bf16, 128>), grid, dim3(128), 0, st, a);
     }
     return hipGetLastError();
 }

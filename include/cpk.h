@@ -228,12 +228,31 @@ int cpk_roll_append(const void *k_old, const void *v_old, const void *k_chunk,
  *         every row that sees at least one slot both forms give the same
  *         bits.
  *   out   [c][Hq][D]
- * CPK_EINVAL if c > C, abs_end < c or the sizes are inconsistent.
+ *   ws    NULL, or device workspace of at least
+ *         cpk_roll_workspace_size(...) bytes (owned by the caller, 16-byte
+ *         aligned, no initial contents needed).  With a workspace the key
+ *         range is split across workgroups (a chunk of c rows over C slots
+ *         otherwise occupies only (c / rows per block) x Hkv workgroups) and
+ *         the parts are merged in a fixed order by a second launch; the
+ *         result then differs from the unsplit one only by rounding.  Both
+ *         mask forms of one call split identically.
+ * CPK_EINVAL if c > C, abs_end < c or the sizes are inconsistent;
+ * CPK_EWORKSPACE if ws is too small.
  */
 int cpk_roll_attention(const void *q, const void *k, const void *v,
                        const void *mask, int abs_end, int n_leftpad, int Hq,
                        int Hkv, int C, int c, int D, int dtype, float scale,
-                       void *out, void *stream);
+                       void *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Workspace bytes cpk_roll_attention uses for a split key range with these
+ * shapes: parts x c x Hq x (head_dim + 4) x 4 (one fp32 record per part,
+ * row and query head: running maximum, sum, two pad words, the partial
+ * output).  0 when the shapes are not split (fp32, or enough workgroups
+ * without splitting); a call may then pass ws = NULL.
+ */
+size_t cpk_roll_workspace_size(int Hq, int Hkv, int C, int c, int head_dim,
+                               int dtype);
 
 /* ------------------------------------------------------------ diagnostics */
 

@@ -265,6 +265,32 @@ def test_rolling_small_with_left_pad_full_compare():
     assert bitwise(out_a[n_left:], out_m[n_left:]), "explicit != computed mask"
 
 
+def test_rolling_split_vs_unsplit():
+    """The rolling attention with a workspace (key range split over 4 parts
+    of one 128-key tile each, merged in part order) and without one: both
+    against the oracle, explicit == computed mask bitwise in each form, and
+    the two forms within rounding of each other."""
+    L, C, c, H, D = 1000, 512, 128, 4, 128
+    assert cpk.cpk_roll_workspace_size(H, H, C, c, D, torch.float16) == 4 * c * H * (D + 4) * 4
+    say(f"case: rolling fp16 split vs unsplit L={L} C={C} c={c} H={H}")
+    q, k, v = si.rolling_inputs(L=L, H=H, D=D, seed=402)
+    qs, ks, vs = (si.storage(x) for x in (q, k, v))
+    ref, n_left, _, _, masks = oracle.roll_prefill(qs, ks, vs, C, c, oracle.F16)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    mk = [torch.from_numpy(m.astype(np.float16)).cuda() for m in masks]
+    outs = {}
+    for split in (True, False):
+        out_a, _, _, _ = cpk.roll_prefill(qd, kd, vd, C, c, split=split)
+        out_m, _, _, _ = cpk.roll_prefill(qd, kd, vd, C, c, masks=mk, split=split)
+        torch.cuda.synchronize()
+        check(out_a[n_left:], ref[n_left:], 2e-2, f"split={split} vs oracle")
+        assert bitwise(out_a[n_left:], out_m[n_left:]), f"split={split}: explicit != computed"
+        outs[split] = out_a
+    d = float((outs[True][n_left:].float() - outs[False][n_left:].float()).abs().max())
+    say(f"  split vs unsplit: max-abs {d:.3e}")
+    assert d <= 4e-3
+
+
 def test_workload4_rolling_full_size():
     L, C, c, H, D = 4096, 2048, 256, 16, 128
     say(f"case: workload 4 rolling fp16 L={L} C={C} c={c} H={H} (sampled rows)")

@@ -3,6 +3,8 @@ header declares, its host logic (ladder, split, planner) agrees with the
 oracle and the pages' printed values, and invalid arguments are rejected on
 the host before any launch (no GPU is touched by these tests)."""
 import ctypes
+
+import torch
 import json
 import os
 import re
@@ -177,5 +179,22 @@ def test_roll_validation():
     # output overlaps input
     assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE, FAKE * 6, 1, 2, 8, 4, 64, cpk.CPK_F16, None) == cpk.CPK_EINVAL
     g = cpk._lib.cpk_roll_attention
-    assert g(FAKE, FAKE, FAKE, None, 100, 0, 16, 16, 64, 128, 128, cpk.CPK_F16, 0.0, FAKE, None) == cpk.CPK_EINVAL
-    assert g(FAKE, FAKE, FAKE, None, 10, 0, 16, 16, 64, 32, 128, cpk.CPK_F16, 0.0, FAKE, None) == cpk.CPK_EINVAL
+    assert g(FAKE, FAKE, FAKE, None, 100, 0, 16, 16, 64, 128, 128, cpk.CPK_F16, 0.0, FAKE,
+             None, 0, None) == cpk.CPK_EINVAL
+    assert g(FAKE, FAKE, FAKE, None, 10, 0, 16, 16, 64, 32, 128, cpk.CPK_F16, 0.0, FAKE,
+             None, 0, None) == cpk.CPK_EINVAL
+    # a workspace smaller than the split needs
+    assert g(FAKE, FAKE, FAKE, None, 4096, 0, 16, 16, 2048, 256, 128, cpk.CPK_F16, 0.0, FAKE,
+             FAKE, 16, None) == cpk.CPK_EWORKSPACE
+
+
+def test_roll_workspace_size():
+    """Rolling workload shapes (16 heads, no GQA, C = 2048, c = 256): 64
+    workgroups unsplit, so the 16 key tiles are split 4 ways."""
+    f16 = torch.float16
+    assert cpk.cpk_roll_workspace_size(16, 16, 2048, 256, 128, f16) == 4 * 256 * 16 * 132 * 4
+    assert cpk.cpk_roll_workspace_size(16, 16, 2048, 256, 128, torch.float32) == 0
+    # enough workgroups already: no split
+    assert cpk.cpk_roll_workspace_size(32, 8, 8192, 4096, 128, torch.bfloat16) == 0
+    # never more parts than key tiles
+    assert cpk.cpk_roll_workspace_size(1, 1, 128, 64, 64, f16) == 0
