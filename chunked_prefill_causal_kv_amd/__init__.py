@@ -53,6 +53,7 @@ def _load() -> ctypes.CDLL:
     F = ctypes.c_float
     sig = {
         "cpk_version": ([], I),
+        "cpk_set_attention_kernel": ([I], I),
         "cpk_last_error": ([], ctypes.c_char_p),
         "cpk_device_info": ([ctypes.c_char_p, I, IP], I),
         "cpk_ladder_rungs": ([I, IP, IP], I),
@@ -134,6 +135,33 @@ class KVCache:
 
 def cpk_version() -> int:
     return _lib.cpk_version()
+
+
+ATTN_AUTO, ATTN_NARROW, ATTN_WIDE = 0, 1, 2
+
+
+def cpk_set_attention_kernel(kind: int) -> int:
+    """Process-wide bf16/fp16 attention kernel choice (ATTN_AUTO, ATTN_NARROW
+    or ATTN_WIDE) for chunk and varlen attention; returns the previous one."""
+    r = _lib.cpk_set_attention_kernel(int(kind))
+    if r < 0:
+        _check(r)
+    return r
+
+
+class attention_kernel:
+    """Context manager: run a block with the given attention kernel choice."""
+
+    def __init__(self, kind: int):
+        self.kind = kind
+
+    def __enter__(self):
+        self.prev = cpk_set_attention_kernel(self.kind)
+        return self
+
+    def __exit__(self, *exc):
+        cpk_set_attention_kernel(self.prev)
+        return False
 
 
 def cpk_last_error() -> str:

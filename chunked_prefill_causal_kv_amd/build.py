@@ -3,7 +3,12 @@
     python chunked_prefill_causal_kv_amd/build.py
 
 Every HIP source is compiled with packed-fp32 instruction selection turned
-off (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
+off (``-Xclang -target-feature -Xclang -packed-fp32-ops``), and with matrix
+instructions selected in their vector-register form
+(``-mllvm -amdgpu-mfma-vgpr-form=1``): the 128-column attention kernel keeps
+its scores in vector registers for the softmax and its query fragments in
+accumulation registers, which this form lets the register allocator do
+without copies; the other kernels compile to the same code either way.
 """
 from __future__ import annotations
 
@@ -31,6 +36,7 @@ def hipcc() -> str:
 def _flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 

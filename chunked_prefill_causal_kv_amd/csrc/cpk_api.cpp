@@ -4,6 +4,7 @@
 #include "../../include/cpk.h"
 #include "cpk_internal.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -99,11 +100,31 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return x < y + nb && y < x + na;
 }
 
+std::atomic<int> g_attn_kernel{CPK_ATTN_AUTO};
+
+// Whether the 128-column kernel serves a bf16/fp16 chunk or varlen
+// attention launch of `rows` rows (the longest sequence's, in varlen).
+bool use_wide(int dtype, int group, int kv_heads, int rows)
+{
+    if (dtype == CPK_F32) return false;
+    const int k = g_attn_kernel.load(std::memory_order_relaxed);
+    if (k != CPK_ATTN_AUTO) return k == CPK_ATTN_WIDE;
+    const int br = cpk::attn_rows_per_block(dtype, group, true);
+    return (int64_t)((rows + br - 1) / br) * kv_heads >= cpk::kWideMinGroups;
+}
+
 }  // namespace
 
 extern "C" {
 
-int cpk_version(void) { return 100; }
+int cpk_version(void) { return 101; }
+
+int cpk_set_attention_kernel(int kind)
+{
+    if (kind != CPK_ATTN_AUTO && kind != CPK_ATTN_NARROW && kind != CPK_ATTN_WIDE)
+        return fail(CPK_EINVAL, "set_attention_kernel: unknown kind %d", kind);
+    return g_attn_kernel.exchange(kind);
+}
 
 const char *cpk_last_error(void) { return g_err.c_str(); }
 
@@ -209,8 +230,9 @@ static int attention_common(const void *q, const cpk_kv_cache *cache, int b, int
     fill_scale(a, resolve_scale(scale, a.D));
     a.slot = b; a.q_row0 = 0; a.out_row0 = 0; a.rows = rows; a.q_src_rows = real_rows;
     a.out_rows = real_rows; a.n_keys = past_len + rows; a.key_lo = 0; a.causal_base = past_len;
-    const int br = cpk::attn_rows_per_block(cache->dtype, q_heads / cache->kv_heads);
-    return hip_status(cpk::launch_attention(a, cache->dtype, (rows + br - 1) / br, 1, st),
+    const bool wide = use_wide(cache->dtype, q_heads / cache->kv_heads, cache->kv_heads, rows);
+    const int br = cpk::attn_rows_per_block(cache->dtype, q_heads / cache->kv_heads, wide);
+    return hip_status(cpk::launch_attention(a, cache->dtype, (rows + br - 1) / br, 1, wide, st),
                       "attention launch");
 }
 
@@ -349,9 +371,11 @@ int cpk_varlen_step(const void *q, const void *k_new, const void *v_new,
         fill_scale(a, sc);
         a.varlen = 1; a.cu_rows = cu_rows; a.past_lens = past_lens; a.slots = slots;
         a.n_seqs = n_seqs; a.min_rows = dec_ok ? 2 : 1;
-        const int br = cpk::attn_rows_per_block(cache->dtype, G);
-        r = hip_status(cpk::launch_attention(a, cache->dtype, (max_rows + br - 1) / br, n_seqs, st),
-                       "varlen prefill");
+        const bool wide = use_wide(cache->dtype, G, cache->kv_heads, max_rows);
+        const int br = cpk::attn_rows_per_block(cache->dtype, G, wide);
+        r = hip_status(
+            cpk::launch_attention(a, cache->dtype, (max_rows + br - 1) / br, n_seqs, wide, st),
+            "varlen prefill");
         if (r) return r;
     }
     return ok();
@@ -395,7 +419,7 @@ static void roll_split(int Hq, int Hkv, int C, int c, int dtype, int *n_parts, i
     *n_parts = 1;
     *part_tiles = 0;
     if (dtype == CPK_F32 || Hkv < 1 || Hq < Hkv || Hq % Hkv) return;
-    const int br = cpk::attn_rows_per_block(dtype, Hq / Hkv);
+    const int br = cpk::attn_rows_per_block(dtype, Hq / Hkv, false);
     const int base = ((c + br - 1) / br) * Hkv;
     const int tiles = (C + cpk::kAttnTileKeys - 1) / cpk::kAttnTileKeys;
     int s = kSplitTarget / (base > 0 ? base : 1);
@@ -459,9 +483,10 @@ int cpk_roll_attention(const void *q, const void *k, const void *v, const void *
     a.n_parts = parts;
     a.part_tiles = pt;
     a.part_ws = (float *)ws;
-    const int br = cpk::attn_rows_per_block(dtype, Hq / Hkv);
-    r = hip_status(cpk::launch_attention(a, dtype, (c + br - 1) / br, 1, (hipStream_t)stream),
-                   "roll_attention launch");
+    const int br = cpk::attn_rows_per_block(dtype, Hq / Hkv, false);
+    r = hip_status(
+        cpk::launch_attention(a, dtype, (c + br - 1) / br, 1, false, (hipStream_t)stream),
+        "roll_attention launch");
     if (r || parts <= 1) return r;
     return hip_status(cpk::launch_attention_combine(a, dtype, (hipStream_t)stream),
                       "roll_attention combine");

@@ -92,9 +92,13 @@ hipError_t launch_roll_append(const void *k_old, const void *v_old, const void *
                               int C, int c, int row_bytes, hipStream_t st);
 
 // Attention: grid.x = row blocks x KV heads (KV head fastest), grid.z = sequences.
-int attn_rows_per_block(int dtype, int group);
+// `wide` selects the 128-column bf16/fp16 kernel (chunk and varlen
+// attention only: the rolling form keeps the 64-column kernel, which also
+// takes the explicit additive mask, so both of its forms stay bit-equal).
+constexpr int kWideMinGroups = 256;   // auto choice: wide once its grid fills the CUs
+int attn_rows_per_block(int dtype, int group, bool wide);
 hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
-                            hipStream_t st);
+                            bool wide, hipStream_t st);
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int max_segs, hipStream_t st);
 

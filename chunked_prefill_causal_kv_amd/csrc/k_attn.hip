@@ -554,6 +554,514 @@ void attn_mfma_kernel(AttnArgs a)
     }
 }
 
+// ------------------------------------------------------------ wide kernel
+//
+// attn_wide_kernel: 128 query columns per workgroup, 4 waves (one per SIMD)
+// and 64-key tiles.  Wave w takes column group w / 2 (64 columns = two
+// 32-column MFMA blocks) and key half w % 2 (32 of the 64 keys of every
+// tile).  Every K or V fragment a wave reads from LDS feeds two MFMAs and
+// every staged tile serves 128 columns: half the LDS reads and L2->LDS fill
+// per flop of attn_mfma_kernel.
+//
+// With a single wave per SIMD nothing hides latency but the wave's own
+// instruction stream, so the loop is software-pipelined across tiles: while
+// the matrix unit computes the scores of tile t+1 the vector unit turns
+// the scores of tile t into probabilities, and while it accumulates P V of
+// tile t the vector unit masks and reduces the scores of tile t+1.  K and V
+// tiles live in separate two-stage rings, K one tile ahead of V, so one
+// barrier per tile suffices.  Fragment layouts, swizzles, the lazy maximum
+// and the split records are those of attn_mfma_kernel; the two key halves
+// are merged once at the end through LDS.
+
+constexpr int kWQC = 128;        // query columns per workgroup
+constexpr int kWThreads = 256;   // 4 waves = 2 column groups x 2 key halves
+constexpr int kWBK = 64;         // keys per tile
+constexpr int kWStages = 4;      // ring slots: tiles are loaded three ahead
+
+// Exchange between the two 32-lane halves without LDS: permlane32_swap of a
+// value with itself yields the low half's value in every lane (first
+// result) and the high half's (second); both halves then combine the same
+// operands in the same order, so their results are bit-identical.
+__device__ __forceinline__ float half_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Keep a value in accumulation registers: the matrix instructions read
+// their A/B operands from them directly, which leaves the vector registers
+// to the softmax.  (An empty asm with an "a" constraint; no instruction.)
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 in_agprs(uint4 x)
+{
+    u32x4_t t = {x.x, x.y, x.z, x.w};
+    asm volatile("" : "+a"(t));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// Mark a value as produced here: an empty asm that takes and returns it in
+// vector registers, so that its computation is not moved past a later
+// branch (it is then scheduled among the independent matrix instructions
+// before that branch).  No instruction is emitted.
+__device__ __forceinline__ uint4 here(uint4 x)
+{
+    u32x4_t t = {x.x, x.y, x.z, x.w};
+    asm volatile("" : "+v"(t));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+template <typename TR, int D>
+__global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_wide_kernel(AttnArgs a)
+{
+    using TL = Tile<D>;
+    constexpr int NCH = TL::NCH;
+    constexpr int NS = D / 16;      // k-steps of the QK^T contraction
+    constexpr int NDB = D / 32;     // 32-wide d blocks of O^T
+    constexpr int WAVES = kWThreads / 64;
+    constexpr int TILE = kWBK * D;                  // uint16 elements of one K or V tile
+    constexpr int LOADS = kWBK * NCH / kWThreads;   // 16-byte loads per thread per tensor
+    static_assert(kWBK * NCH % kWThreads == 0, "tile loads split evenly");
+    static_assert(kAttnTileKeys % kWBK == 0, "split parts are whole tiles");
+    // s_waitcnt immediates (gfx9 encoding): vector memory count <= the
+    // loads of one or two later tiles (2 * LOADS per tile per wave), the
+    // other counters unconstrained
+    constexpr int kTileLoads = 2 * LOADS;
+    static_assert(2 * kTileLoads < 64, "vmcnt field is 6 bits");
+    constexpr int kWaitOne =
+        (kTileLoads & 15) | (7 << 4) | (15 << 8) | ((kTileLoads >> 4) << 14);
+    constexpr int kWaitTwo =
+        ((2 * kTileLoads) & 15) | (7 << 4) | (15 << 8) | ((2 * kTileLoads) >> 4 << 14);
+
+    // Four ring slots, each a K tile then a V tile, declared as separate
+    // arrays so that the compiler can tell that reading one slot while
+    // others are being filled by direct loads needs no wait for those loads.
+    // After the loop, slot 2*kh + (column / 64) stages the fp32 partial sums
+    // of 64 columns of key half kh.
+    static_assert(kWStages == 4, "four statically named ring slots");
+    static_assert(64 * D * 4 <= 2 * TILE * 2, "a slot holds 64 fp32 partial rows");
+    __shared__ __attribute__((aligned(16))) uint16_t ring0[2 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t ring1[2 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t ring2[2 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t ring3[2 * TILE];
+    __shared__ float ml[2 * 2 * kWQC];
+
+    SeqView sv;
+    if (!resolve_seq(a, blockIdx.z, sv)) return;
+    const int G = a.Hq / a.Hkv;
+    const int BR = kWQC / G;                // rows per workgroup
+    const int g = blockIdx.x % a.Hkv;       // KV head fastest: one KV head per XCD
+    const int r0 = (blockIdx.x / a.Hkv) * BR;
+    if (r0 >= sv.rows) return;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c32 = lane & 31;
+    const int hi = lane >> 5;
+    const int cg = wave >> 1;               // columns 64*cg .. +64
+    const int kh = wave & 1;                // keys 32*kh .. +32 of every tile
+
+    const uint16_t *kc = (const uint16_t *)a.k + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
+    const uint16_t *vc = (const uint16_t *)a.v + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
+
+    // ---- query fragments (B operand of S^T = K Q^T) of the two column blocks
+    uint4 qf[2][NS];
+    int lim[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int qc = cg * 64 + cb * 32 + c32;
+        const int row = r0 + qc / G;
+        const bool ok = (qc < BR * G) && (row < sv.rows);
+        const int rr = ok ? row : r0;
+        const int srow = rr < sv.q_src_rows ? rr : sv.q_src_rows - 1;
+        const int head = g * G + (ok ? qc % G : 0);
+        lim[cb] = sv.causal_base + rr;
+        const uint16_t *qp =
+            (const uint16_t *)a.q + ((int64_t)(sv.q_row0 + srow) * a.Hq + head) * D + 8 * hi;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qf[cb][s] = in_agprs(*(const uint4 *)(qp + 16 * s));
+    }
+
+    // ---- key range of this workgroup (and of its split part), in tiles
+    const int last_row = min(r0 + BR, sv.rows) - 1;
+    const int key_end = min(sv.n_keys, sv.causal_base + last_row + 1);   // exclusive
+    int t_first = sv.key_lo / kWBK;
+    int t_last = (key_end - 1) / kWBK;
+    if (a.n_parts > 1) {
+        constexpr int R = kAttnTileKeys / kWBK;
+        t_first = max(t_first, (int)blockIdx.y * a.part_tiles * R);
+        t_last = min(t_last, ((int)blockIdx.y + 1) * a.part_tiles * R - 1);
+    }
+
+    // ---- direct global->LDS tile loads: load i of this wave fills LDS
+    // chunks [(i*WAVES + wave)*64, +64) of the tile, one 16-byte chunk per
+    // lane, holding global chunk (pos ^ swizzle(row)) of its row; rows past
+    // the last valid key re-read that key
+    auto load16 = [](const char *src, uint16_t *dst) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    };
+    auto issue = [&](const uint16_t *base, int kt, uint16_t *dst, bool is_v) {
+        const int key0 = kt * kWBK;
+        const char *tb = (const char *)(base + (int64_t)key0 * D);
+        const int clamp = sv.n_keys - 1 - key0;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int blk = i * WAVES + wave;
+            const int t = blk * 64 + lane;
+            const int row = t / NCH;
+            const int pos = t % NCH;
+            const int sw = is_v ? TL::swz_v(row) : TL::swz_k(row);
+            const uint32_t off = (uint32_t)(min(row, clamp) * D + (pos ^ sw) * 8) * 2u;
+            load16(tb + off, dst + blk * 64 * 8);
+        }
+    };
+
+    // ---- accumulators and per-column softmax state
+    f32x16_t oacc[NDB][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[db][cb][j] = 0.f;
+    float m_run[2] = {-INFINITY, -INFINITY};
+    float l_run[2] = {0.f, 0.f};
+    const float c = a.scale_log2;
+
+    const int g16 = (lane >> 4) & 1;
+    const int si = lane & 15;
+    const int vrow_off = kh * 32 + 4 * hi + (si >> 2);   // + 16*s2 + 8*j2
+    const int vcol = 16 * g16 + 4 * (si & 3);            // + 32*db
+    const int krow = kh * 32 + c32;
+
+    // ---- the pieces of one tile's work for this wave
+    // S^T[32 keys x 64 cols] from the K tile at Kb (each K fragment read
+    // once, all reads issued up front, each feeding both column blocks)
+    auto scores = [&](const uint16_t *Kb, f32x16_t (&sa)[2]) {
+        const uint16_t *kr = Kb + krow * D;
+        const int sk = TL::swz_k(krow);
+        uint4 kf[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) kf[s] = *(const uint4 *)(kr + ((2 * s + hi) ^ sk) * 8);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) sa[cb][j] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            sa[0] = TR::mfma(kf[s], qf[0][s], sa[0]);
+            sa[1] = TR::mfma(kf[s], qf[1][s], sa[1]);
+        }
+    };
+    // register j of sa[cb] in lane (c32, hi): key
+    // 64*kt + 32*kh + 8*(j/4) + 4*hi + (j%4) of column 64*cg + 32*cb + c32
+    auto mask_scores = [&](int kt, f32x16_t (&sa)[2]) {
+        const bool full = (kt * kWBK >= sv.key_lo) && ((kt + 1) * kWBK <= sv.n_keys) &&
+                          ((kt + 1) * kWBK - 1 <= sv.causal_base + r0);
+        if (!full) {
+            const int kbase = kt * kWBK + kh * 32 + 4 * hi;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const int lo = sv.key_lo - kbase;
+                const int hi_ = min(lim[cb], sv.n_keys - 1) - kbase;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int o = 8 * (j >> 2) + (j & 3);
+                    sa[cb][j] = (o >= lo && o <= hi_) ? sa[cb][j] : -INFINITY;
+                }
+            }
+        }
+    };
+    auto tile_max = [&](const f32x16_t (&sa)[2], float (&mt)[2]) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            float mx = sa[cb][0];
+#pragma unroll
+            for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sa[cb][j]);
+            mt[cb] = half_max(mx) * c;
+        }
+    };
+    // online softmax (exp2 domain), lazy maximum: raise the running maximum
+    // only where a tile's exceeds it by more than 2^8 (rare after the first
+    // tile)
+    auto rescale = [&](const float (&mt)[2]) {
+        const bool n0 = mt[0] > m_run[0] + kLazyLog2;
+        const bool n1 = mt[1] > m_run[1] + kLazyLog2;
+        if (__builtin_amdgcn_ballot_w64(n0 || n1) != 0) {
+            const float al0 = n0 ? exp2f(m_run[0] - mt[0]) : 1.0f;
+            const float al1 = n1 ? exp2f(m_run[1] - mt[1]) : 1.0f;
+            m_run[0] = n0 ? mt[0] : m_run[0];
+            m_run[1] = n1 ? mt[1] : m_run[1];
+            l_run[0] *= al0;
+            l_run[1] *= al1;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    oacc[db][0][j] *= al0;
+                    oacc[db][1][j] *= al1;
+                }
+        }
+    };
+    // probabilities as B operands (k-step s2 holds registers 8*s2 .. +7)
+    auto probs = [&](const f32x16_t (&sa)[2], uint4 (&pb)[2][2]) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const float mu = m_run[cb] == -INFINITY ? 0.f : m_run[cb];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p0 =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(sa[cb][8 * s2 + 2 * i], c, -mu));
+                    const float p1 =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(sa[cb][8 * s2 + 2 * i + 1], c, -mu));
+                    w[i] = TR::pack(p0, p1);
+                }
+                pb[cb][s2] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    };
+    // V^T fragments of this wave's 32 keys of the V tile at Vb (k-step s2,
+    // d block db), and O^T[d x 64 cols] += V^T[d x 32 keys] P^T[32 keys x
+    // 64 cols] (each fragment feeding both column blocks), then the row
+    // sums of P
+    auto vfrags = [&](const uint16_t *Vb, uint4 (&vf)[NDB][2]) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                uint2 half[2];
+#pragma unroll
+                for (int j2 = 0; j2 < 2; ++j2) {
+                    const int vrow = vrow_off + 16 * s2 + 8 * j2;
+                    const int dd = 32 * db + vcol;
+                    const uint16_t *vp =
+                        Vb + vrow * D + (((dd >> 3) ^ TL::swz_v(vrow)) << 3) + (dd & 7);
+                    const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)vp);
+                    half[j2] = __builtin_bit_cast(uint2, r);
+                }
+                vf[db][s2] = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
+            }
+    };
+    auto accumulate = [&](const uint4 (&vf)[NDB][2], const uint4 (&pb)[2][2]) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                oacc[db][0] = TR::mfma(vf[db][s2], pb[0][s2], oacc[db][0]);
+                oacc[db][1] = TR::mfma(vf[db][s2], pb[1][s2], oacc[db][1]);
+            }
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                l_run[cb] = TR::dot2(pb[cb][s2].x, TR::kOnes, l_run[cb]);
+                l_run[cb] = TR::dot2(pb[cb][s2].y, TR::kOnes, l_run[cb]);
+                l_run[cb] = TR::dot2(pb[cb][s2].z, TR::kOnes, l_run[cb]);
+                l_run[cb] = TR::dot2(pb[cb][s2].w, TR::kOnes, l_run[cb]);
+            }
+    };
+
+    // ---- software-pipelined tile loop over four ring slots: tile
+    // t_first + i sits in slot i % 4 and is loaded three steps ahead.  The
+    // step for tile t (t < t_last) computes the scores of tile t+1 on the
+    // matrix unit while the vector unit turns the scores of tile t into
+    // probabilities, then accumulates P V of tile t while the vector unit
+    // masks and reduces the scores of tile t+1; the running-maximum check
+    // for tile t+1 closes the step.  It needs K(t+1) and V(t): it waits for
+    // its loads with at most those of tile t+2 pending, passes a barrier
+    // (after which the slot of tile t-1, whose K and V were last read by
+    // the two previous steps, is free) and refills that slot with tile t+3.
+    // The barrier carries no memory fence, which would wait for every load
+    // in flight; empty asm statements with a memory clobber keep the
+    // compiler from moving LDS accesses across it.
+    auto sync = [&](bool one_pending) {
+        if (one_pending)
+            __builtin_amdgcn_s_waitcnt(kWaitOne);
+        else
+            __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    auto refill = [&](int t, uint16_t *slot) {
+        if (t <= t_last) {
+            issue(kc, t, slot, false);
+            issue(vc, t, slot + TILE, true);
+        }
+    };
+    auto step = [&](int t, const uint16_t *cur, const uint16_t *nxt, uint16_t *free_slot,
+                    f32x16_t (&scur)[2], f32x16_t (&snxt)[2]) {
+        // V(t) is complete and visible since the previous step's barrier
+        uint4 vf[NDB][2];
+        vfrags(cur + TILE, vf);
+        sync(t + 2 <= t_last);
+        refill(t + 3, free_slot);
+        uint4 pb[2][2];
+        float mt[2];
+        scores(nxt, snxt);
+        probs(scur, pb);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) pb[cb][s2] = here(pb[cb][s2]);
+        mask_scores(t + 1, snxt);
+        accumulate(vf, pb);
+        tile_max(snxt, mt);
+        rescale(mt);
+    };
+    auto drain = [&](const uint16_t *cur, const f32x16_t (&scur)[2]) {
+        sync(false);
+        uint4 vf[NDB][2];
+        vfrags(cur + TILE, vf);
+        uint4 pb[2][2];
+        probs(scur, pb);
+        accumulate(vf, pb);
+    };
+    if (t_last >= t_first) {
+        f32x16_t s0[2], s1[2];
+        refill(t_first, ring0);
+        refill(t_first + 1, ring1);
+        refill(t_first + 2, ring2);
+        {
+            // tile t_first: its loads are the oldest of up to three tiles
+            if (t_first + 2 <= t_last)
+                __builtin_amdgcn_s_waitcnt(kWaitTwo);
+            else
+                __builtin_amdgcn_s_waitcnt(0);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            float mt[2];
+            scores(ring0, s0);
+            mask_scores(t_first, s0);
+            tile_max(s0, mt);
+            rescale(mt);
+        }
+        // whole rounds of four steps, then up to three, then the last tile
+        int t = t_first;
+        for (; t + 4 <= t_last; t += 4) {
+            step(t, ring0, ring1, ring3, s0, s1);
+            step(t + 1, ring1, ring2, ring0, s1, s0);
+            step(t + 2, ring2, ring3, ring1, s0, s1);
+            step(t + 3, ring3, ring0, ring2, s1, s0);
+        }
+        if (t < t_last) step(t++, ring0, ring1, ring3, s0, s1);
+        if (t < t_last) step(t++, ring1, ring2, ring0, s1, s0);
+        if (t < t_last) step(t++, ring2, ring3, ring1, s0, s1);
+        const int last = (t_last - t_first) & 3;   // slot of the last tile
+        const uint16_t *cur = last == 0 ? ring0 : last == 1 ? ring1 : last == 2 ? ring2 : ring3;
+        if (last & 1)
+            drain(cur, s1);
+        else
+            drain(cur, s0);
+    }
+    __syncthreads();   // all waves are done with the tiles: reuse LDS below
+
+    // ---- merge the two key halves: half kh stages its scaled partial sums
+    // (fp32 [column][D], float4-swizzled by column) at float offset kh*128*D
+    float *Ms = ml;
+    float *Ls = ml + 2 * kWQC;
+    // fp32 partial row of key half h, column col
+    auto stage_row = [&](int h, int col) -> float * {
+        uint16_t *slot = h == 0 ? (col < 64 ? ring0 : ring1) : (col < 64 ? ring2 : ring3);
+        return (float *)slot + (col & 63) * D;
+    };
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const float lt = half_sum(l_run[cb]);
+        if (hi == 0) {
+            Ms[kh * kWQC + cg * 64 + cb * 32 + c32] = m_run[cb];
+            Ls[kh * kWQC + cg * 64 + cb * 32 + c32] = lt;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int col = cg * 64 + cb * 32 + c32;
+        const float m0 = Ms[col], m1 = Ms[kWQC + col];
+        const float M = fmaxf(m0, m1);
+        const float e0 = (m0 == -INFINITY) ? 0.f : exp2f(m0 - M);
+        const float e1 = (m1 == -INFINITY) ? 0.f : exp2f(m1 - M);
+        const float den = e0 * Ls[col] + e1 * Ls[kWQC + col];
+        const float mine = kh ? e1 : e0;
+        // split parts keep the sum unnormalised (the combine normalises)
+        const float f = a.n_parts > 1 ? mine : (den > 0.f ? mine / den : 0.f);
+        float *dst = stage_row(kh, col);
+        const int sw = TL::swz_o(col);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const int d4 = db * 8 + 2 * j4 + hi;     // float4 column of d = 4*d4
+                const float4 v4 =
+                    make_float4(oacc[db][cb][4 * j4] * f, oacc[db][cb][4 * j4 + 1] * f,
+                                oacc[db][cb][4 * j4 + 2] * f, oacc[db][cb][4 * j4 + 3] * f);
+                *(float4 *)(dst + 4 * (d4 ^ sw)) = v4;
+            }
+    }
+    __syncthreads();
+    {
+        constexpr int PARTS = kWThreads / kWQC;   // threads per query column
+        constexpr int DP = D / PARTS;             // output elements per thread
+        const int oc = tid / PARTS;
+        const int part = tid % PARTS;
+        const int row = r0 + oc / G;
+        const float *s0 = stage_row(0, oc);
+        const float *s1 = stage_row(1, oc);
+        const int sw = TL::swz_o(oc);
+        if (oc < BR * G && row < sv.out_rows && a.n_parts > 1) {
+            const int head = g * G + oc % G;
+            float *rec =
+                a.part_ws + (((int64_t)blockIdx.y * sv.out_rows + row) * a.Hq + head) * (D + 4);
+            if (part == 0) {
+                const float m0 = Ms[oc], m1 = Ms[kWQC + oc];
+                const float M = fmaxf(m0, m1);
+                const float den = ((m0 == -INFINITY) ? 0.f : exp2f(m0 - M)) * Ls[oc] +
+                                  ((m1 == -INFINITY) ? 0.f : exp2f(m1 - M)) * Ls[kWQC + oc];
+                *(float4 *)rec = make_float4(M, den, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int d4 = 0; d4 < DP; d4 += 4) {
+                const int d = part * DP + d4;
+                const int off = 4 * ((d >> 2) ^ sw);
+                const float4 x = *(const float4 *)(s0 + off);
+                const float4 y = *(const float4 *)(s1 + off);
+                *(float4 *)(rec + 4 + d) = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+            }
+        } else if (oc < BR * G && row < sv.out_rows) {
+            const int head = g * G + oc % G;
+            uint16_t *op = (uint16_t *)a.out + ((int64_t)(sv.out_row0 + row) * a.Hq + head) * D +
+                           part * DP;
+#pragma unroll
+            for (int d8 = 0; d8 < DP; d8 += 8) {
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int d = part * DP + d8 + 4 * i;
+                    const int off = 4 * ((d >> 2) ^ sw);
+                    const float4 x = *(const float4 *)(s0 + off);
+                    const float4 y = *(const float4 *)(s1 + off);
+                    w[2 * i] = TR::pack(x.x + y.x, x.y + y.y);
+                    w[2 * i + 1] = TR::pack(x.z + y.z, x.w + y.w);
+                }
+                *(uint4 *)(op + d8) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    }
+}
+
 // Merge of the split parts of a key range: for each (row, query head), in
 // part order, M = max_p M_p, f_p = 2^(M_p - M), out = sum_p f_p O_p /
 // sum_p f_p den_p.  One thread per output element d.
@@ -679,17 +1187,29 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a)
 
 }  // namespace
 
-int attn_rows_per_block(int dtype, int group)
+int attn_rows_per_block(int dtype, int group, bool wide)
 {
     (void)dtype;
-    return kQC / group;
+    return (wide ? kWQC : kQC) / group;
 }
 
 hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
-                            hipStream_t st)
+                            bool wide, hipStream_t st)
 {
     const dim3 grid(row_blocks * a.Hkv, a.n_parts > 1 ? a.n_parts : 1, n_seq_grid);
-    if (dtype == 0) {
+    if (wide && dtype != 0) {
+        if (dtype == 1) {
+            if (a.D == 64)
+                hipLaunchKernelGGL((attn_wide_kernel<F16, 64>), grid, dim3(kWThreads), 0, st, a);
+            else
+                hipLaunchKernelGGL((attn_wide_kernel<F16, 128>), grid, dim3(kWThreads), 0, st, a);
+        } else {
+            if (a.D == 64)
+                hipLaunchKernelGGL((attn_wide_kernel<Bf16, 64>), grid, dim3(kWThreads), 0, st, a);
+            else
+                hipLaunchKernelGGL((attn_wide_kernel<Bf16, 128>), grid, dim3(kWThreads), 0, st, a);
+        }
+    } else if (dtype == 0) {
         if (a.D == 64)
             hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, st, a);
         else

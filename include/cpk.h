@@ -52,6 +52,13 @@ enum cpk_status {
 
 enum cpk_dtype { CPK_F32 = 0, CPK_F16 = 1, CPK_BF16 = 2 };
 
+/* bf16/fp16 attention kernel choice (cpk_set_attention_kernel) */
+enum cpk_attention_kernel {
+    CPK_ATTN_AUTO = 0,     /* by launch size (the default)                  */
+    CPK_ATTN_NARROW = 1,   /* 64 query columns per workgroup, 8 waves       */
+    CPK_ATTN_WIDE = 2,     /* 128 query columns per workgroup, 4 waves      */
+};
+
 /*
  * A KV cache bound at physical capacity, with the true number of valid
  * positions per sequence carried beside it in seqlens_k (ONNX GenAI Wiki
@@ -261,6 +268,19 @@ const char *cpk_last_error(void);
 
 /* Library ABI version (major * 100 + minor). */
 int cpk_version(void);
+
+/*
+ * Which bf16/fp16 kernel serves chunk attention (cpk_chunk_attention,
+ * cpk_prefill_chunk) and the prompt rows of cpk_varlen_step; fp32 and the
+ * rolling form (cpk_roll_attention) are unaffected.  Both kernels compute
+ * the same attention to within rounding; each alone is deterministic and
+ * gives a row the same bits whether its prompt runs in one pass or in
+ * chunks.  CPK_ATTN_AUTO takes the wide kernel when its launch has at
+ * least as many workgroups as the GPU has compute units (256), else the
+ * narrow one.  The setting is process-wide and meant for diagnostics and
+ * tests; it returns the previous setting, or CPK_EINVAL for an unknown kind.
+ */
+int cpk_set_attention_kernel(int kind);
 
 /*
  * Name and compute-unit count of the current HIP device.  name receives at

@@ -129,15 +129,26 @@ def test_fp32_demo_chunked_and_one_shot():
 
 # ----------------------------------------------- GQA shapes, full compare
 
+KERNELS = {"narrow": 1, "wide": 2}
+
+
+@pytest.mark.parametrize("kernel", ["narrow", "wide"])
 @pytest.mark.parametrize("dtype,Hq,Hkv,D,L,W", [
     (torch.bfloat16, 8, 2, 128, 700, 256),
     (torch.bfloat16, 16, 2, 64, 333, 128),
     (torch.bfloat16, 4, 4, 128, 300, 200),
     (torch.float16, 8, 2, 128, 450, 256),
     (torch.bfloat16, 24, 8, 128, 260, 100),
+    (torch.bfloat16, 12, 4, 128, 290, 97),
+    (torch.bfloat16, 32, 2, 64, 200, 64),
 ])
-def test_chunked_prefill_full_compare(dtype, Hq, Hkv, D, L, W):
-    say(f"case: chunked prefill {dtype} Hq={Hq} Hkv={Hkv} D={D} L={L} W={W}")
+def test_chunked_prefill_full_compare(kernel, dtype, Hq, Hkv, D, L, W):
+    say(f"case: chunked prefill [{kernel}] {dtype} Hq={Hq} Hkv={Hkv} D={D} L={L} W={W}")
+    with cpk.attention_kernel(KERNELS[kernel]):
+        _chunked_prefill_full_compare(dtype, Hq, Hkv, D, L, W)
+
+
+def _chunked_prefill_full_compare(dtype, Hq, Hkv, D, L, W):
     dn = {torch.bfloat16: "bf16", torch.float16: "f16"}[dtype]
     q, k, v = si.gqa_prompt(L=L, Hq=Hq, Hkv=Hkv, D=D, dtype=dn, seed=7 + L)
     qs, ks, vs = (si.storage(x) for x in (q, k, v))
@@ -169,19 +180,31 @@ def test_workload2_gqa_bf16_full_size():
     q, k, v = si.gqa_prompt()
     qs, ks, vs = (si.storage(x) for x in (q, k, v))
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    cache = cpk.KVCache(1, 8, 8192, 128, torch.bfloat16)
-    poison(cache)
-    out_c, widths = cpk.prefill_chunked(cache, 0, qd, kd, vd, 512, pad=True)
-    one = cpk.KVCache(1, 8, 8192, 128, torch.bfloat16)
-    cpk.cpk_kv_append(one, 0, kd, vd, 0)
-    out_1 = cpk.cpk_chunk_attention(qd, one, 0, 0)
-    torch.cuda.synchronize()
-    assert widths == [512] * 8    # 7 x 512 + 416 padded to 512: eight M=512 forwards
     chunks = cpk.cpk_split_chunks(4000, 512)
     rows = sample_rows(4000, chunks)
     ref = oracle_rows(qs, ks, vs, rows, oracle.BF16)
-    check(out_c[torch.from_numpy(rows).cuda()], ref, 2e-2, f"chunked vs oracle ({len(rows)} rows)")
-    assert bitwise(out_c, out_1), "chunked != one-shot"
+    one = cpk.KVCache(1, 8, 8192, 128, torch.bfloat16)
+    cpk.cpk_kv_append(one, 0, kd, vd, 0)
+    res = {}
+    for kind in ("auto", "narrow", "wide"):
+        with cpk.attention_kernel({"auto": 0, **KERNELS}[kind]):
+            cache = cpk.KVCache(1, 8, 8192, 128, torch.bfloat16)
+            poison(cache)
+            out_c, widths = cpk.prefill_chunked(cache, 0, qd, kd, vd, 512, pad=True)
+            out_1 = cpk.cpk_chunk_attention(qd, one, 0, 0)
+            torch.cuda.synchronize()
+        assert widths == [512] * 8    # 7 x 512 + 416 padded to 512: eight M=512 forwards
+        check(out_c[torch.from_numpy(rows).cuda()], ref, 2e-2,
+              f"[{kind}] chunked vs oracle ({len(rows)} rows)")
+        check(out_1[torch.from_numpy(rows).cuda()], ref, 2e-2,
+              f"[{kind}] one-shot vs oracle ({len(rows)} rows)")
+        res[kind] = (out_c, out_1)
+    for kind in ("narrow", "wide"):
+        assert bitwise(*res[kind]), f"[{kind}] chunked != one-shot"
+    # the automatic choice: 512-row chunks fill 128 wide workgroups (fewer
+    # than the 256 CUs) and take the narrow kernel; the 4000-row pass the wide
+    assert bitwise(res["auto"][0], res["narrow"][0])
+    assert bitwise(res["auto"][1], res["wide"][1])
     assert int(cache.seqlens_k[0]) == 4000
     assert np.array_equal(si.storage(cache.k[0, :, :4000]), ks.transpose(1, 0, 2))
     assert np.array_equal(si.storage(cache.v[0, :, :4000]), vs.transpose(1, 0, 2))
@@ -225,8 +248,14 @@ def test_workload3_ladder_twice_on_dirty_cache():
         check(outs[0][torch.from_numpy(rows).cuda()], ref, 2e-2, f"L={L} widths={widths}")
 
 
-def test_rows_equal_capacity_and_single_row_chunks():
-    say("case: W=1 chunks and a prompt filling the cache exactly")
+@pytest.mark.parametrize("kernel", ["narrow", "wide"])
+def test_rows_equal_capacity_and_single_row_chunks(kernel):
+    say(f"case: [{kernel}] W=1 chunks and a prompt filling the cache exactly")
+    with cpk.attention_kernel(KERNELS[kernel]):
+        _rows_equal_capacity_and_single_row_chunks()
+
+
+def _rows_equal_capacity_and_single_row_chunks():
     q, k, v = si.gqa_prompt(L=40, Hq=8, Hkv=2, D=128, seed=300)
     qs, ks, vs = (si.storage(x) for x in (q, k, v))
     ref = oracle.prefill_one_shot(oracle.Cache(oracle.BF16, 1, 2, 40, 128), 0, qs, ks, vs)
@@ -318,12 +347,18 @@ def test_workload4_rolling_full_size():
 
 # ------------------------------------------------ HIP graph replay
 
-def test_graph_replay_of_chunked_prefill():
+@pytest.mark.parametrize("kernel", ["narrow", "wide"])
+def test_graph_replay_of_chunked_prefill(kernel):
     """A chunked prefill (rewind, then cpk_prefill_chunk per chunk with the
     padded tail) captured once as a HIP graph: every replay, with eager work
     between replays, matches the eager run bit for bit (output, cache rows,
     seqlens_k)."""
-    say("case: HIP graph of rewind + padded chunked prefill (L=1300, W=512), 3 replays")
+    say(f"case: HIP graph [{kernel}] of rewind + padded chunked prefill (L=1300, W=512), 3 replays")
+    with cpk.attention_kernel(KERNELS[kernel]):
+        _graph_replay_of_chunked_prefill()
+
+
+def _graph_replay_of_chunked_prefill():
     L, W, Hq, Hkv, D = 1300, 512, 16, 4, 128
     q, k, v = si.gqa_prompt(L=L, Hq=Hq, Hkv=Hkv, D=D, seed=700)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
@@ -421,10 +456,12 @@ def _run_mixed(n_dec, ctx_lo, ctx_hi, prompt, budget, Hq, Hkv, D, seed, cap, che
     return step
 
 
-def test_mixed_step_small_full_compare():
-    say("case: mixed step small: 5 decodes ctx 20..300, prompt 700, budget 128, G=4")
-    steps = _run_mixed(5, 20, 300, 700, 128, 8, 2, 128, seed=500, cap=1024,
-                       check_steps=set(range(10)), every=1)
+@pytest.mark.parametrize("kernel", ["narrow", "wide"])
+def test_mixed_step_small_full_compare(kernel):
+    say(f"case: mixed step small [{kernel}]: 5 decodes ctx 20..300, prompt 700, budget 128, G=4")
+    with cpk.attention_kernel(KERNELS[kernel]):
+        steps = _run_mixed(5, 20, 300, 700, 128, 8, 2, 128, seed=500, cap=1024,
+                           check_steps=set(range(10)), every=1)
     assert steps == 6
 
 

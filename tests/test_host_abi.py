@@ -198,3 +198,21 @@ def test_roll_workspace_size():
     assert cpk.cpk_roll_workspace_size(32, 8, 8192, 4096, 128, torch.bfloat16) == 0
     # never more parts than key tiles
     assert cpk.cpk_roll_workspace_size(1, 1, 128, 64, 64, f16) == 0
+
+
+def test_attention_kernel_setting():
+    """The kernel choice is process-wide, returns the previous setting and
+    rejects unknown kinds without changing the setting."""
+    prev = cpk.cpk_set_attention_kernel(cpk.ATTN_WIDE)
+    try:
+        assert prev == cpk.ATTN_AUTO
+        assert cpk.cpk_set_attention_kernel(cpk.ATTN_NARROW) == cpk.ATTN_WIDE
+        with pytest.raises(cpk.CpkError):
+            cpk.cpk_set_attention_kernel(3)
+        with pytest.raises(cpk.CpkError):
+            cpk.cpk_set_attention_kernel(-1)
+        with cpk.attention_kernel(cpk.ATTN_WIDE):
+            assert cpk.cpk_set_attention_kernel(cpk.ATTN_WIDE) == cpk.ATTN_WIDE
+        assert cpk.cpk_set_attention_kernel(cpk.ATTN_AUTO) == cpk.ATTN_NARROW
+    finally:
+        cpk.cpk_set_attention_kernel(cpk.ATTN_AUTO)
