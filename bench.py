@@ -3,18 +3,20 @@
 
 Step = one chunked prefill of a 4000-token GQA prompt (32 query / 8 KV
 heads, head dim 128, bf16, cache bound at capacity 8192) in W = 512 chunks
-through the C ABI: rewind to 0, then cpk_prefill_chunk per chunk (padded
-append, the 416-row tail padded to 512, chunk attention, truncation, true
-length recorded).  The step is captured once as a HIP graph and replayed
+through the C ABI: rewind to 0, then cpk_prefill_chunk per chunk (one
+launch each: chunk attention that also appends the padded chunk's K/V to
+the cache, the 416-row tail padded to 512, truncation, true length
+recorded).  The step is captured once as a HIP graph and replayed
 (checked bit for bit against an eager step); the eager per-call step time is
 reported beside it.  Inputs are seeded synthetic N(0,1) values already
 resident in HBM.
 
 value  = algorithmic attention TFLOP/s of the whole step: 4*D*Hq flops per
          visible (query, key) pair, 131.10 GFLOP per step, / step time.
-roofline = the attention kernel alone: per-launch algorithmic flops over its
-         average launch duration (HIP events on the launch stream), against
-         the bf16 dense MFMA peak of 2.5 PFLOP/s.
+roofline = the attention kernel alone (each cpk_prefill_chunk launch):
+         per-launch algorithmic flops over its average launch duration (HIP
+         events on the launch stream), against the bf16 dense MFMA peak of
+         2.5 PFLOP/s.
 secondary = decode rows of the mixed-step workload (64 sequences, contexts
          uniform in [512, 16384]) as a decode-only packed step: KV bytes read
          per second against the 8 TB/s HBM peak; a steady-state W=512 chunk
@@ -95,18 +97,17 @@ def bench_chunked(cpk, si, torch, steps, warmup):
     flops = [chunk_flops(p, r, Hq, D) for p, r in chunks]
 
     def step(events):
+        # each padded chunk is one launch of the attention kernel, which
+        # also appends the chunk's K/V to the cache (fused append)
         if cache.lens[0]:
             cpk.cpk_rewind(cache, 0, 0)
         for i, (past, rows) in enumerate(chunks):
-            width = cpk.cpk_ladder_width(W, rows)
             sl = slice(past, past + rows)
-            cpk.cpk_kv_append(cache, 0, k[sl], v[sl], past, rows=width)
             if events is not None:
                 events[i][0].record(stream)
-            cpk.cpk_chunk_attention(q[sl], cache, 0, past, rows=width, out=out[sl])
+            cpk.cpk_prefill_chunk(q[sl], k[sl], v[sl], cache, 0, past, W, pad=True, out=out[sl])
             if events is not None:
                 events[i][1].record(stream)
-            cpk.cpk_rewind(cache, 0, past + rows)
 
     for _ in range(warmup):
         step(None)

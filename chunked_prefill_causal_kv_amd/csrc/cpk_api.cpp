@@ -208,9 +208,14 @@ int cpk_kv_append(const cpk_kv_cache *cache, int b, const void *k_new, const voi
                       "kv_append launch");
 }
 
+// Chunk attention; with k_new / v_new set (bf16/fp16 only) the kernel also
+// performs the chunk's append (fused): it reads the chunk's own keys from
+// the new rows, writes them to the cache (padded rows repeat the last real
+// row) and sets seqlens_k[b] = past_len + real_rows.
 static int attention_common(const void *q, const cpk_kv_cache *cache, int b, int q_heads,
                             int past_len, int rows, int real_rows, float scale, void *out,
-                            hipStream_t st)
+                            hipStream_t st, const void *k_new = nullptr,
+                            const void *v_new = nullptr)
 {
     int r = check_cache(cache);
     if (r) return r;
@@ -230,6 +235,10 @@ static int attention_common(const void *q, const cpk_kv_cache *cache, int b, int
     fill_scale(a, resolve_scale(scale, a.D));
     a.slot = b; a.q_row0 = 0; a.out_row0 = 0; a.rows = rows; a.q_src_rows = real_rows;
     a.out_rows = real_rows; a.n_keys = past_len + rows; a.key_lo = 0; a.causal_base = past_len;
+    if (k_new) {
+        a.k_new = k_new; a.v_new = v_new; a.new_base = past_len; a.new_rows = real_rows;
+        a.seqlens = cache->seqlens_k; a.len_after = past_len + real_rows;
+    }
     const bool wide = use_wide(cache->dtype, q_heads / cache->kv_heads, cache->kv_heads, rows);
     const int br = cpk::attn_rows_per_block(cache->dtype, q_heads / cache->kv_heads, wide);
     return hip_status(cpk::launch_attention(a, cache->dtype, (rows + br - 1) / br, 1, wide, st),
@@ -276,6 +285,16 @@ int cpk_prefill_chunk(const void *q, const void *k, const void *v, const cpk_kv_
         return fail(CPK_ECAPACITY, "prefill_chunk: %d + %d padded rows exceed capacity %d",
                     past_len, width, cache->capacity);
     hipStream_t st = (hipStream_t)stream;
+    if (cache->dtype != CPK_F32) {
+        // one launch: the attention kernel appends the chunk itself (it
+        // reads the chunk's keys from k/v, writes the padded rows to the
+        // cache and records the true length past_len + real_rows)
+        r = attention_common(q, cache, b, q_heads, past_len, width, real_rows, scale, out, st,
+                             k, v);
+        if (r) return r;
+        if (issued_rows) *issued_rows = width;
+        return ok();
+    }
     const int rb = cache->head_dim * elem_size(cache->dtype);
     // the append writes the padded rows but records the true length
     // past_len + real_rows (the rewind of the padding, folded into the copy;

@@ -49,6 +49,7 @@
 #include "cpk_internal.h"
 
 #include <hip/hip_bf16.h>
+#include <limits.h>
 #include <math.h>
 
 namespace cpk {
@@ -173,6 +174,66 @@ __device__ __forceinline__ bool resolve_seq(const AttnArgs &a, int z, SeqView &s
     return true;
 }
 
+// Fused append: the cache rows of one row block and KV head, copied from
+// the new rows in 16-byte pieces.  load() issues the reads (held in
+// registers), store() the writes; callers issue the writes before any tile
+// load, so the kernels' counted waits on tile loads stay exact (loads
+// complete in order; older outstanding stores only make a wait stricter).
+template <int D, int THREADS, int MAXROWS>
+struct FusedAppend {
+    static constexpr int NCH = D / 8;
+    static constexpr int PER = (MAXROWS * NCH * 2 + THREADS - 1) / THREADS;
+    uint4 val[PER];
+    __device__ __forceinline__ void load(const AttnArgs &a, int g, int r0, int n_rows, int tid)
+    {
+        const int n = n_rows * NCH;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int c = tid + j * THREADS;
+            if (c < 2 * n) {
+                const bool isv = c >= n;
+                const int cc = isv ? c - n : c;
+                const int src = min(r0 + cc / NCH, a.new_rows - 1);
+                const uint16_t *sp = (const uint16_t *)(isv ? a.v_new : a.k_new) +
+                                     ((int64_t)src * a.Hkv + g) * D + (cc % NCH) * 8;
+                val[j] = *(const uint4 *)sp;
+            }
+        }
+    }
+    __device__ __forceinline__ void store(const AttnArgs &a, int g, int r0, int n_rows, int tid)
+    {
+        const int n = n_rows * NCH;
+        uint16_t *ck = (uint16_t *)a.k + ((int64_t)a.slot * a.Hkv + g) * a.cap * D;
+        uint16_t *cv = (uint16_t *)a.v + ((int64_t)a.slot * a.Hkv + g) * a.cap * D;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int c = tid + j * THREADS;
+            if (c < 2 * n) {
+                const bool isv = c >= n;
+                const int cc = isv ? c - n : c;
+                uint16_t *dp = (isv ? cv : ck) + (int64_t)(a.new_base + r0 + cc / NCH) * D +
+                               (cc % NCH) * 8;
+                *(uint4 *)dp = val[j];
+            }
+        }
+        if (blockIdx.x == 0 && tid == 0) a.seqlens[a.slot] = a.len_after;
+    }
+};
+
+// Source of one 16-byte piece of a K or V tile: cache row `key` of this KV
+// head, or (fused append, key >= new_base) the matching new row.
+__device__ __forceinline__ const char *kv_src(const uint16_t *cache_head, const void *new_rows,
+                                              const AttnArgs &a, int g, int D, int key,
+                                              int chunk_elem)
+{
+    if (key >= a.new_base && new_rows) {
+        const int i = min(key - a.new_base, a.new_rows - 1);
+        return (const char *)((const uint16_t *)new_rows + ((int64_t)i * a.Hkv + g) * D +
+                              chunk_elem);
+    }
+    return (const char *)(cache_head + (int64_t)key * D + chunk_elem);
+}
+
 template <typename TR, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_mfma_kernel(AttnArgs a)
@@ -210,6 +271,15 @@ void attn_mfma_kernel(AttnArgs a)
 
     const uint16_t *kc = (const uint16_t *)a.k + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
     const uint16_t *vc = (const uint16_t *)a.v + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
+    const bool fused = a.k_new != nullptr;
+    // keys at or past new_lo come from the new rows (never from the cache)
+    const int new_lo = fused ? a.new_base : INT_MAX;
+    if (fused) {
+        FusedAppend<D, kThreads, kQC> ap;
+        const int n_rows = min(r0 + BR, sv.rows) - r0;
+        ap.load(a, g, r0, n_rows, tid);
+        ap.store(a, g, r0, n_rows, tid);
+    }
 
     // ---- query fragment (B operand of S^T = K Q^T): column qc
     uint4 qf[NS];
@@ -264,14 +334,14 @@ void attn_mfma_kernel(AttnArgs a)
         const int key0 = kt * kBK;
         const char *kt_base = (const char *)(kc + (int64_t)key0 * D);
         const char *vt_base = (const char *)(vc + (int64_t)key0 * D);
-        if (key0 + kBK <= sv.n_keys) {
+        if (key0 + kBK <= sv.n_keys && key0 + kBK <= new_lo) {
 #pragma unroll
             for (int i = 0; i < TL::LOADS; ++i) {
                 const int blk = i * TL::WAVES + wave;
                 load16(kt_base + koff[i], Kb + blk * 64 * 8);
                 load16(vt_base + voff[i], Vb + blk * 64 * 8);
             }
-        } else {
+        } else if (!fused) {
             // the tile runs past the last valid key: those rows re-read it
 #pragma unroll
             for (int i = 0; i < TL::LOADS; ++i) {
@@ -280,6 +350,17 @@ void attn_mfma_kernel(AttnArgs a)
                     (uint32_t)max(0, key0 + lrow[i] - (sv.n_keys - 1)) * (uint32_t)(D * 2);
                 load16(kt_base + (koff[i] - back), Kb + blk * 64 * 8);
                 load16(vt_base + (voff[i] - back), Vb + blk * 64 * 8);
+            }
+        } else {
+            // fused append: rows at or past new_base come from the new rows
+#pragma unroll
+            for (int i = 0; i < TL::LOADS; ++i) {
+                const int blk = i * TL::WAVES + wave;
+                const int key = min(key0 + lrow[i], sv.n_keys - 1);
+                const int kch = (int)(koff[i] / 2u) - lrow[i] * D;   // swizzled chunk element
+                const int vch = (int)(voff[i] / 2u) - lrow[i] * D;
+                load16(kv_src(kc, a.k_new, a, g, D, key, kch), Kb + blk * 64 * 8);
+                load16(kv_src(vc, a.v_new, a, g, D, key, vch), Vb + blk * 64 * 8);
             }
         }
     };
@@ -671,6 +752,13 @@ void attn_wide_kernel(AttnArgs a)
 
     const uint16_t *kc = (const uint16_t *)a.k + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
     const uint16_t *vc = (const uint16_t *)a.v + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
+    const bool fused = a.k_new != nullptr;
+    if (fused) {
+        FusedAppend<D, kWThreads, kWQC> ap;
+        const int n_rows = min(r0 + BR, sv.rows) - r0;
+        ap.load(a, g, r0, n_rows, tid);
+        ap.store(a, g, r0, n_rows, tid);
+    }
 
     // ---- query fragments (B operand of S^T = K Q^T) of the two column blocks
     uint4 qf[2][NS];
@@ -713,15 +801,30 @@ void attn_wide_kernel(AttnArgs a)
         const int key0 = kt * kWBK;
         const char *tb = (const char *)(base + (int64_t)key0 * D);
         const int clamp = sv.n_keys - 1 - key0;
+        if (!fused || key0 + kWBK <= a.new_base) {
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int blk = i * WAVES + wave;
-            const int t = blk * 64 + lane;
-            const int row = t / NCH;
-            const int pos = t % NCH;
-            const int sw = is_v ? TL::swz_v(row) : TL::swz_k(row);
-            const uint32_t off = (uint32_t)(min(row, clamp) * D + (pos ^ sw) * 8) * 2u;
-            load16(tb + off, dst + blk * 64 * 8);
+            for (int i = 0; i < LOADS; ++i) {
+                const int blk = i * WAVES + wave;
+                const int t = blk * 64 + lane;
+                const int row = t / NCH;
+                const int pos = t % NCH;
+                const int sw = is_v ? TL::swz_v(row) : TL::swz_k(row);
+                const uint32_t off = (uint32_t)(min(row, clamp) * D + (pos ^ sw) * 8) * 2u;
+                load16(tb + off, dst + blk * 64 * 8);
+            }
+        } else {
+            // fused append: rows at or past new_base come from the new rows
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int blk = i * WAVES + wave;
+                const int t = blk * 64 + lane;
+                const int row = t / NCH;
+                const int pos = t % NCH;
+                const int sw = is_v ? TL::swz_v(row) : TL::swz_k(row);
+                load16(kv_src(base, is_v ? a.v_new : a.k_new, a, g, D, key0 + min(row, clamp),
+                              (pos ^ sw) * 8),
+                       dst + blk * 64 * 8);
+            }
         }
     };
 

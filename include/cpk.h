@@ -162,11 +162,14 @@ int cpk_rewind(const cpk_kv_cache *cache, int b, int new_len, int cur_len,
  * v by repeating their last real row; append every padded row; attend
  * every padded row; write the real rows to out; rewind the cache to
  * past_len + real_rows.  q [real_rows][q_heads][D], k/v
- * [real_rows][kv_heads][D], out [real_rows][q_heads][D].  Same result as
- * cpk_kv_append(rows = width) + cpk_chunk_attention(rows = width) +
- * cpk_rewind(past_len + real_rows), in two launches (the append records the
- * true length); the padding is an index clamp inside the kernels, so no
- * scratch memory is used.
+ * [real_rows][kv_heads][D], out [real_rows][q_heads][D].  Same result
+ * (output bits, cache bytes, seqlens_k) as cpk_kv_append(rows = width) +
+ * cpk_chunk_attention(rows = width) + cpk_rewind(past_len + real_rows).
+ * bf16/fp16 run as one launch: the attention kernel reads the chunk's own
+ * keys from k/v and writes them to the cache itself (fused append); fp32
+ * runs as an append launch that records the true length plus an attention
+ * launch.  The padding is an index clamp inside the kernels, so no scratch
+ * memory is used.  k and v must not overlap the cache.
  * *issued_rows (may be NULL) receives the padded width.
  * CPK_EINVAL if real_rows < 1 or real_rows > W; CPK_ECAPACITY if the
  * padded rows do not fit.

@@ -173,6 +173,59 @@ def _chunked_prefill_full_compare(dtype, Hq, Hkv, D, L, W):
     assert np.array_equal(si.storage(c1.v[0, :, :L]), vs.transpose(1, 0, 2))
 
 
+@pytest.mark.parametrize("kernel", ["narrow", "wide"])
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,past,real,W", [
+    (torch.bfloat16, 32, 8, 128, 512, 416, 512),
+    (torch.bfloat16, 12, 4, 128, 77, 150, 512),
+    (torch.float16, 8, 2, 64, 300, 1, 96),
+    (torch.bfloat16, 16, 16, 128, 0, 200, 256),
+])
+def test_fused_append_matches_two_launches(kernel, dtype, Hq, Hkv, D, past, real, W):
+    """cpk_prefill_chunk appends inside the attention kernel: output bits,
+    every cache byte it writes (padded rows included) and seqlens_k equal
+    the separate append (padded width) + attention launches."""
+    say(f"case: fused append [{kernel}] {dtype} Hq={Hq} Hkv={Hkv} D={D} past={past} "
+        f"real={real} W={W}")
+    dn = {torch.bfloat16: "bf16", torch.float16: "f16"}[dtype]
+    q, k, v = si.gqa_prompt(L=past + real, Hq=Hq, Hkv=Hkv, D=D, dtype=dn, seed=900 + past)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    width = cpk.cpk_ladder_width(W, real)
+    cap = past + width + 64
+    with cpk.attention_kernel(KERNELS[kernel]):
+        caches, outs = [], []
+        for fused in (True, False):
+            c = cpk.KVCache(1, Hkv, cap, D, dtype)
+            poison(c)
+            if past:
+                cpk.cpk_kv_append(c, 0, kd[:past], vd[:past], 0)
+            sl = slice(past, past + real)
+            if fused:
+                out, w = cpk.cpk_prefill_chunk(qd[sl], kd[sl], vd[sl], c, 0, past, W, pad=True)
+                assert w == width
+            else:
+                cpk.cpk_kv_append(c, 0, kd[sl], vd[sl], past, rows=width)
+                out = cpk.cpk_chunk_attention(qd[sl], c, 0, past, rows=width)
+                cpk.cpk_rewind(c, 0, past + real)
+            torch.cuda.synchronize()
+            caches.append(c)
+            outs.append(out)
+    assert bitwise(outs[0], outs[1]), "fused output differs"
+    n = past + width
+    assert bitwise(caches[0].k[:, :, :n], caches[1].k[:, :, :n])
+    assert bitwise(caches[0].v[:, :, :n], caches[1].v[:, :, :n])
+    assert int(caches[0].seqlens_k[0]) == past + real == int(caches[1].seqlens_k[0])
+    # padded rows repeat the last real row
+    last = si.storage(k[past + real - 1])
+    for i in range(past + real, n):
+        assert np.array_equal(si.storage(caches[0].k[0, :, i]), last)
+    # bytes past the padded width are untouched (still the NaN poison)
+    assert torch.isnan(caches[0].k[:, :, n:].float()).all()
+    qs, ks, vs = (si.storage(x) for x in (q, k, v))
+    rows_idx = np.arange(past, past + real)
+    ref = oracle_rows(qs, ks, vs, rows_idx, ODT[dtype])
+    check(outs[0], ref, TOL[dtype], "fused vs oracle")
+
+
 # ---------------------------------------------- workload 2: GQA bf16 W=512
 
 def test_workload2_gqa_bf16_full_size():
