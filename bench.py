@@ -303,11 +303,13 @@ def bench_ladder(cpk, si, torch, reps=2):
             "note": "eager cpk_prefill_chunk calls (append + attention per chunk)"}
 
 
-def bench_rolling(cpk, si, torch, explicit_mask=True):
+def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=5):
     """Rolling right-aligned cache: 4096 fp16 tokens, 16 heads, C = 2048,
-    c = 256; per chunk roll_append (out of place, double-buffered) then
-    roll_attention with the explicit (c, C) additive mask (0 visible,
-    -32768 masked)."""
+    c = 256; per chunk roll_append (out of place, double-buffered: C rows
+    moved) then roll_attention, or with ring=True ring_append (c rows moved)
+    then ring_attention; with the explicit (c, C) additive mask (0 visible,
+    -32768 masked) or visibility computed in the kernel.  Median of reps
+    timed passes over the 16 chunks."""
     L, H, D, C, c = 4096, 16, 128, 2048, 256
     q, k, v = (x.cuda() for x in si.rolling_inputs())
     n = L // c
@@ -324,30 +326,56 @@ def bench_rolling(cpk, si, torch, explicit_mask=True):
     out = torch.empty_like(q)
 
     def run():
-        cur = 0
+        cur, start = 0, 0
         for j in range(n):
             sl = slice(j * c, (j + 1) * c)
+            m = masks[j] if explicit_mask else None
+            if ring:
+                start = cpk.cpk_ring_append(k[sl].unsqueeze(0), v[sl].unsqueeze(0), bufs[0],
+                                            bufs[1], start)
+                cpk.cpk_ring_attention(q[sl], bufs[0][0], bufs[1][0], (j + 1) * c, 0, start,
+                                       mask=m, out=out[sl])
+                continue
             ko, vo = bufs[2 * cur], bufs[2 * cur + 1]
             kn, vn = bufs[2 * (1 - cur)], bufs[2 * (1 - cur) + 1]
             cpk.cpk_roll_append(ko, vo, k[sl].unsqueeze(0), v[sl].unsqueeze(0), kn, vn)
             cur = 1 - cur
-            cpk.cpk_roll_attention(q[sl], kn[0], vn[0], (j + 1) * c, 0,
-                                   mask=masks[j] if explicit_mask else None, out=out[sl])
+            cpk.cpk_roll_attention(q[sl], kn[0], vn[0], (j + 1) * c, 0, mask=m, out=out[sl])
 
+    # the 16 chunks are captured once as a HIP graph (after an eager pass
+    # that also allocates the split workspace), so host launch gaps drop out
     run()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "replay differs"
+    ms = statistics.median(times)
     f = 4 * D * H * pairs
     how = "the explicit (c, C) mask" if explicit_mask else "visibility computed in the kernel"
-    return {"chunks": n, "gflop": round(f / 1e9, 2), "ms": round(ms, 4),
+    what = "ring_append + ring_attention" if ring else "roll_append + roll_attention"
+    return {"chunks": n, "gflop": round(f / 1e9, 2), "ms": round(ms, 4), "ms_min": round(min(times), 4),
             "tflops": round(f / (ms * 1e-3) / 1e12, 1), "dtype": "fp16",
-            "note": f"roll_append + roll_attention with {how}, per chunk"}
+            "note": f"{what} with {how}, per chunk; 16 chunks replayed as a HIP graph, "
+                    f"median of {reps} replays"}
 
 
 def bench_mixed(cpk, si, torch, budget):
@@ -502,6 +530,11 @@ def main():
         log(f"bench: rolling {secondary['rolling_fp16']}")
         secondary["rolling_fp16_computed_mask"] = bench_rolling(cpk, si, torch, False)
         log(f"bench: rolling {secondary['rolling_fp16_computed_mask']}")
+        secondary["rolling_fp16_ring"] = bench_rolling(cpk, si, torch, True, ring=True)
+        log(f"bench: rolling {secondary['rolling_fp16_ring']}")
+        secondary["rolling_fp16_ring_computed_mask"] = bench_rolling(cpk, si, torch, False,
+                                                                     ring=True)
+        log(f"bench: rolling {secondary['rolling_fp16_ring_computed_mask']}")
         for budget in (2048, 8192):
             mixed = bench_mixed(cpk, si, torch, budget)
             secondary[f"mixed_budget_{budget}"] = mixed

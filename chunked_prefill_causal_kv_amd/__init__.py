@@ -69,6 +69,9 @@ def _load() -> ctypes.CDLL:
         "cpk_roll_append": ([P, P, P, P, P, P, I, I, I, I, I, I, P], I),
         "cpk_roll_attention": ([P, P, P, P, I, I, I, I, I, I, I, I, F, P, P, Z, P], I),
         "cpk_roll_workspace_size": ([I, I, I, I, I, I], Z),
+        "cpk_ring_append": ([P, P, P, P, I, I, I, I, I, I, I, P], I),
+        "cpk_ring_attention": ([P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, Z, P], I),
+        "cpk_ring_view": ([P, P, P, P, I, I, I, I, I, I, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -336,6 +339,46 @@ def cpk_roll_attention(q, k, v, abs_end: int, n_leftpad: int, mask=None, scale: 
     return out
 
 
+def cpk_ring_append(k_chunk, v_chunk, k_ring, v_ring, start: int, stream=None) -> int:
+    """Write chunk rows [B, c, H, D] over the c oldest slots of rings
+    [B, H, C, D] whose logical slot 0 is physical `start`; returns the new
+    start (start + c) mod C."""
+    B, H, C, D = k_ring.shape
+    c = k_chunk.shape[1]
+    _check(_lib.cpk_ring_append(_ptr(k_chunk), _ptr(v_chunk), _ptr(k_ring), _ptr(v_ring), B, H,
+                                C, c, D, DTYPE_CODE[k_ring.dtype], start, _stream(stream)))
+    return (start + c) % C
+
+
+def cpk_ring_attention(q, k_ring, v_ring, abs_end: int, n_leftpad: int, start: int, mask=None,
+                       scale: float = 0.0, out=None, stream=None, split: bool = True):
+    """cpk_roll_attention over a ring k/v [Hkv, C, D] with logical slot 0 at
+    physical `start`."""
+    c, Hq, D = q.shape
+    Hkv, C, _ = k_ring.shape
+    if out is None:
+        out = torch.empty_like(q)
+    ws = None
+    if split:
+        ws = _roll_workspace(cpk_roll_workspace_size(Hq, Hkv, C, c, D, q.dtype), q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * 4
+    _check(_lib.cpk_ring_attention(_ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(mask), abs_end,
+                                   n_leftpad, Hq, Hkv, C, c, D, DTYPE_CODE[q.dtype],
+                                   float(scale), start, _ptr(out), _ptr(ws), ws_bytes,
+                                   _stream(stream)))
+    return out
+
+
+def cpk_ring_view(k_ring, v_ring, start: int, k_out=None, v_out=None, stream=None):
+    """The logical (literal-shift) view of rings [B, H, C, D]."""
+    B, H, C, D = k_ring.shape
+    k_out = torch.empty_like(k_ring) if k_out is None else k_out
+    v_out = torch.empty_like(v_ring) if v_out is None else v_out
+    _check(_lib.cpk_ring_view(_ptr(k_ring), _ptr(v_ring), _ptr(k_out), _ptr(v_out), B, H, C, D,
+                              DTYPE_CODE[k_ring.dtype], start, _stream(stream)))
+    return k_out, v_out
+
+
 # ------------------------------------------------------------------- drivers
 
 def prefill_chunked(cache: KVCache, b: int, q, k, v, W: int, pad: bool = True,
@@ -382,3 +425,29 @@ def roll_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream
         cpk_roll_attention(q[sl], kn[0], vn[0], (j + 1) * c, n_left, mask=m, scale=scale,
                            out=out[sl], stream=stream, split=split)
     return out, n_left, bufs[2 * cur][0], bufs[2 * cur + 1][0]
+
+
+def ring_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream=None,
+                 split: bool = True):
+    """roll_prefill over a ring buffer: per chunk, cpk_ring_append (c rows
+    moved) and cpk_ring_attention.  Same outputs, bit for bit.  Returns
+    (out over the padded sequence, n_leftpad, k ring, v ring, start)."""
+    L, Hq, D = q.shape
+    Hkv = k.shape[1]
+    n_left = (-L) % c
+    if n_left:
+        z = lambda x: torch.cat([torch.zeros((n_left,) + tuple(x.shape[1:]), dtype=x.dtype,
+                                             device=x.device), x])
+        q, k, v = z(q), z(k), z(v)
+    Lp = L + n_left
+    kr = torch.zeros((1, Hkv, C, D), dtype=q.dtype, device=q.device)
+    vr = torch.zeros_like(kr)
+    out = torch.empty_like(q)
+    start = 0
+    for j in range(Lp // c):
+        sl = slice(j * c, (j + 1) * c)
+        start = cpk_ring_append(k[sl].unsqueeze(0), v[sl].unsqueeze(0), kr, vr, start, stream)
+        m = None if masks is None else masks[j]
+        cpk_ring_attention(q[sl], kr[0], vr[0], (j + 1) * c, n_left, start, mask=m, scale=scale,
+                           out=out[sl], stream=stream, split=split)
+    return out, n_left, kr[0], vr[0], start

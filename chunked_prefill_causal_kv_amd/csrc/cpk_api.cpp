@@ -458,10 +458,10 @@ size_t cpk_roll_workspace_size(int Hq, int Hkv, int C, int c, int head_dim, int 
     return (size_t)parts * (size_t)c * (size_t)Hq * (size_t)(head_dim + 4) * sizeof(float);
 }
 
-int cpk_roll_attention(const void *q, const void *k, const void *v, const void *mask,
-                       int abs_end, int n_leftpad, int Hq, int Hkv, int C, int c, int D,
-                       int dtype, float scale, void *out, void *ws, size_t ws_bytes,
-                       void *stream)
+static int roll_attention_impl(const void *q, const void *k, const void *v, const void *mask,
+                               int abs_end, int n_leftpad, int Hq, int Hkv, int C, int c, int D,
+                               int dtype, float scale, int ring_start, void *out, void *ws,
+                               size_t ws_bytes, void *stream)
 {
     int r = check_dtype_dim(dtype, D);
     if (r) return r;
@@ -502,6 +502,7 @@ int cpk_roll_attention(const void *q, const void *k, const void *v, const void *
     a.n_parts = parts;
     a.part_tiles = pt;
     a.part_ws = (float *)ws;
+    a.ring_start = ring_start;
     const int br = cpk::attn_rows_per_block(dtype, Hq / Hkv, false);
     r = hip_status(
         cpk::launch_attention(a, dtype, (c + br - 1) / br, 1, false, (hipStream_t)stream),
@@ -509,6 +510,72 @@ int cpk_roll_attention(const void *q, const void *k, const void *v, const void *
     if (r || parts <= 1) return r;
     return hip_status(cpk::launch_attention_combine(a, dtype, (hipStream_t)stream),
                       "roll_attention combine");
+}
+
+int cpk_roll_attention(const void *q, const void *k, const void *v, const void *mask,
+                       int abs_end, int n_leftpad, int Hq, int Hkv, int C, int c, int D,
+                       int dtype, float scale, void *out, void *ws, size_t ws_bytes,
+                       void *stream)
+{
+    return roll_attention_impl(q, k, v, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D, dtype, scale,
+                               0, out, ws, ws_bytes, stream);
+}
+
+int cpk_ring_attention(const void *q, const void *k_ring, const void *v_ring, const void *mask,
+                       int abs_end, int n_leftpad, int Hq, int Hkv, int C, int c, int D,
+                       int dtype, float scale, int start, void *out, void *ws, size_t ws_bytes,
+                       void *stream)
+{
+    if (C < 1 || start < 0 || start >= C)
+        return fail(CPK_EINVAL, "ring_attention: start=%d outside [0, C=%d)", start, C);
+    return roll_attention_impl(q, k_ring, v_ring, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D,
+                               dtype, scale, start, out, ws, ws_bytes, stream);
+}
+
+int cpk_ring_append(const void *k_chunk, const void *v_chunk, void *k_ring, void *v_ring, int B,
+                    int H, int C, int c, int D, int dtype, int start, void *stream)
+{
+    int r = check_dtype_dim(dtype, D);
+    if (r) return r;
+    if (B < 1 || H < 1 || C < 1 || c < 1 || c > C || start < 0 || start >= C)
+        return fail(CPK_EINVAL, "ring_append: B=%d H=%d C=%d c=%d start=%d", B, H, C, c, start);
+    if (!k_chunk || !v_chunk || !k_ring || !v_ring)
+        return fail(CPK_EINVAL, "ring_append: NULL buffer");
+    if (!aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(k_ring) || !aligned16(v_ring))
+        return fail(CPK_EALIGN, "ring_append: buffer not aligned");
+    const size_t ring_bytes = (size_t)B * H * C * D * elem_size(dtype);
+    const size_t chunk_bytes = (size_t)B * H * c * D * elem_size(dtype);
+    const void *srcs[2] = {k_chunk, v_chunk};
+    for (int i = 0; i < 2; ++i)
+        if (overlaps(srcs[i], chunk_bytes, k_ring, ring_bytes) ||
+            overlaps(srcs[i], chunk_bytes, v_ring, ring_bytes))
+            return fail(CPK_EINVAL, "ring_append: a chunk overlaps a ring");
+    if (overlaps(k_ring, ring_bytes, v_ring, ring_bytes))
+        return fail(CPK_EINVAL, "ring_append: k_ring and v_ring overlap");
+    return hip_status(cpk::launch_ring_append(k_chunk, v_chunk, k_ring, v_ring, B, H, C, c,
+                                              D * elem_size(dtype), start, (hipStream_t)stream),
+                      "ring_append launch");
+}
+
+int cpk_ring_view(const void *k_ring, const void *v_ring, void *k_out, void *v_out, int B, int H,
+                  int C, int D, int dtype, int start, void *stream)
+{
+    int r = check_dtype_dim(dtype, D);
+    if (r) return r;
+    if (B < 1 || H < 1 || C < 1 || start < 0 || start >= C)
+        return fail(CPK_EINVAL, "ring_view: B=%d H=%d C=%d start=%d", B, H, C, start);
+    if (!k_ring || !v_ring || !k_out || !v_out) return fail(CPK_EINVAL, "ring_view: NULL buffer");
+    if (!aligned16(k_ring) || !aligned16(v_ring) || !aligned16(k_out) || !aligned16(v_out))
+        return fail(CPK_EALIGN, "ring_view: buffer not aligned");
+    const size_t bytes = (size_t)B * H * C * D * elem_size(dtype);
+    const void *ins[2] = {k_ring, v_ring};
+    for (int i = 0; i < 2; ++i)
+        if (overlaps(ins[i], bytes, k_out, bytes) || overlaps(ins[i], bytes, v_out, bytes))
+            return fail(CPK_EINVAL, "ring_view: output overlaps a ring");
+    if (overlaps(k_out, bytes, v_out, bytes)) return fail(CPK_EINVAL, "ring_view: outputs overlap");
+    return hip_status(cpk::launch_ring_view(k_ring, v_ring, k_out, v_out, B, H, C,
+                                            D * elem_size(dtype), start, (hipStream_t)stream),
+                      "ring_view launch");
 }
 
 }  // extern "C"

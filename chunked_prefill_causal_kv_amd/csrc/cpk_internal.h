@@ -69,6 +69,10 @@ struct AttnArgs {
     int new_rows;
     int32_t *seqlens;
     int len_after;
+
+    // rolling ring buffer (64-column kernel): logical key s of the rolling
+    // view sits at physical row (ring_start + s) mod cap; 0 = no ring
+    int ring_start;
 };
 
 // Split-KV decode: one query row per sequence.
@@ -103,6 +107,13 @@ hipError_t launch_set_len(int32_t *seqlens, int b, int len, hipStream_t st);
 hipError_t launch_roll_append(const void *k_old, const void *v_old, const void *k_chunk,
                               const void *v_chunk, void *k_new, void *v_new, int B, int H,
                               int C, int c, int row_bytes, hipStream_t st);
+// ring buffer: chunk row t of (b, h) -> physical slot (start + t) mod C
+hipError_t launch_ring_append(const void *k_chunk, const void *v_chunk, void *k_ring,
+                              void *v_ring, int B, int H, int C, int c, int row_bytes, int start,
+                              hipStream_t st);
+// logical view: out slot s <- physical slot (start + s) mod C
+hipError_t launch_ring_view(const void *k_ring, const void *v_ring, void *k_out, void *v_out,
+                            int B, int H, int C, int row_bytes, int start, hipStream_t st);
 
 // Attention: grid.x = row blocks x KV heads (KV head fastest), grid.z = sequences.
 // `wide` selects the 128-column bf16/fp16 kernel (chunk and varlen

@@ -220,8 +220,9 @@ struct FusedAppend {
     }
 };
 
-// Source of one 16-byte piece of a K or V tile: cache row `key` of this KV
-// head, or (fused append, key >= new_base) the matching new row.
+// Source of one 16-byte piece of a K or V tile: the cache row of logical
+// key `key` of this KV head (physical row (ring_start + key) mod cap), or
+// (fused append, key >= new_base) the matching new row.
 __device__ __forceinline__ const char *kv_src(const uint16_t *cache_head, const void *new_rows,
                                               const AttnArgs &a, int g, int D, int key,
                                               int chunk_elem)
@@ -231,7 +232,9 @@ __device__ __forceinline__ const char *kv_src(const uint16_t *cache_head, const 
         return (const char *)((const uint16_t *)new_rows + ((int64_t)i * a.Hkv + g) * D +
                               chunk_elem);
     }
-    return (const char *)(cache_head + (int64_t)key * D + chunk_elem);
+    int phys = key + a.ring_start;
+    if (phys >= a.cap) phys -= a.cap;
+    return (const char *)(cache_head + (int64_t)phys * D + chunk_elem);
 }
 
 template <typename TR, int D>
@@ -332,16 +335,21 @@ void attn_mfma_kernel(AttnArgs a)
     auto issue_tile = [&](int kt, uint16_t *Kb) {
         uint16_t *Vb = Kb + kBK * D;
         const int key0 = kt * kBK;
-        const char *kt_base = (const char *)(kc + (int64_t)key0 * D);
-        const char *vt_base = (const char *)(vc + (int64_t)key0 * D);
-        if (key0 + kBK <= sv.n_keys && key0 + kBK <= new_lo) {
+        // physical row of the tile's first key (rolling ring buffer; the
+        // identity otherwise), and whether the tile's rows stay contiguous
+        int phys0 = key0 + a.ring_start;
+        if (phys0 >= a.cap) phys0 -= a.cap;
+        const bool nowrap = phys0 + kBK <= a.cap;
+        const char *kt_base = (const char *)(kc + (int64_t)phys0 * D);
+        const char *vt_base = (const char *)(vc + (int64_t)phys0 * D);
+        if (key0 + kBK <= sv.n_keys && key0 + kBK <= new_lo && nowrap) {
 #pragma unroll
             for (int i = 0; i < TL::LOADS; ++i) {
                 const int blk = i * TL::WAVES + wave;
                 load16(kt_base + koff[i], Kb + blk * 64 * 8);
                 load16(vt_base + voff[i], Vb + blk * 64 * 8);
             }
-        } else if (!fused) {
+        } else if (!fused && nowrap) {
             // the tile runs past the last valid key: those rows re-read it
 #pragma unroll
             for (int i = 0; i < TL::LOADS; ++i) {
@@ -352,7 +360,8 @@ void attn_mfma_kernel(AttnArgs a)
                 load16(vt_base + (voff[i] - back), Vb + blk * 64 * 8);
             }
         } else {
-            // fused append: rows at or past new_base come from the new rows
+            // per-row sources: fused append (rows at or past new_base come
+            // from the new rows) or a ring tile that wraps around
 #pragma unroll
             for (int i = 0; i < TL::LOADS; ++i) {
                 const int blk = i * TL::WAVES + wave;

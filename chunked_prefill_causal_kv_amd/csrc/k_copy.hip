@@ -115,6 +115,48 @@ int grid_for(int64_t items)
     return (int)blocks;
 }
 
+// Ring-buffer append: the c new rows overwrite the c oldest physical slots.
+__global__ void ring_append_kernel(const vec16 *__restrict__ kc, const vec16 *__restrict__ vc,
+                                   vec16 *__restrict__ kr, vec16 *__restrict__ vr, int B, int H,
+                                   int C, int c, int vpr, int start)
+{
+    const int64_t total = (int64_t)B * c * H * vpr;   // chunk order [B][c][H][vpr]
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int e = (int)(i % vpr);
+        const int64_t r1 = i / vpr;
+        const int h = (int)(r1 % H);
+        const int64_t r2 = r1 / H;
+        const int t = (int)(r2 % c);
+        const int b = (int)(r2 / c);
+        int slot = start + t;
+        if (slot >= C) slot -= C;
+        const int64_t dst = (((int64_t)b * H + h) * C + slot) * vpr + e;
+        kr[dst] = kc[i];
+        vr[dst] = vc[i];
+    }
+}
+
+// Logical view of a ring: slot s of the output is physical slot (start + s) mod C.
+__global__ void ring_view_kernel(const vec16 *__restrict__ kr, const vec16 *__restrict__ vr,
+                                 vec16 *__restrict__ ko, vec16 *__restrict__ vo, int B, int H,
+                                 int C, int vpr, int start)
+{
+    const int64_t total = (int64_t)B * H * C * vpr;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int e = (int)(i % vpr);
+        const int64_t r1 = i / vpr;
+        const int s = (int)(r1 % C);
+        const int64_t bh = r1 / C;
+        int slot = start + s;
+        if (slot >= C) slot -= C;
+        const int64_t src = (bh * C + slot) * vpr + e;
+        ko[i] = kr[src];
+        vo[i] = vr[src];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_kv_append(const void *k_new, const void *v_new, void *ck, void *cv,
@@ -158,6 +200,29 @@ hipError_t launch_roll_append(const void *k_old, const void *v_old, const void *
     hipLaunchKernelGGL(roll_append_kernel, dim3(grid_for(items)), dim3(256), 0, st,
                        (const vec16 *)k_old, (const vec16 *)v_old, (const vec16 *)k_chunk,
                        (const vec16 *)v_chunk, (vec16 *)k_new, (vec16 *)v_new, B, H, C, c, vpr);
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_append(const void *k_chunk, const void *v_chunk, void *k_ring,
+                              void *v_ring, int B, int H, int C, int c, int row_bytes, int start,
+                              hipStream_t st)
+{
+    const int vpr = row_bytes / 16;
+    const int64_t items = (int64_t)B * c * H * vpr;
+    hipLaunchKernelGGL(ring_append_kernel, dim3(grid_for(items)), dim3(256), 0, st,
+                       (const vec16 *)k_chunk, (const vec16 *)v_chunk, (vec16 *)k_ring,
+                       (vec16 *)v_ring, B, H, C, c, vpr, start);
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_view(const void *k_ring, const void *v_ring, void *k_out, void *v_out,
+                            int B, int H, int C, int row_bytes, int start, hipStream_t st)
+{
+    const int vpr = row_bytes / 16;
+    const int64_t items = (int64_t)B * H * C * vpr;
+    hipLaunchKernelGGL(ring_view_kernel, dim3(grid_for(items)), dim3(256), 0, st,
+                       (const vec16 *)k_ring, (const vec16 *)v_ring, (vec16 *)k_out,
+                       (vec16 *)v_out, B, H, C, vpr, start);
     return hipGetLastError();
 }
 

@@ -255,6 +255,45 @@ int cpk_roll_attention(const void *q, const void *k, const void *v,
                        void *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Rolling cache as a ring buffer (the rolling cache of the Horizon developer
+ * blog "Chunk Prefill", sections 3 and 4, without the O(C) shift per chunk).
+ * A ring of C physical slots per (batch, head), [B][H][C][D], and a start
+ * index: logical slot s (0 = oldest, C-1 = newest) of the literal shifted
+ * cache cat(old, chunk)[c:] is physical slot (start + s) mod C.  The caller
+ * keeps start; a ring that starts zeroed with start = 0 matches a literal
+ * cache that starts zeroed.
+ *
+ * cpk_ring_append writes the c chunk rows ([B][c][H][D]) over the c oldest
+ * slots, physical (start + t) mod C for row t; the caller then sets
+ * start = (start + c) mod C, after which the logical view equals the
+ * literal shift byte for byte.  O(c) bytes moved instead of O(C).
+ * CPK_EINVAL if c > C, start outside [0, C), or a chunk overlaps a ring.
+ */
+int cpk_ring_append(const void *k_chunk, const void *v_chunk, void *k_ring, void *v_ring,
+                    int B, int H, int C, int c, int D, int dtype, int start, void *stream);
+
+/*
+ * cpk_roll_attention over a ring (batch 1: k_ring / v_ring [Hkv][C][D]) whose
+ * logical slot 0 is physical slot `start` (the value after the chunk's
+ * append).  Keys are visited in logical order, so the result is bit-identical
+ * to cpk_roll_attention over the literal shifted cache; mask, workspace and
+ * errors as there, plus CPK_EINVAL if start is outside [0, C).
+ */
+int cpk_ring_attention(const void *q, const void *k_ring, const void *v_ring,
+                       const void *mask, int abs_end, int n_leftpad, int Hq, int Hkv,
+                       int C, int c, int D, int dtype, float scale, int start, void *out,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The logical view of a ring as a contiguous cache: out slot s = physical
+ * slot (start + s) mod C, for K and V, [B][H][C][D] each (interoperation
+ * and checks; not on the per-chunk path).  CPK_EINVAL if start is outside
+ * [0, C) or an output overlaps an input.
+ */
+int cpk_ring_view(const void *k_ring, const void *v_ring, void *k_out, void *v_out, int B,
+                  int H, int C, int D, int dtype, int start, void *stream);
+
+/*
  * Workspace bytes cpk_roll_attention uses for a split key range with these
  * shapes: parts x c x Hq x (head_dim + 4) x 4 (one fp32 record per part,
  * row and query head: running maximum, sum, two pad words, the partial

@@ -398,6 +398,73 @@ def test_workload4_rolling_full_size():
     check(out[torch.from_numpy(rows).cuda()], ref, 2e-2, f"sliding window ({len(rows)} rows)")
 
 
+@pytest.mark.parametrize("L,C,c,H,D", [
+    (1000, 512, 128, 4, 128),    # 24 left-pad rows, start walks 0, 128, 256, 384
+    (1000, 300, 96, 2, 64),      # C not a multiple of the key tile, start wraps mid-tile
+    (700, 256, 256, 3, 128),     # c == C: every append overwrites the whole ring
+])
+def test_ring_matches_literal_shift(L, C, c, H, D):
+    """The ring-buffer rolling cache: after every chunk its logical view
+    equals the literal shift cat(old, chunk)[c:] byte for byte, and ring
+    attention equals rolling attention over the literal cache bit for bit
+    (both mask forms, split and unsplit), and the oracle within tolerance."""
+    say(f"case: ring vs literal shift fp16 L={L} C={C} c={c} H={H} D={D}")
+    q, k, v = si.rolling_inputs(L=L, H=H, D=D, seed=410 + C)
+    qs, ks, vs = (si.storage(x) for x in (q, k, v))
+    ref, n_left, rk, rv, masks = oracle.roll_prefill(qs, ks, vs, C, c, oracle.F16)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    mk = [torch.from_numpy(m.astype(np.float16)).cuda() for m in masks]
+    # per chunk: literal double buffer against the ring and its view
+    z = lambda x: torch.cat([torch.zeros((n_left,) + tuple(x.shape[1:]), dtype=x.dtype,
+                                         device=x.device), x])
+    qp, kp, vp = z(qd), z(kd), z(vd)
+    bufs = [torch.zeros((1, H, C, D), dtype=torch.float16, device="cuda") for _ in range(4)]
+    kr = torch.zeros((1, H, C, D), dtype=torch.float16, device="cuda")
+    vr = torch.zeros_like(kr)
+    start, cur = 0, 0
+    for j in range(qp.shape[0] // c):
+        sl = slice(j * c, (j + 1) * c)
+        ko, vo = bufs[2 * cur], bufs[2 * cur + 1]
+        kn, vn = bufs[2 * (1 - cur)], bufs[2 * (1 - cur) + 1]
+        cpk.cpk_roll_append(ko, vo, kp[sl].unsqueeze(0), vp[sl].unsqueeze(0), kn, vn)
+        cur = 1 - cur
+        start = cpk.cpk_ring_append(kp[sl].unsqueeze(0), vp[sl].unsqueeze(0), kr, vr, start)
+        assert start == ((j + 1) * c) % C
+        kview, vview = cpk.cpk_ring_view(kr, vr, start)
+        torch.cuda.synchronize()
+        assert bitwise(kview, kn) and bitwise(vview, vn), f"chunk {j}: ring view != literal shift"
+        for split in (True, False):
+            for m in (None, mk[j]):
+                lit = cpk.cpk_roll_attention(qp[sl], kn[0], vn[0], (j + 1) * c, n_left, mask=m,
+                                             split=split)
+                rng = cpk.cpk_ring_attention(qp[sl], kr[0], vr[0], (j + 1) * c, n_left, start,
+                                             mask=m, split=split)
+                torch.cuda.synchronize()
+                assert bitwise(lit, rng), f"chunk {j} split={split} mask={m is not None}"
+    out_r, nl, gk, gv, st = cpk.ring_prefill(qd, kd, vd, C, c)
+    torch.cuda.synchronize()
+    assert nl == n_left and st == start
+    kview, vview = cpk.cpk_ring_view(gk.unsqueeze(0), gv.unsqueeze(0), st)
+    assert np.array_equal(si.storage(kview[0]), rk) and np.array_equal(si.storage(vview[0]), rv)
+    check(out_r[n_left:], ref[n_left:], 2e-2, "ring prefill vs oracle (real rows)")
+
+
+def test_workload4_ring_full_size():
+    L, C, c, H, D = 4096, 2048, 256, 16, 128
+    say(f"case: workload 4 on the ring buffer, L={L} C={C} c={c} H={H}: bit-equal to the shift")
+    q, k, v = si.rolling_inputs()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    masks = [torch.from_numpy(oracle.chunk_mask(L, 0, j, c, C).astype(np.float16)).cuda()
+             for j in range(L // c)]
+    for m in (None, masks):
+        lit, _, lk, lv = cpk.roll_prefill(qd, kd, vd, C, c, masks=m)
+        rng, _, rk, rv, st = cpk.ring_prefill(qd, kd, vd, C, c, masks=m)
+        torch.cuda.synchronize()
+        assert st == 0     # 16 chunks of 256 = 2 full turns of the ring
+        assert bitwise(lit, rng), f"mask={m is not None}: ring output differs"
+        assert bitwise(rk, lk) and bitwise(rv, lv)
+
+
 # ------------------------------------------------ HIP graph replay
 
 @pytest.mark.parametrize("kernel", ["narrow", "wide"])

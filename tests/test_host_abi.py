@@ -216,3 +216,30 @@ def test_attention_kernel_setting():
         assert cpk.cpk_set_attention_kernel(cpk.ATTN_AUTO) == cpk.ATTN_NARROW
     finally:
         cpk.cpk_set_attention_kernel(cpk.ATTN_AUTO)
+
+
+def test_ring_validation():
+    """Ring-buffer entry points reject bad shapes, start indices and aliasing
+    on the host (fake aligned pointers, never dereferenced)."""
+    F16 = cpk.CPK_F16
+    ap = cpk._lib.cpk_ring_append
+    big = FAKE * 64   # far from the other fake buffers
+    # start outside [0, C)
+    assert ap(FAKE, FAKE * 2, big, big * 2, 1, 2, 8, 4, 64, F16, 8, None) == cpk.CPK_EINVAL
+    assert ap(FAKE, FAKE * 2, big, big * 2, 1, 2, 8, 4, 64, F16, -1, None) == cpk.CPK_EINVAL
+    # c > C
+    assert ap(FAKE, FAKE * 2, big, big * 2, 1, 2, 8, 9, 64, F16, 0, None) == cpk.CPK_EINVAL
+    # a chunk overlapping a ring
+    assert ap(big, FAKE * 2, big, big * 2, 1, 2, 8, 4, 64, F16, 0, None) == cpk.CPK_EINVAL
+    # unaligned
+    assert ap(FAKE + 8, FAKE * 2, big, big * 2, 1, 2, 8, 4, 64, F16, 0, None) == cpk.CPK_EALIGN
+    # bad head dim
+    assert ap(FAKE, FAKE * 2, big, big * 2, 1, 2, 8, 4, 96, F16, 0, None) == cpk.CPK_EDTYPE
+    at = cpk._lib.cpk_ring_attention
+    assert at(FAKE, FAKE, FAKE, None, 4096, 0, 16, 16, 2048, 256, 128, F16, 0.0, 2048, FAKE,
+              None, 0, None) == cpk.CPK_EINVAL
+    assert at(FAKE, FAKE, FAKE, None, 100, 0, 16, 16, 64, 128, 128, F16, 0.0, 0, FAKE,
+              None, 0, None) == cpk.CPK_EINVAL
+    vw = cpk._lib.cpk_ring_view
+    assert vw(FAKE, FAKE * 2, big, big * 2, 1, 2, 8, 64, F16, 8, None) == cpk.CPK_EINVAL
+    assert vw(FAKE, FAKE * 2, FAKE, big * 2, 1, 2, 8, 64, F16, 0, None) == cpk.CPK_EINVAL
