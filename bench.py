@@ -378,11 +378,16 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=5):
                     f"median of {reps} replays"}
 
 
-def bench_mixed(cpk, si, torch, budget):
+def bench_mixed(cpk, si, torch, budget, overlap=False, reps=3):
     """Mixed step: 64 running decodes (contexts U[512, 16384]) plus a
-    20,000-token prompt under a token budget, one cpk_varlen_step per step
-    (packed inputs built before timing).  Each step is compared with
-    sum = bytes/HBM + flops/MFMA and max = max of the two (perfect overlap)."""
+    20,000-token prompt under a token budget, one packed step per budget
+    (packed inputs built before timing): cpk_varlen_step, or with
+    overlap=True the decode rows and the prompt rows on two streams.  Each
+    step is compared with sum = bytes/HBM + flops/MFMA and max = max of the
+    two (perfect overlap).  The whole schedule is also captured as a HIP
+    graph and replayed: its time per step is the inter-token latency proxy
+    of the running decodes (one token each per step) and its total the
+    time-to-first-token proxy of the prompt (ready after its last chunk)."""
     Hq, Hkv, D, CAP, P = 32, 8, 128, 20480, 20000
     ctxs = si.mixed_contexts()
     n_dec = len(ctxs)
@@ -412,11 +417,18 @@ def bench_mixed(cpk, si, torch, budget):
         lens = [x + 1 for x in lens]
         done += rows
 
+    side = torch.cuda.Stream()
+
     def run(events=None):
         for i, (q, kn, vn, slots, cu, past, meta, ws, out, _, _) in enumerate(steps):
             if events is not None:
                 events[i][0].record(torch.cuda.current_stream())
-            cpk.cpk_varlen_step(q, kn, vn, cache, slots, cu, past, out=out, ws=ws, dev_meta=meta)
+            if overlap:
+                cpk.varlen_step_overlapped(q, kn, vn, cache, slots, cu, past, side, out=out,
+                                           ws=ws, dev_meta=meta)
+            else:
+                cpk.cpk_varlen_step(q, kn, vn, cache, slots, cu, past, out=out, ws=ws,
+                                    dev_meta=meta)
             if events is not None:
                 events[i][1].record(torch.cuda.current_stream())
 
@@ -426,6 +438,30 @@ def bench_mixed(cpk, si, torch, budget):
     run(evs)
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in evs]
+    ref_out = [st[8].clone() for st in steps]
+    # the whole schedule as one graph (steps rewrite the same cache rows,
+    # so replays are repeatable)
+    cap_stream = torch.cuda.Stream()
+    cap_stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap_stream):
+        run()
+    torch.cuda.current_stream().wait_stream(cap_stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    g_ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(torch.cuda.current_stream())
+        graph.replay()
+        e1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        g_ms.append(e0.elapsed_time(e1))
+    for st, ro in zip(steps, ref_out):
+        assert torch.equal(st[8].view(torch.int16), ro.view(torch.int16)), "replay differs"
+    g_tot = statistics.median(g_ms)
     table = []
     for (*_, kv_bytes, flops), m in zip(steps, ms):
         t_mem = kv_bytes / (PEAK_HBM_GBPS * 1e9) * 1e3
@@ -434,11 +470,13 @@ def bench_mixed(cpk, si, torch, budget):
                       "max_bound_ms": round(max(t_mem, t_mma), 4),
                       "tflops": round(flops / (m * 1e-3) / 1e12, 1)})
     tot = sum(ms)
-    return {"budget": budget, "steps": len(steps), "ms_total": round(tot, 3),
-            "ms_per_step": round(tot / len(steps), 4),
+    return {"budget": budget, "streams": 2 if overlap else 1, "steps": len(steps),
+            "ms_total": round(g_tot, 3), "ms_per_step": round(g_tot / len(steps), 4),
+            "itl_proxy_ms": round(g_tot / len(steps), 4), "ttft_proxy_ms": round(g_tot, 3),
+            "ms_total_eager_calls": round(tot, 3),
             "sum_bound_ms_total": round(sum(t["sum_bound_ms"] for t in table), 3),
             "max_bound_ms_total": round(sum(t["max_bound_ms"] for t in table), 3),
-            "per_step": table}
+            "per_step_eager": table}
 
 
 def calibrate_copy(cpk, torch, reps=3):
@@ -536,11 +574,14 @@ def main():
                                                                      ring=True)
         log(f"bench: rolling {secondary['rolling_fp16_ring_computed_mask']}")
         for budget in (2048, 8192):
-            mixed = bench_mixed(cpk, si, torch, budget)
-            secondary[f"mixed_budget_{budget}"] = mixed
-            log(f"bench: mixed budget {budget}: {mixed['ms_per_step']} ms/step over "
-                f"{mixed['steps']} steps (bounds: sum {mixed['sum_bound_ms_total']} ms, "
-                f"max {mixed['max_bound_ms_total']} ms in total)")
+            for overlap in (False, True):
+                mixed = bench_mixed(cpk, si, torch, budget, overlap)
+                key = f"mixed_budget_{budget}" + ("_two_streams" if overlap else "")
+                secondary[key] = mixed
+                log(f"bench: mixed budget {budget}, {mixed['streams']} stream(s): "
+                    f"{mixed['ms_per_step']} ms/step over {mixed['steps']} steps, TTFT proxy "
+                    f"{mixed['ttft_proxy_ms']} ms (bounds: sum {mixed['sum_bound_ms_total']} ms, "
+                    f"max {mixed['max_bound_ms_total']} ms in total)")
     sha = attn_src_sha()
     value = r["total_flops"] / (ms_graph * 1e-3) / 1e12
     line = {

@@ -66,6 +66,7 @@ def _load() -> ctypes.CDLL:
         "cpk_prefill_chunk": ([P, P, P, CP, I, I, I, I, I, I, F, P, IP, P], I),
         "cpk_varlen_workspace_size": ([I, I, I, I], Z),
         "cpk_varlen_step": ([P, P, P, CP, P, P, P, I32P, I32P, I32P, I, I, I, F, P, P, Z, P], I),
+        "cpk_varlen_step_phases": ([P, P, P, CP, P, P, P, I32P, I32P, I32P, I, I, I, F, P, P, Z, I, P], I),
         "cpk_roll_append": ([P, P, P, P, P, P, I, I, I, I, I, I, P], I),
         "cpk_roll_attention": ([P, P, P, P, I, I, I, I, I, I, I, I, F, P, P, Z, P], I),
         "cpk_roll_workspace_size": ([I, I, I, I, I, I], Z),
@@ -258,14 +259,17 @@ def cpk_varlen_workspace_size(n_seqs: int, q_heads: int, max_ctx: int, head_dim:
     return int(_lib.cpk_varlen_workspace_size(n_seqs, q_heads, max_ctx, head_dim))
 
 
+PHASE_APPEND, PHASE_DECODE, PHASE_PREFILL, PHASE_ALL = 1, 2, 4, 7
+
+
 def cpk_varlen_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache: KVCache,
                     slots: Sequence[int], cu_rows: Sequence[int], past_lens: Sequence[int],
                     scale: float = 0.0, out: Optional[torch.Tensor] = None,
                     ws: Optional[torch.Tensor] = None, dev_meta: Optional[torch.Tensor] = None,
-                    stream=None) -> torch.Tensor:
-    """One packed mixed step.  slots/cu_rows/past_lens are host sequences;
-    their device copies go in dev_meta (int32 [3*n+1], built here if not
-    given)."""
+                    stream=None, phases: int = PHASE_ALL) -> torch.Tensor:
+    """One packed mixed step (or the given phases of it).  slots/cu_rows/
+    past_lens are host sequences; their device copies go in dev_meta (int32
+    [3*n+1], built here if not given)."""
     n = len(slots)
     total, Hq, D = q.shape
     if out is None:
@@ -284,11 +288,46 @@ def cpk_varlen_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, c
     if ws is None:
         ws = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
     ws_bytes = ws.numel() * ws.element_size()
-    _check(_lib.cpk_varlen_step(_ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(cache.desc),
-                                d_slots, d_cu, d_past, h_slots, h_cu, h_past, n, total, Hq,
-                                float(scale), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
-    for s, slot in enumerate(slots):
-        cache.lens[slot] = past_lens[s] + cu_rows[s + 1] - cu_rows[s]
+    _check(_lib.cpk_varlen_step_phases(_ptr(q), _ptr(k_new), _ptr(v_new),
+                                       ctypes.byref(cache.desc), d_slots, d_cu, d_past, h_slots,
+                                       h_cu, h_past, n, total, Hq, float(scale), _ptr(out),
+                                       _ptr(ws), ws_bytes, int(phases), _stream(stream)))
+    if phases & PHASE_APPEND:
+        for s, slot in enumerate(slots):
+            cache.lens[slot] = past_lens[s] + cu_rows[s + 1] - cu_rows[s]
+    return out
+
+
+def cpk_varlen_step_phases(q, k_new, v_new, cache: KVCache, slots, cu_rows, past_lens,
+                           phases: int, scale: float = 0.0, out=None, ws=None, dev_meta=None,
+                           stream=None):
+    """The given phases (PHASE_APPEND | PHASE_DECODE | PHASE_PREFILL) of a
+    packed mixed step."""
+    return cpk_varlen_step(q, k_new, v_new, cache, slots, cu_rows, past_lens, scale, out, ws,
+                           dev_meta, stream, phases)
+
+
+def varlen_step_overlapped(q, k_new, v_new, cache: KVCache, slots, cu_rows, past_lens,
+                           side_stream, scale: float = 0.0, out=None, ws=None, dev_meta=None):
+    """One packed mixed step with the decode rows and the prompt rows on two
+    streams: append + decode on the current stream, the prompt attention on
+    side_stream after the append; the current stream then waits for it.
+    Same outputs as cpk_varlen_step, bit for bit."""
+    if out is None:
+        out = torch.empty_like(q)
+    if dev_meta is None:
+        dev_meta = torch.tensor(list(slots) + list(cu_rows) + list(past_lens),
+                                dtype=torch.int32).to(q.device)
+    main = torch.cuda.current_stream()
+    cpk_varlen_step(q, k_new, v_new, cache, slots, cu_rows, past_lens, scale, out, ws, dev_meta,
+                    phases=PHASE_APPEND)
+    side_stream.wait_stream(main)
+    with torch.cuda.stream(side_stream):
+        cpk_varlen_step(q, k_new, v_new, cache, slots, cu_rows, past_lens, scale, out, ws,
+                        dev_meta, phases=PHASE_PREFILL)
+    cpk_varlen_step(q, k_new, v_new, cache, slots, cu_rows, past_lens, scale, out, ws, dev_meta,
+                    phases=PHASE_DECODE)
+    main.wait_stream(side_stream)
     return out
 
 

@@ -323,6 +323,21 @@ int cpk_varlen_step(const void *q, const void *k_new, const void *v_new,
                     const int32_t *h_past_lens, int n_seqs, int total_rows, int q_heads,
                     float scale, void *out, void *ws, size_t ws_bytes, void *stream)
 {
+    return cpk_varlen_step_phases(q, k_new, v_new, cache, slots, cu_rows, past_lens, h_slots,
+                                  h_cu_rows, h_past_lens, n_seqs, total_rows, q_heads, scale,
+                                  out, ws, ws_bytes, CPK_PHASE_ALL, stream);
+}
+
+int cpk_varlen_step_phases(const void *q, const void *k_new, const void *v_new,
+                           const cpk_kv_cache *cache, const int32_t *slots,
+                           const int32_t *cu_rows, const int32_t *past_lens,
+                           const int32_t *h_slots, const int32_t *h_cu_rows,
+                           const int32_t *h_past_lens, int n_seqs, int total_rows, int q_heads,
+                           float scale, void *out, void *ws, size_t ws_bytes, int phases,
+                           void *stream)
+{
+    if (phases < 1 || (phases & ~CPK_PHASE_ALL))
+        return fail(CPK_EINVAL, "varlen: phases=%d", phases);
     int r = check_cache(cache);
     if (r) return r;
     if ((r = check_heads(q_heads, cache->kv_heads))) return r;
@@ -359,7 +374,7 @@ int cpk_varlen_step(const void *q, const void *k_new, const void *v_new,
         }
     }
     const int max_segs = (max_ctx + cpk::kDecodeSeg - 1) / cpk::kDecodeSeg;
-    if (n_dec > 0) {
+    if (n_dec > 0 && (phases & CPK_PHASE_DECODE)) {
         const size_t need = cpk_varlen_workspace_size(n_seqs, q_heads, max_ctx, cache->head_dim);
         if (!ws || ws_bytes < need)
             return fail(CPK_EWORKSPACE, "varlen: workspace %zu bytes, need %zu", ws_bytes, need);
@@ -367,13 +382,16 @@ int cpk_varlen_step(const void *q, const void *k_new, const void *v_new,
     }
     hipStream_t st = (hipStream_t)stream;
     const int rb = cache->head_dim * elem_size(cache->dtype);
-    r = hip_status(cpk::launch_kv_append_varlen(k_new, v_new, cache->k, cache->v, cache->seqlens_k,
-                                                cache->kv_heads, cache->capacity, rb, cu_rows,
-                                                past_lens, slots, n_seqs, total_rows, st),
-                   "varlen append");
-    if (r) return r;
+    if (phases & CPK_PHASE_APPEND) {
+        r = hip_status(cpk::launch_kv_append_varlen(k_new, v_new, cache->k, cache->v,
+                                                    cache->seqlens_k, cache->kv_heads,
+                                                    cache->capacity, rb, cu_rows, past_lens,
+                                                    slots, n_seqs, total_rows, st),
+                       "varlen append");
+        if (r) return r;
+    }
     const float sc = resolve_scale(scale, cache->head_dim);
-    if (n_dec > 0) {
+    if (n_dec > 0 && (phases & CPK_PHASE_DECODE)) {
         cpk::DecodeArgs d = {};
         d.q = q; d.k = cache->k; d.v = cache->v; d.out = out; d.ws = (float *)ws;
         d.Hq = q_heads; d.Hkv = cache->kv_heads; d.D = cache->head_dim; d.cap = cache->capacity;
@@ -383,7 +401,7 @@ int cpk_varlen_step(const void *q, const void *k_new, const void *v_new,
         r = hip_status(cpk::launch_decode(d, cache->dtype, max_segs, st), "varlen decode");
         if (r) return r;
     }
-    if (n_pre > 0) {
+    if (n_pre > 0 && (phases & CPK_PHASE_PREFILL)) {
         cpk::AttnArgs a = {};
         a.q = q; a.k = cache->k; a.v = cache->v; a.out = out; a.mask = nullptr;
         a.Hq = q_heads; a.Hkv = cache->kv_heads; a.D = cache->head_dim; a.cap = cache->capacity;

@@ -52,6 +52,14 @@ enum cpk_status {
 
 enum cpk_dtype { CPK_F32 = 0, CPK_F16 = 1, CPK_BF16 = 2 };
 
+/* phases of a packed mixed step (cpk_varlen_step_phases) */
+enum cpk_varlen_phase {
+    CPK_PHASE_APPEND = 1,    /* every sequence's new rows into the cache      */
+    CPK_PHASE_DECODE = 2,    /* one-row sequences: split-KV decode + combine  */
+    CPK_PHASE_PREFILL = 4,   /* sequences of two or more rows: chunk attention */
+    CPK_PHASE_ALL = 7,
+};
+
 /* bf16/fp16 attention kernel choice (cpk_set_attention_kernel) */
 enum cpk_attention_kernel {
     CPK_ATTN_AUTO = 0,     /* by launch size (the default)                  */
@@ -211,6 +219,23 @@ int cpk_varlen_step(const void *q, const void *k_new, const void *v_new,
                     const int32_t *h_past_lens, int n_seqs, int total_rows,
                     int q_heads, float scale, void *out, void *ws,
                     size_t ws_bytes, void *stream);
+
+/*
+ * cpk_varlen_step restricted to the given phases (a nonzero subset of
+ * CPK_PHASE_ALL), with the same arguments, validation and errors.  The
+ * decode and prefill phases read the cache after the append and write
+ * disjoint output rows (decode also the workspace), so a caller may run
+ * APPEND | DECODE on one stream and PREFILL on a second stream that waits
+ * for the first's append; cpk_varlen_step is all three on one stream.  The
+ * outputs are bit-identical either way.
+ */
+int cpk_varlen_step_phases(const void *q, const void *k_new, const void *v_new,
+                           const cpk_kv_cache *cache, const int32_t *slots,
+                           const int32_t *cu_rows, const int32_t *past_lens,
+                           const int32_t *h_slots, const int32_t *h_cu_rows,
+                           const int32_t *h_past_lens, int n_seqs, int total_rows, int q_heads,
+                           float scale, void *out, void *ws, size_t ws_bytes, int phases,
+                           void *stream);
 
 /*
  * Rolling fixed-capacity cache step (Horizon developer blog "Chunk

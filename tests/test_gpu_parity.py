@@ -585,6 +585,47 @@ def test_mixed_step_small_full_compare(kernel):
     assert steps == 6
 
 
+def test_mixed_step_two_streams_bit_equal():
+    """Decode rows and prompt rows of each packed step on two streams
+    (append + decode on the current stream, the prompt attention on a side
+    stream after the append): outputs and cache bit-identical to the
+    single-stream step, over the budgeted steps of a small mixed workload."""
+    say("case: mixed step on two streams vs one: 6 decodes ctx 30..900, prompt 1500, budget 256")
+    n_dec, Hq, Hkv, D, cap, prompt, budget = 6, 16, 4, 128, 2048, 1500, 256
+    ctxs = si.mixed_contexts(n_dec, 30, 900, seed=520)
+    caches = []
+    for _ in range(2):
+        c = cpk.KVCache(n_dec + 1, Hkv, cap, D, torch.bfloat16)
+        si.fill_seeded(c.k, 521)
+        si.fill_seeded(c.v, 522)
+        caches.append(c)
+    pq, pk, pv = (x.cuda() for x in si.gqa_prompt(L=prompt, Hq=Hq, Hkv=Hkv, D=D, seed=523))
+    g = si.generator(524)
+    side = torch.cuda.Stream()
+    done, lens, steps = 0, list(ctxs), 0
+    while done < prompt:
+        rows = cpk.cpk_plan_step(budget, n_dec, prompt - done)
+        dq = si.randn((n_dec, Hq, D), "bf16", g).cuda()
+        dk = si.randn((n_dec, Hkv, D), "bf16", g).cuda()
+        dv = si.randn((n_dec, Hkv, D), "bf16", g).cuda()
+        q = torch.cat([dq, pq[done:done + rows]])
+        kn = torch.cat([dk, pk[done:done + rows]])
+        vn = torch.cat([dv, pv[done:done + rows]])
+        slots = list(range(n_dec + 1))
+        cu = list(range(n_dec + 1)) + [n_dec + rows]
+        past = lens + [done]
+        o1 = cpk.cpk_varlen_step(q, kn, vn, caches[0], slots, cu, past)
+        o2 = cpk.varlen_step_overlapped(q, kn, vn, caches[1], slots, cu, past, side)
+        torch.cuda.synchronize()
+        assert bitwise(o1, o2), f"step {steps}: two-stream output differs"
+        lens = [x + 1 for x in lens]
+        done += rows
+        steps += 1
+    assert bitwise(caches[0].k, caches[1].k) and bitwise(caches[0].v, caches[1].v)
+    assert torch.equal(caches[0].seqlens_k, caches[1].seqlens_k)
+    say(f"  {steps} steps bit-identical")
+
+
 def test_workload5_mixed_full_size_budget_2048():
     say("case: workload 5: 64 decodes ctx U[512,16384], 20000-token prompt, budget 2048")
     steps = _run_mixed(64, 512, 16384, 20000, 2048, 32, 8, 128, seed=si.SEEDS["mixed"],

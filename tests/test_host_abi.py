@@ -243,3 +243,12 @@ def test_ring_validation():
     vw = cpk._lib.cpk_ring_view
     assert vw(FAKE, FAKE * 2, big, big * 2, 1, 2, 8, 64, F16, 8, None) == cpk.CPK_EINVAL
     assert vw(FAKE, FAKE * 2, FAKE, big * 2, 1, 2, 8, 64, F16, 0, None) == cpk.CPK_EINVAL
+
+
+def test_varlen_phases_validation():
+    """cpk_varlen_step_phases takes a nonzero subset of the three phases."""
+    f = cpk._lib.cpk_varlen_step_phases
+    for bad in (0, 8, -1, 15):
+        r = f(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None, 1, 1, 8, 0.0, FAKE,
+              FAKE, 0, bad, None)
+        assert r == cpk.CPK_EINVAL, bad
