@@ -378,7 +378,7 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=5):
                     f"median of {reps} replays"}
 
 
-def bench_mixed(cpk, si, torch, budget, overlap=False, reps=3):
+def bench_mixed(cpk, si, torch, budget, overlap=False, reps=3, paged=False):
     """Mixed step: 64 running decodes (contexts U[512, 16384]) plus a
     20,000-token prompt under a token budget, one packed step per budget
     (packed inputs built before timing): cpk_varlen_step, or with
@@ -387,11 +387,21 @@ def bench_mixed(cpk, si, torch, budget, overlap=False, reps=3):
     two (perfect overlap).  The whole schedule is also captured as a HIP
     graph and replayed: its time per step is the inter-token latency proxy
     of the running decodes (one token each per step) and its total the
-    time-to-first-token proxy of the prompt (ready after its last chunk)."""
+    time-to-first-token proxy of the prompt (ready after its last chunk).
+    paged=True runs the same steps over a paged cache (256-position blocks,
+    block table a seeded shuffle of the pool)."""
     Hq, Hkv, D, CAP, P = 32, 8, 128, 20480, 20000
     ctxs = si.mixed_contexts()
     n_dec = len(ctxs)
-    cache = cpk.KVCache(n_dec + 1, Hkv, CAP, D, torch.bfloat16)
+    if paged:
+        bs = 256
+        maxb = CAP // bs
+        nb = (n_dec + 1) * maxb
+        cache = cpk.PagedKVCache(n_dec + 1, Hkv, nb, bs, maxb, D, torch.bfloat16)
+        perm = torch.randperm(nb, generator=si.generator(35))
+        cache.block_table.copy_(perm.view(n_dec + 1, maxb).to(torch.int32))
+    else:
+        cache = cpk.KVCache(n_dec + 1, Hkv, CAP, D, torch.bfloat16)
     si.fill_seeded(cache.k, 31)
     si.fill_seeded(cache.v, 32)
     pq, pk, pv = (x.cuda() for x in si.gqa_prompt(L=P, seed=33))
@@ -470,7 +480,8 @@ def bench_mixed(cpk, si, torch, budget, overlap=False, reps=3):
                       "max_bound_ms": round(max(t_mem, t_mma), 4),
                       "tflops": round(flops / (m * 1e-3) / 1e12, 1)})
     tot = sum(ms)
-    return {"budget": budget, "streams": 2 if overlap else 1, "steps": len(steps),
+    return {"budget": budget, "streams": 2 if overlap else 1, "paged": paged,
+            "steps": len(steps),
             "ms_total": round(g_tot, 3), "ms_per_step": round(g_tot / len(steps), 4),
             "itl_proxy_ms": round(g_tot / len(steps), 4), "ttft_proxy_ms": round(g_tot, 3),
             "ms_total_eager_calls": round(tot, 3),
@@ -573,15 +584,18 @@ def main():
         secondary["rolling_fp16_ring_computed_mask"] = bench_rolling(cpk, si, torch, False,
                                                                      ring=True)
         log(f"bench: rolling {secondary['rolling_fp16_ring_computed_mask']}")
-        for budget in (2048, 8192):
-            for overlap in (False, True):
-                mixed = bench_mixed(cpk, si, torch, budget, overlap)
-                key = f"mixed_budget_{budget}" + ("_two_streams" if overlap else "")
-                secondary[key] = mixed
-                log(f"bench: mixed budget {budget}, {mixed['streams']} stream(s): "
-                    f"{mixed['ms_per_step']} ms/step over {mixed['steps']} steps, TTFT proxy "
-                    f"{mixed['ttft_proxy_ms']} ms (bounds: sum {mixed['sum_bound_ms_total']} ms, "
-                    f"max {mixed['max_bound_ms_total']} ms in total)")
+        for budget, overlap, paged in ((2048, False, False), (2048, True, False),
+                                       (2048, False, True), (8192, False, False),
+                                       (8192, True, False)):
+            mixed = bench_mixed(cpk, si, torch, budget, overlap, paged=paged)
+            key = (f"mixed_budget_{budget}" + ("_two_streams" if overlap else "") +
+                   ("_paged" if paged else ""))
+            secondary[key] = mixed
+            log(f"bench: mixed budget {budget}, {mixed['streams']} stream(s)"
+                f"{', paged' if paged else ''}: "
+                f"{mixed['ms_per_step']} ms/step over {mixed['steps']} steps, TTFT proxy "
+                f"{mixed['ttft_proxy_ms']} ms (bounds: sum {mixed['sum_bound_ms_total']} ms, "
+                f"max {mixed['max_bound_ms_total']} ms in total)")
     sha = attn_src_sha()
     value = r["total_flops"] / (ms_graph * 1e-3) / 1e12
     line = {

@@ -41,6 +41,15 @@ class cpk_kv_cache(ctypes.Structure):
                 ("dtype", ctypes.c_int32)]
 
 
+class cpk_paged_cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("seqlens_k", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run "
@@ -50,6 +59,7 @@ def _load() -> ctypes.CDLL:
     IP = ctypes.POINTER(ctypes.c_int)
     I32P = ctypes.POINTER(ctypes.c_int32)
     CP = ctypes.POINTER(cpk_kv_cache)
+    PCP = ctypes.POINTER(cpk_paged_cache)
     F = ctypes.c_float
     sig = {
         "cpk_version": ([], I),
@@ -66,6 +76,7 @@ def _load() -> ctypes.CDLL:
         "cpk_prefill_chunk": ([P, P, P, CP, I, I, I, I, I, I, F, P, IP, P], I),
         "cpk_varlen_workspace_size": ([I, I, I, I], Z),
         "cpk_varlen_step": ([P, P, P, CP, P, P, P, I32P, I32P, I32P, I, I, I, F, P, P, Z, P], I),
+        "cpk_paged_varlen_step": ([P, P, P, PCP, P, P, P, I32P, I32P, I32P, I, I, I, F, P, P, Z, I, P], I),
         "cpk_varlen_step_phases": ([P, P, P, CP, P, P, P, I32P, I32P, I32P, I, I, I, F, P, P, Z, I, P], I),
         "cpk_roll_append": ([P, P, P, P, P, P, I, I, I, I, I, I, P], I),
         "cpk_roll_attention": ([P, P, P, P, I, I, I, I, I, I, I, I, F, P, P, Z, P], I),
@@ -133,6 +144,41 @@ class KVCache:
     @property
     def head_dim(self):
         return self.desc.head_dim
+
+
+class PagedKVCache:
+    """Paged cache: K/V pools [n_blocks, kv_heads, block_size, head_dim], a
+    device block table [batch, max_blocks] (int32) that the caller fills
+    (blocks may be shared between slots), seqlens_k on the device and a host
+    mirror `lens`."""
+
+    def __init__(self, batch: int, kv_heads: int, n_blocks: int, block_size: int,
+                 max_blocks: int, head_dim: int, dtype=torch.bfloat16, device="cuda"):
+        shape = (n_blocks, kv_heads, block_size, head_dim)
+        self.k = torch.zeros(shape, dtype=dtype, device=device)
+        self.v = torch.zeros(shape, dtype=dtype, device=device)
+        self.block_table = torch.zeros((batch, max_blocks), dtype=torch.int32, device=device)
+        self.seqlens_k = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.lens = [0] * batch
+        self.dtype = dtype
+        self.desc = cpk_paged_cache(self.k.data_ptr(), self.v.data_ptr(),
+                                    self.block_table.data_ptr(), self.seqlens_k.data_ptr(),
+                                    batch, kv_heads, block_size, n_blocks, max_blocks, head_dim,
+                                    DTYPE_CODE[dtype])
+
+    @property
+    def block_size(self):
+        return self.desc.block_size
+
+    def gather(self, slot: int, n: int):
+        """Positions [0, n) of a slot as contiguous [kv_heads, n, head_dim]
+        K and V (a copy, for checks)."""
+        bs = self.block_size
+        nb = (n + bs - 1) // bs
+        ids = self.block_table[slot, :nb].long()
+        k = self.k[ids].permute(1, 0, 2, 3).reshape(self.k.shape[1], nb * bs, -1)[:, :n]
+        v = self.v[ids].permute(1, 0, 2, 3).reshape(self.v.shape[1], nb * bs, -1)[:, :n]
+        return k, v
 
 
 # ---------------------------------------------------------------- host logic
@@ -262,13 +308,13 @@ def cpk_varlen_workspace_size(n_seqs: int, q_heads: int, max_ctx: int, head_dim:
 PHASE_APPEND, PHASE_DECODE, PHASE_PREFILL, PHASE_ALL = 1, 2, 4, 7
 
 
-def cpk_varlen_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache: KVCache,
+def cpk_varlen_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache,
                     slots: Sequence[int], cu_rows: Sequence[int], past_lens: Sequence[int],
                     scale: float = 0.0, out: Optional[torch.Tensor] = None,
                     ws: Optional[torch.Tensor] = None, dev_meta: Optional[torch.Tensor] = None,
                     stream=None, phases: int = PHASE_ALL) -> torch.Tensor:
-    """One packed mixed step (or the given phases of it).  slots/cu_rows/
-    past_lens are host sequences; their device copies go in dev_meta (int32
+    """One packed mixed step (or the given phases of it) over a KVCache or a
+    PagedKVCache.  slots/cu_rows/past_lens are host sequences; their device copies go in dev_meta (int32
     [3*n+1], built here if not given)."""
     n = len(slots)
     total, Hq, D = q.shape
@@ -288,10 +334,11 @@ def cpk_varlen_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, c
     if ws is None:
         ws = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
     ws_bytes = ws.numel() * ws.element_size()
-    _check(_lib.cpk_varlen_step_phases(_ptr(q), _ptr(k_new), _ptr(v_new),
-                                       ctypes.byref(cache.desc), d_slots, d_cu, d_past, h_slots,
-                                       h_cu, h_past, n, total, Hq, float(scale), _ptr(out),
-                                       _ptr(ws), ws_bytes, int(phases), _stream(stream)))
+    fn = (_lib.cpk_paged_varlen_step if isinstance(cache, PagedKVCache)
+          else _lib.cpk_varlen_step_phases)
+    _check(fn(_ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(cache.desc), d_slots, d_cu,
+              d_past, h_slots, h_cu, h_past, n, total, Hq, float(scale), _ptr(out), _ptr(ws),
+              ws_bytes, int(phases), _stream(stream)))
     if phases & PHASE_APPEND:
         for s, slot in enumerate(slots):
             cache.lens[slot] = past_lens[s] + cu_rows[s + 1] - cu_rows[s]
@@ -303,6 +350,15 @@ def cpk_varlen_step_phases(q, k_new, v_new, cache: KVCache, slots, cu_rows, past
                            stream=None):
     """The given phases (PHASE_APPEND | PHASE_DECODE | PHASE_PREFILL) of a
     packed mixed step."""
+    return cpk_varlen_step(q, k_new, v_new, cache, slots, cu_rows, past_lens, scale, out, ws,
+                           dev_meta, stream, phases)
+
+
+def cpk_paged_varlen_step(q, k_new, v_new, cache: PagedKVCache, slots, cu_rows, past_lens,
+                          phases: int = PHASE_ALL, scale: float = 0.0, out=None, ws=None,
+                          dev_meta=None, stream=None):
+    """A packed mixed step (or the given phases) over a paged cache."""
+    assert isinstance(cache, PagedKVCache)
     return cpk_varlen_step(q, k_new, v_new, cache, slots, cu_rows, past_lens, scale, out, ws,
                            dev_meta, stream, phases)
 

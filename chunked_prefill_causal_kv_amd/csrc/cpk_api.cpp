@@ -5,6 +5,7 @@
 #include "cpk_internal.h"
 
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -328,6 +329,24 @@ int cpk_varlen_step(const void *q, const void *k_new, const void *v_new,
                                   out, ws, ws_bytes, CPK_PHASE_ALL, stream);
 }
 
+}  // extern "C"
+
+// Block-table addressing of a paged pool (nullptr: contiguous cache).
+struct Paging {
+    const int32_t *table;
+    int max_blocks, block_size, n_blocks;
+};
+
+static int varlen_impl(const void *q, const void *k_new, const void *v_new,
+                       const cpk_kv_cache *cache, const Paging *pg, const int32_t *slots,
+                       const int32_t *cu_rows, const int32_t *past_lens,
+                       const int32_t *h_slots, const int32_t *h_cu_rows,
+                       const int32_t *h_past_lens, int n_seqs, int total_rows, int q_heads,
+                       float scale, void *out, void *ws, size_t ws_bytes, int phases,
+                       void *stream);
+
+extern "C" {
+
 int cpk_varlen_step_phases(const void *q, const void *k_new, const void *v_new,
                            const cpk_kv_cache *cache, const int32_t *slots,
                            const int32_t *cu_rows, const int32_t *past_lens,
@@ -335,6 +354,51 @@ int cpk_varlen_step_phases(const void *q, const void *k_new, const void *v_new,
                            const int32_t *h_past_lens, int n_seqs, int total_rows, int q_heads,
                            float scale, void *out, void *ws, size_t ws_bytes, int phases,
                            void *stream)
+{
+    return varlen_impl(q, k_new, v_new, cache, nullptr, slots, cu_rows, past_lens, h_slots,
+                       h_cu_rows, h_past_lens, n_seqs, total_rows, q_heads, scale, out, ws,
+                       ws_bytes, phases, stream);
+}
+
+int cpk_paged_varlen_step(const void *q, const void *k_new, const void *v_new,
+                          const cpk_paged_cache *pc, const int32_t *slots,
+                          const int32_t *cu_rows, const int32_t *past_lens,
+                          const int32_t *h_slots, const int32_t *h_cu_rows,
+                          const int32_t *h_past_lens, int n_seqs, int total_rows, int q_heads,
+                          float scale, void *out, void *ws, size_t ws_bytes, int phases,
+                          void *stream)
+{
+    if (!pc) return fail(CPK_EINVAL, "paged: cache is NULL");
+    if (!pc->block_table) return fail(CPK_EINVAL, "paged: block_table is NULL");
+    if (pc->block_size < 256 || pc->block_size % 256 != 0)
+        return fail(CPK_EINVAL, "paged: block_size %d must be a positive multiple of 256",
+                    pc->block_size);
+    if (pc->n_blocks < 1 || pc->max_blocks < 1)
+        return fail(CPK_EINVAL, "paged: n_blocks=%d max_blocks=%d", pc->n_blocks, pc->max_blocks);
+    if ((int64_t)pc->max_blocks * pc->block_size > INT32_MAX / 2)
+        return fail(CPK_EINVAL, "paged: max_blocks x block_size too large");
+    if (pc->dtype == CPK_F32) return fail(CPK_EDTYPE, "paged: bf16 or fp16 only");
+    if (((uintptr_t)pc->block_table & 3u) != 0)
+        return fail(CPK_EALIGN, "paged: block_table not 4-byte aligned");
+    cpk_kv_cache view = {};
+    view.k = pc->k; view.v = pc->v; view.seqlens_k = pc->seqlens_k;
+    view.batch = pc->batch; view.kv_heads = pc->kv_heads; view.head_dim = pc->head_dim;
+    view.dtype = pc->dtype; view.capacity = pc->max_blocks * pc->block_size;
+    const Paging pg = {pc->block_table, pc->max_blocks, pc->block_size, pc->n_blocks};
+    return varlen_impl(q, k_new, v_new, &view, &pg, slots, cu_rows, past_lens, h_slots,
+                       h_cu_rows, h_past_lens, n_seqs, total_rows, q_heads, scale, out, ws,
+                       ws_bytes, phases, stream);
+}
+
+}  // extern "C"
+
+static int varlen_impl(const void *q, const void *k_new, const void *v_new,
+                       const cpk_kv_cache *cache, const Paging *pg, const int32_t *slots,
+                       const int32_t *cu_rows, const int32_t *past_lens,
+                       const int32_t *h_slots, const int32_t *h_cu_rows,
+                       const int32_t *h_past_lens, int n_seqs, int total_rows, int q_heads,
+                       float scale, void *out, void *ws, size_t ws_bytes, int phases,
+                       void *stream)
 {
     if (phases < 1 || (phases & ~CPK_PHASE_ALL))
         return fail(CPK_EINVAL, "varlen: phases=%d", phases);
@@ -383,10 +447,11 @@ int cpk_varlen_step_phases(const void *q, const void *k_new, const void *v_new,
     hipStream_t st = (hipStream_t)stream;
     const int rb = cache->head_dim * elem_size(cache->dtype);
     if (phases & CPK_PHASE_APPEND) {
-        r = hip_status(cpk::launch_kv_append_varlen(k_new, v_new, cache->k, cache->v,
-                                                    cache->seqlens_k, cache->kv_heads,
-                                                    cache->capacity, rb, cu_rows, past_lens,
-                                                    slots, n_seqs, total_rows, st),
+        r = hip_status(cpk::launch_kv_append_varlen(
+                           k_new, v_new, cache->k, cache->v, cache->seqlens_k, cache->kv_heads,
+                           cache->capacity, rb, cu_rows, past_lens, slots, n_seqs, total_rows,
+                           pg ? pg->table : nullptr, pg ? pg->max_blocks : 0,
+                           pg ? pg->block_size : 0, pg ? pg->n_blocks : 0, st),
                        "varlen append");
         if (r) return r;
     }
@@ -398,6 +463,10 @@ int cpk_varlen_step_phases(const void *q, const void *k_new, const void *v_new,
         d.scale_log2 = (float)((double)sc * 1.4426950408889634);
         d.max_segs = max_segs;
         d.cu_rows = cu_rows; d.past_lens = past_lens; d.slots = slots; d.n_seqs = n_seqs;
+        if (pg) {
+            d.block_table = pg->table; d.max_blocks = pg->max_blocks;
+            d.block_size = pg->block_size; d.n_blocks = pg->n_blocks;
+        }
         r = hip_status(cpk::launch_decode(d, cache->dtype, max_segs, st), "varlen decode");
         if (r) return r;
     }
@@ -408,6 +477,10 @@ int cpk_varlen_step_phases(const void *q, const void *k_new, const void *v_new,
         fill_scale(a, sc);
         a.varlen = 1; a.cu_rows = cu_rows; a.past_lens = past_lens; a.slots = slots;
         a.n_seqs = n_seqs; a.min_rows = dec_ok ? 2 : 1;
+        if (pg) {
+            a.block_table = pg->table; a.max_blocks = pg->max_blocks;
+            a.block_size = pg->block_size; a.n_blocks = pg->n_blocks;
+        }
         const bool wide = use_wide(cache->dtype, G, cache->kv_heads, max_rows);
         const int br = cpk::attn_rows_per_block(cache->dtype, G, wide);
         r = hip_status(
@@ -417,6 +490,8 @@ int cpk_varlen_step_phases(const void *q, const void *k_new, const void *v_new,
     }
     return ok();
 }
+
+extern "C" {
 
 int cpk_roll_append(const void *k_old, const void *v_old, const void *k_chunk,
                     const void *v_chunk, void *k_new, void *v_new, int B, int H, int C, int c,

@@ -73,7 +73,24 @@ struct AttnArgs {
     // rolling ring buffer (64-column kernel): logical key s of the rolling
     // view sits at physical row (ring_start + s) mod cap; 0 = no ring
     int ring_start;
+
+    // paged cache (varlen mode): with block_size > 0, k / v are pools
+    // [n_blocks][Hkv][block_size][D] and position p of the sequence in slot
+    // s lives in block block_table[s * max_blocks + p / block_size] (ids
+    // clamped into [0, n_blocks)); block_size is a multiple of 256
+    const int32_t *block_table;
+    int max_blocks, block_size, n_blocks;
 };
+
+// Row of position `pos` (head g) in a paged pool, as an element offset; the
+// block id is clamped into the pool so a bad table cannot address outside.
+__device__ __forceinline__ int64_t paged_row(const int32_t *table, int max_blocks, int bs,
+                                             int n_blocks, int Hkv, int slot, int g, int pos)
+{
+    int b = table[(int64_t)slot * max_blocks + pos / bs];
+    b = b < 0 ? 0 : (b >= n_blocks ? n_blocks - 1 : b);
+    return ((int64_t)b * Hkv + g) * bs + pos % bs;
+}
 
 // Split-KV decode: one query row per sequence.
 struct DecodeArgs {
@@ -90,6 +107,9 @@ struct DecodeArgs {
     const int32_t *past_lens;
     const int32_t *slots;
     int n_seqs;
+    // paged cache, as in AttnArgs (block_size 0: contiguous [batch][Hkv][cap][D])
+    const int32_t *block_table;
+    int max_blocks, block_size, n_blocks;
 };
 
 constexpr int kDecodeSeg = 256;   // keys per decode work item (4 waves x 64)
@@ -98,11 +118,13 @@ constexpr int kDecodeSeg = 256;   // keys per decode work item (4 waves x 64)
 hipError_t launch_kv_append(const void *k_new, const void *v_new, void *ck, void *cv,
                             int32_t *seqlens, int Hkv, int cap, int row_bytes, int slot,
                             int past, int rows, int src_rows, int len_after, hipStream_t st);
+// paged (block_size > 0): ck / cv are pools, as in AttnArgs
 hipError_t launch_kv_append_varlen(const void *k_new, const void *v_new, void *ck, void *cv,
                                    int32_t *seqlens, int Hkv, int cap, int row_bytes,
                                    const int32_t *cu_rows, const int32_t *past_lens,
                                    const int32_t *slots, int n_seqs, int total_rows,
-                                   hipStream_t st);
+                                   const int32_t *block_table, int max_blocks, int block_size,
+                                   int n_blocks, hipStream_t st);
 hipError_t launch_set_len(int32_t *seqlens, int b, int len, hipStream_t st);
 hipError_t launch_roll_append(const void *k_old, const void *v_old, const void *k_chunk,
                               const void *v_chunk, void *k_new, void *v_new, int B, int H,

@@ -340,8 +340,17 @@ void attn_mfma_kernel(AttnArgs a)
         int phys0 = key0 + a.ring_start;
         if (phys0 >= a.cap) phys0 -= a.cap;
         const bool nowrap = phys0 + kBK <= a.cap;
-        const char *kt_base = (const char *)(kc + (int64_t)phys0 * D);
-        const char *vt_base = (const char *)(vc + (int64_t)phys0 * D);
+        const char *kt_base, *vt_base;
+        if (a.block_size) {
+            // paged pool: the tile lies inside one block
+            const int64_t row = paged_row(a.block_table, a.max_blocks, a.block_size, a.n_blocks,
+                                          a.Hkv, sv.slot, g, key0);
+            kt_base = (const char *)((const uint16_t *)a.k + row * D);
+            vt_base = (const char *)((const uint16_t *)a.v + row * D);
+        } else {
+            kt_base = (const char *)(kc + (int64_t)phys0 * D);
+            vt_base = (const char *)(vc + (int64_t)phys0 * D);
+        }
         if (key0 + kBK <= sv.n_keys && key0 + kBK <= new_lo && nowrap) {
 #pragma unroll
             for (int i = 0; i < TL::LOADS; ++i) {
@@ -809,6 +818,12 @@ void attn_wide_kernel(AttnArgs a)
     auto issue = [&](const uint16_t *base, int kt, uint16_t *dst, bool is_v) {
         const int key0 = kt * kWBK;
         const char *tb = (const char *)(base + (int64_t)key0 * D);
+        if (a.block_size) {
+            // paged pool: the tile lies inside one block
+            const int64_t row = paged_row(a.block_table, a.max_blocks, a.block_size, a.n_blocks,
+                                          a.Hkv, sv.slot, g, key0);
+            tb = (const char *)((const uint16_t *)(is_v ? a.v : a.k) + row * D);
+        }
         const int clamp = sv.n_keys - 1 - key0;
         if (!fused || key0 + kWBK <= a.new_base) {
 #pragma unroll

@@ -46,7 +46,8 @@ __global__ void kv_append_varlen_kernel(const vec16 *__restrict__ kn, const vec1
                                         const int32_t *__restrict__ cu_rows,
                                         const int32_t *__restrict__ past_lens,
                                         const int32_t *__restrict__ slots, int n_seqs,
-                                        int total_rows)
+                                        int total_rows, const int32_t *__restrict__ table,
+                                        int max_blocks, int bs, int n_blocks)
 {
     const int64_t total = (int64_t)total_rows * Hkv * vpr;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -63,7 +64,10 @@ __global__ void kv_append_varlen_kernel(const vec16 *__restrict__ kn, const vec1
         }
         const int s = lo;
         const int r = t - cu_rows[s];
-        const int64_t dst = (((int64_t)slots[s] * Hkv + h) * cap + past_lens[s] + r) * vpr + c;
+        const int pos = past_lens[s] + r;
+        const int64_t row = bs ? paged_row(table, max_blocks, bs, n_blocks, Hkv, slots[s], h, pos)
+                               : ((int64_t)slots[s] * Hkv + h) * cap + pos;
+        const int64_t dst = row * vpr + c;
         const int64_t src = ((int64_t)t * Hkv + h) * vpr + c;
         ck[dst] = kn[src];
         cv[dst] = vn[src];
@@ -175,13 +179,15 @@ hipError_t launch_kv_append_varlen(const void *k_new, const void *v_new, void *c
                                    int32_t *seqlens, int Hkv, int cap, int row_bytes,
                                    const int32_t *cu_rows, const int32_t *past_lens,
                                    const int32_t *slots, int n_seqs, int total_rows,
-                                   hipStream_t st)
+                                   const int32_t *block_table, int max_blocks, int block_size,
+                                   int n_blocks, hipStream_t st)
 {
     const int vpr = row_bytes / 16;
     const int64_t items = (int64_t)total_rows * Hkv * vpr;
     hipLaunchKernelGGL(kv_append_varlen_kernel, dim3(grid_for(items)), dim3(256), 0, st,
                        (const vec16 *)k_new, (const vec16 *)v_new, (vec16 *)ck, (vec16 *)cv,
-                       seqlens, Hkv, cap, vpr, cu_rows, past_lens, slots, n_seqs, total_rows);
+                       seqlens, Hkv, cap, vpr, cu_rows, past_lens, slots, n_seqs, total_rows,
+                       block_table, max_blocks, block_size, n_blocks);
     return hipGetLastError();
 }
 

@@ -153,8 +153,14 @@ void decode_kernel(DecodeArgs a)
     const int gi = wave * GPW + gq;            // lane group inside the workgroup
     const int j = lane % LPK;                  // this lane's 8 elements: [8j, 8j + 8)
 
-    // uniform bases of this (slot, KV head); per-lane 32-bit byte offsets
-    const int64_t head_off = ((int64_t)slot * a.Hkv + g) * a.cap * D * 2;
+    // uniform bases (of this slot and KV head, or of the block holding this
+    // 256-key segment in a paged pool; key_org is the key at the base);
+    // per-lane 32-bit byte offsets
+    const int key_org = a.block_size ? sb : 0;
+    const int64_t head_off =
+        (a.block_size ? paged_row(a.block_table, a.max_blocks, a.block_size, a.n_blocks, a.Hkv,
+                                  slot, g, sb)
+                      : ((int64_t)slot * a.Hkv + g) * a.cap) * D * 2;
     const char *kbase = (const char *)a.k + head_off;
     const char *vbase = (const char *)a.v + head_off;
 
@@ -172,7 +178,7 @@ void decode_kernel(DecodeArgs a)
         const int key0 = wbase + st * STEP + kKK * gq;
 #pragma unroll
         for (int kk = 0; kk < kKK; ++kk) {
-            const uint32_t off = (uint32_t)min(key0 + kk, wlast) * (D * 2) + 16u * j;
+            const uint32_t off = (uint32_t)(min(key0 + kk, wlast) - key_org) * (D * 2) + 16u * j;
             b.k[kk] = load_stream(kbase, off);
             b.v[kk] = load_stream(vbase, off);
         }

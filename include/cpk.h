@@ -280,6 +280,56 @@ int cpk_roll_attention(const void *q, const void *k, const void *v,
                        void *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * A paged KV cache for the packed mixed step: K and V pools of fixed-size
+ * blocks, and per sequence slot a table of block ids (paged attention, one
+ * of the serving techniques the Ultralytics glossary "Chunked Prefill" lists
+ * beside chunked prefill: a prompt prefilled over several steps grows its
+ * cache block by block instead of reserving its whole length up front; and
+ * shared prefix blocks give the prompt-prefix reuse listed there too).
+ * Position p of slot s lives in block block_table[s * max_blocks +
+ * p / block_size] at row p % block_size.  Blocks may be shared between
+ * slots (a common prefix is then stored once); appends write only the
+ * blocks of the positions they append.
+ *   k, v        device pools [n_blocks][kv_heads][block_size][head_dim]
+ *   block_table device int32 [batch][max_blocks]; entries for the positions
+ *               a call touches must name blocks in [0, n_blocks) (the
+ *               kernels clamp out-of-range ids, so a bad table gives wrong
+ *               values, never an access outside the pools)
+ *   seqlens_k   device int32 [batch]
+ *   block_size  a positive multiple of 256 (a key tile or decode segment
+ *               never crosses a block)
+ * A slot's capacity is max_blocks * block_size.  bf16 and fp16 only.
+ */
+typedef struct cpk_paged_cache {
+    void *k;
+    void *v;
+    int32_t *block_table;
+    int32_t *seqlens_k;
+    int32_t batch;
+    int32_t kv_heads;
+    int32_t block_size;
+    int32_t n_blocks;
+    int32_t max_blocks;
+    int32_t head_dim;
+    int32_t dtype;
+} cpk_paged_cache;
+
+/*
+ * cpk_varlen_step_phases over a paged cache: same arguments, phases,
+ * workspace and results (bit for bit, given the same contents at the same
+ * positions) as over a contiguous cache.  CPK_EINVAL for a NULL table,
+ * block_size not a positive multiple of 256, or non-positive counts;
+ * CPK_EDTYPE for fp32.
+ */
+int cpk_paged_varlen_step(const void *q, const void *k_new, const void *v_new,
+                          const cpk_paged_cache *cache, const int32_t *slots,
+                          const int32_t *cu_rows, const int32_t *past_lens,
+                          const int32_t *h_slots, const int32_t *h_cu_rows,
+                          const int32_t *h_past_lens, int n_seqs, int total_rows, int q_heads,
+                          float scale, void *out, void *ws, size_t ws_bytes, int phases,
+                          void *stream);
+
+/*
  * Rolling cache as a ring buffer (the rolling cache of the Horizon developer
  * blog "Chunk Prefill", sections 3 and 4, without the O(C) shift per chunk).
  * A ring of C physical slots per (batch, head), [B][H][C][D], and a start

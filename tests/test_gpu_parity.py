@@ -626,6 +626,117 @@ def test_mixed_step_two_streams_bit_equal():
     say(f"  {steps} steps bit-identical")
 
 
+def _to_paged(cont: "cpk.KVCache", paged: "cpk.PagedKVCache", n_pos):
+    """Copy positions [0, n_pos[s]) of every slot of a contiguous cache into
+    the paged pools through the block table (test plumbing)."""
+    bs = paged.block_size
+    table = paged.block_table.cpu()
+    for s, n in enumerate(n_pos):
+        for i in range((n + bs - 1) // bs):
+            b = int(table[s, i])
+            paged.k[b] = cont.k[s, :, i * bs:(i + 1) * bs]
+            paged.v[b] = cont.v[s, :, i * bs:(i + 1) * bs]
+        paged.lens[s] = n
+    paged.seqlens_k.copy_(cont.seqlens_k)
+
+
+@pytest.mark.parametrize("kernel", ["narrow", "wide"])
+def test_paged_varlen_matches_contiguous(kernel):
+    """The packed mixed step over a paged cache (256-position blocks in a
+    shuffled order) equals the step over a contiguous cache bit for bit:
+    outputs of every step, and every cached position afterwards."""
+    say(f"case: paged vs contiguous mixed steps [{kernel}]: 5 decodes ctx 40..1500, prompt 900")
+    n_dec, Hq, Hkv, D, cap, prompt, budget, bs = 5, 16, 4, 128, 2048, 900, 300, 256
+    ctxs = si.mixed_contexts(n_dec, 40, 1500, seed=530)
+    B = n_dec + 1
+    cont = cpk.KVCache(B, Hkv, cap, D, torch.bfloat16)
+    si.fill_seeded(cont.k, 531)
+    si.fill_seeded(cont.v, 532)
+    cont.seqlens_k.copy_(torch.tensor(ctxs + [0], dtype=torch.int32))
+    cont.lens = ctxs + [0]
+    maxb = cap // bs
+    paged = cpk.PagedKVCache(B, Hkv, B * maxb + 3, bs, maxb, D, torch.bfloat16)
+    perm = torch.randperm(B * maxb + 3, generator=si.generator(533))[:B * maxb]
+    paged.block_table.copy_(perm.view(B, maxb).to(torch.int32))
+    _to_paged(cont, paged, ctxs + [0])
+    pq, pk, pv = (x.cuda() for x in si.gqa_prompt(L=prompt, Hq=Hq, Hkv=Hkv, D=D, seed=534))
+    g = si.generator(535)
+    done, lens, steps = 0, list(ctxs), 0
+    with cpk.attention_kernel(KERNELS[kernel]):
+        while done < prompt:
+            rows = cpk.cpk_plan_step(budget, n_dec, prompt - done)
+            dq = si.randn((n_dec, Hq, D), "bf16", g).cuda()
+            dk = si.randn((n_dec, Hkv, D), "bf16", g).cuda()
+            dv = si.randn((n_dec, Hkv, D), "bf16", g).cuda()
+            q = torch.cat([dq, pq[done:done + rows]])
+            kn = torch.cat([dk, pk[done:done + rows]])
+            vn = torch.cat([dv, pv[done:done + rows]])
+            slots = list(range(B))
+            cu = list(range(n_dec + 1)) + [n_dec + rows]
+            past = lens + [done]
+            o1 = cpk.cpk_varlen_step(q, kn, vn, cont, slots, cu, past)
+            o2 = cpk.cpk_paged_varlen_step(q, kn, vn, paged, slots, cu, past)
+            torch.cuda.synchronize()
+            assert bitwise(o1, o2), f"step {steps}: paged output differs"
+            lens = [x + 1 for x in lens]
+            done += rows
+            steps += 1
+    assert torch.equal(cont.seqlens_k, paged.seqlens_k)
+    for s, n in enumerate(lens + [prompt]):
+        pk_, pv_ = paged.gather(s, n)
+        assert bitwise(pk_, cont.k[s, :, :n]) and bitwise(pv_, cont.v[s, :, :n]), f"slot {s}"
+    say(f"  {steps} steps bit-identical, cache positions equal")
+
+
+@pytest.mark.parametrize("kernel", ["narrow", "wide"])
+def test_paged_shared_prefix(kernel):
+    """Two prompts with a common 512-token prefix stored once (both block
+    tables name the same two blocks) prefill their own suffixes in one packed
+    step; outputs equal the same step over a contiguous cache holding a copy
+    of the prefix in each slot, bit for bit, and the shared blocks are not
+    written."""
+    say(f"case: paged shared prefix [{kernel}]: prefix 512, suffixes 300 and 177")
+    Hq, Hkv, D, bs, P = 16, 4, 128, 256, 512
+    suf = [300, 177]
+    maxb = 4
+    paged = cpk.PagedKVCache(2, Hkv, 8, bs, maxb, D, torch.bfloat16)
+    paged.block_table.copy_(torch.tensor([[5, 2, 0, 7], [5, 2, 3, 6]], dtype=torch.int32))
+    cont = cpk.KVCache(2, Hkv, maxb * bs, D, torch.bfloat16)
+    pre_k = si.randn((Hkv, P, D), "bf16", si.generator(540)).cuda()
+    pre_v = si.randn((Hkv, P, D), "bf16", si.generator(541)).cuda()
+    for s in range(2):
+        cont.k[s, :, :P] = pre_k
+        cont.v[s, :, :P] = pre_v
+    cont.seqlens_k.fill_(P)
+    cont.lens = [P, P]
+    _to_paged(cont, paged, [P, P])
+    shared_k = paged.k[[5, 2]].clone()
+    qs = [si.randn((n, Hq, D), "bf16", si.generator(542 + i)).cuda() for i, n in enumerate(suf)]
+    ks = [si.randn((n, Hkv, D), "bf16", si.generator(544 + i)).cuda() for i, n in enumerate(suf)]
+    vs = [si.randn((n, Hkv, D), "bf16", si.generator(546 + i)).cuda() for i, n in enumerate(suf)]
+    q, kn, vn = torch.cat(qs), torch.cat(ks), torch.cat(vs)
+    cu = [0, suf[0], suf[0] + suf[1]]
+    with cpk.attention_kernel(KERNELS[kernel]):
+        o1 = cpk.cpk_varlen_step(q, kn, vn, cont, [0, 1], cu, [P, P])
+        o2 = cpk.cpk_paged_varlen_step(q, kn, vn, paged, [0, 1], cu, [P, P])
+        torch.cuda.synchronize()
+    assert bitwise(o1, o2), "shared-prefix output differs"
+    assert bitwise(paged.k[[5, 2]], shared_k), "shared prefix blocks were written"
+    for s in range(2):
+        n = P + suf[s]
+        pk_, pv_ = paged.gather(s, n)
+        assert bitwise(pk_, cont.k[s, :, :n]) and bitwise(pv_, cont.v[s, :, :n])
+    # against the oracle: each sequence's rows over prefix + suffix
+    for s in range(2):
+        kk = oracle.widen(si.storage(cont.k[s, :, :P + suf[s]]), oracle.BF16)
+        vv = oracle.widen(si.storage(cont.v[s, :, :P + suf[s]]), oracle.BF16)
+        qq = oracle.widen(si.storage(qs[s]), oracle.BF16)
+        rows = np.arange(P, P + suf[s], dtype=np.int32)
+        ref = oracle.attention(qq, kk, vv, np.zeros(len(rows), np.int32), rows,
+                               1.0 / math.sqrt(D))
+        check(o2[cu[s]:cu[s + 1]], ref, 2e-2, f"suffix {s} vs oracle")
+
+
 def test_workload5_mixed_full_size_budget_2048():
     say("case: workload 5: 64 decodes ctx U[512,16384], 20000-token prompt, budget 2048")
     steps = _run_mixed(64, 512, 16384, 20000, 2048, 32, 8, 128, seed=si.SEEDS["mixed"],
