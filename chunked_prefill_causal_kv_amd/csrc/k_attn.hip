@@ -237,6 +237,30 @@ __device__ __forceinline__ const char *kv_src(const uint16_t *cache_head, const 
     return (const char *)(cache_head + (int64_t)phys * D + chunk_elem);
 }
 
+// Block rows of a paged pool for consecutive key tiles of one workgroup:
+// the block id of the tile after the current one is read one tile ahead,
+// so the table lookup is off the path of the tile loads that need it.
+struct PagedTiles {
+    int t_next = -1;
+    int blk_next = 0;
+    __device__ __forceinline__ int lookup(const AttnArgs &a, int slot, int key) const
+    {
+        if (key >= a.max_blocks * a.block_size) return 0;   // past the table: unused
+        int b = a.block_table[(int64_t)slot * a.max_blocks + key / a.block_size];
+        return b < 0 ? 0 : (b >= a.n_blocks ? a.n_blocks - 1 : b);
+    }
+    // element offset of tile kt's first row (head g), and prefetch of kt + 1
+    __device__ __forceinline__ int64_t row(const AttnArgs &a, int slot, int g, int kt,
+                                           int tile_keys)
+    {
+        const int key0 = kt * tile_keys;
+        const int b = kt == t_next ? blk_next : lookup(a, slot, key0);
+        t_next = kt + 1;
+        blk_next = lookup(a, slot, key0 + tile_keys);
+        return ((int64_t)b * a.Hkv + g) * a.block_size + key0 % a.block_size;
+    }
+};
+
 template <typename TR, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_mfma_kernel(AttnArgs a)
@@ -332,6 +356,7 @@ void attn_mfma_kernel(AttnArgs a)
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
                                          (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
     };
+    PagedTiles ptiles;
     auto issue_tile = [&](int kt, uint16_t *Kb) {
         uint16_t *Vb = Kb + kBK * D;
         const int key0 = kt * kBK;
@@ -343,8 +368,7 @@ void attn_mfma_kernel(AttnArgs a)
         const char *kt_base, *vt_base;
         if (a.block_size) {
             // paged pool: the tile lies inside one block
-            const int64_t row = paged_row(a.block_table, a.max_blocks, a.block_size, a.n_blocks,
-                                          a.Hkv, sv.slot, g, key0);
+            const int64_t row = ptiles.row(a, sv.slot, g, kt, kBK);
             kt_base = (const char *)((const uint16_t *)a.k + row * D);
             vt_base = (const char *)((const uint16_t *)a.v + row * D);
         } else {
@@ -815,14 +839,14 @@ void attn_wide_kernel(AttnArgs a)
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
                                          (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
     };
+    PagedTiles ptiles;
+    int64_t prow = 0;   // paged: first row of the tile being issued (set by refill)
     auto issue = [&](const uint16_t *base, int kt, uint16_t *dst, bool is_v) {
         const int key0 = kt * kWBK;
         const char *tb = (const char *)(base + (int64_t)key0 * D);
         if (a.block_size) {
             // paged pool: the tile lies inside one block
-            const int64_t row = paged_row(a.block_table, a.max_blocks, a.block_size, a.n_blocks,
-                                          a.Hkv, sv.slot, g, key0);
-            tb = (const char *)((const uint16_t *)(is_v ? a.v : a.k) + row * D);
+            tb = (const char *)((const uint16_t *)(is_v ? a.v : a.k) + prow * D);
         }
         const int clamp = sv.n_keys - 1 - key0;
         if (!fused || key0 + kWBK <= a.new_base) {
@@ -1024,6 +1048,7 @@ void attn_wide_kernel(AttnArgs a)
     };
     auto refill = [&](int t, uint16_t *slot) {
         if (t <= t_last) {
+            if (a.block_size) prow = ptiles.row(a, sv.slot, g, t, kWBK);
             issue(kc, t, slot, false);
             issue(vc, t, slot + TILE, true);
         }
