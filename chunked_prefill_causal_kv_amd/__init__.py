@@ -64,6 +64,7 @@ def _load() -> ctypes.CDLL:
     sig = {
         "cpk_version": ([], I),
         "cpk_set_attention_kernel": ([I], I),
+        "cpk_kv_copy_prefix": ([CP, I, I, I, P], I),
         "cpk_last_error": ([], ctypes.c_char_p),
         "cpk_device_info": ([ctypes.c_char_p, I, IP], I),
         "cpk_ladder_rungs": ([I, IP, IP], I),
@@ -279,6 +280,14 @@ def cpk_chunk_attention(q: torch.Tensor, cache: KVCache, b: int, past_len: int,
     _check(_lib.cpk_chunk_attention(_ptr(q), ctypes.byref(cache.desc), b, Hq, past_len, rows,
                                     real, float(scale), _ptr(out), _stream(stream)))
     return out
+
+
+def cpk_kv_copy_prefix(cache: KVCache, src_slot: int, dst_slot: int, length: int,
+                       stream=None):
+    """Positions [0, length) of src_slot copied to dst_slot; seqlens_k[dst] = length."""
+    _check(_lib.cpk_kv_copy_prefix(ctypes.byref(cache.desc), src_slot, dst_slot, length,
+                                   _stream(stream)))
+    cache.lens[dst_slot] = length
 
 
 def cpk_rewind(cache: KVCache, b: int, new_len: int, stream=None):
@@ -546,3 +555,23 @@ def ring_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream
         cpk_ring_attention(q[sl], kr[0], vr[0], (j + 1) * c, n_left, start, mask=m, scale=scale,
                            out=out[sl], stream=stream, split=split)
     return out, n_left, kr[0], vr[0], start
+
+
+def prefill_with_prefix(cache: KVCache, b: int, src_slot: int, prefix_len: int, q, k, v,
+                        W: int, pad: bool = True, scale: float = 0.0, out=None, stream=None):
+    """Prompt-prefix reuse: the first prefix_len positions of slot b are
+    copied from src_slot (which holds them from an earlier prompt), then only
+    the rest of the prompt (q/k/v: its rows past the prefix, token-major) is
+    prefilled in W-row chunks starting at past_len = prefix_len.  Returns
+    (out for those rows, widths)."""
+    L, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    cpk_kv_copy_prefix(cache, src_slot, b, prefix_len, stream)
+    widths = []
+    for past, rows in cpk_split_chunks(L, W):
+        sl = slice(past, past + rows)
+        _, w = cpk_prefill_chunk(q[sl], k[sl], v[sl], cache, b, prefix_len + past, W, pad,
+                                 scale, out=out[sl], stream=stream)
+        widths.append(w)
+    return out, widths

@@ -254,6 +254,25 @@ int cpk_chunk_attention(const void *q, const cpk_kv_cache *cache, int b, int q_h
                             (hipStream_t)stream);
 }
 
+int cpk_kv_copy_prefix(const cpk_kv_cache *cache, int src_slot, int dst_slot, int len,
+                       void *stream)
+{
+    int r = check_cache(cache);
+    if (r) return r;
+    if (src_slot < 0 || src_slot >= cache->batch || dst_slot < 0 || dst_slot >= cache->batch ||
+        src_slot == dst_slot)
+        return fail(CPK_EINVAL, "copy_prefix: slots %d -> %d (batch %d)", src_slot, dst_slot,
+                    cache->batch);
+    if (len < 0 || len > cache->capacity)
+        return fail(CPK_EINVAL, "copy_prefix: len=%d outside [0, capacity %d]", len,
+                    cache->capacity);
+    return hip_status(cpk::launch_kv_copy_prefix(cache->k, cache->v, cache->seqlens_k,
+                                                 cache->kv_heads, cache->capacity,
+                                                 cache->head_dim * elem_size(cache->dtype),
+                                                 src_slot, dst_slot, len, (hipStream_t)stream),
+                      "copy_prefix launch");
+}
+
 int cpk_rewind(const cpk_kv_cache *cache, int b, int new_len, int cur_len, void *stream)
 {
     int r = check_cache(cache);

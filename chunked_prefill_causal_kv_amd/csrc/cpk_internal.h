@@ -126,6 +126,10 @@ hipError_t launch_kv_append_varlen(const void *k_new, const void *v_new, void *c
                                    const int32_t *block_table, int max_blocks, int block_size,
                                    int n_blocks, hipStream_t st);
 hipError_t launch_set_len(int32_t *seqlens, int b, int len, hipStream_t st);
+// rows [0, len) of slot src copied to slot dst (every KV head); seqlens[dst] = len
+hipError_t launch_kv_copy_prefix(const void *k, const void *v, int32_t *seqlens, int Hkv,
+                                 int cap, int row_bytes, int src, int dst, int len,
+                                 hipStream_t st);
 hipError_t launch_roll_append(const void *k_old, const void *v_old, const void *k_chunk,
                               const void *v_chunk, void *k_new, void *v_new, int B, int H,
                               int C, int c, int row_bytes, hipStream_t st);

@@ -161,7 +161,40 @@ __global__ void ring_view_kernel(const vec16 *__restrict__ kr, const vec16 *__re
     }
 }
 
+// Prefix copy between two slots of one cache: rows [0, len) of every KV head.
+__global__ void kv_copy_prefix_kernel(const vec16 *__restrict__ ck, const vec16 *__restrict__ cv,
+                                      vec16 *__restrict__ dk, vec16 *__restrict__ dv,
+                                      int32_t *seqlens, int Hkv, int cap, int vpr, int src,
+                                      int dst, int len)
+{
+    const int64_t total = (int64_t)Hkv * len * vpr;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int e = (int)(i % vpr);
+        const int64_t r1 = i / vpr;
+        const int pos = (int)(r1 % len);
+        const int h = (int)(r1 / len);
+        const int64_t so = (((int64_t)src * Hkv + h) * cap + pos) * vpr + e;
+        const int64_t d = (((int64_t)dst * Hkv + h) * cap + pos) * vpr + e;
+        dk[d] = ck[so];
+        dv[d] = cv[so];
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) seqlens[dst] = len;
+}
+
 }  // namespace
+
+hipError_t launch_kv_copy_prefix(const void *k, const void *v, int32_t *seqlens, int Hkv,
+                                 int cap, int row_bytes, int src, int dst, int len,
+                                 hipStream_t st)
+{
+    const int vpr = row_bytes / 16;
+    const int64_t items = (int64_t)Hkv * len * vpr;
+    hipLaunchKernelGGL(kv_copy_prefix_kernel, dim3(grid_for(items > 0 ? items : 1)), dim3(256),
+                       0, st, (const vec16 *)k, (const vec16 *)v, (vec16 *)k, (vec16 *)v,
+                       seqlens, Hkv, cap, vpr, src, dst, len);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const void *k_new, const void *v_new, void *ck, void *cv,
                             int32_t *seqlens, int Hkv, int cap, int row_bytes, int slot,

@@ -164,6 +164,19 @@ int cpk_rewind(const cpk_kv_cache *cache, int b, int new_len, int cur_len,
                void *stream);
 
 /*
+ * Prompt-prefix reuse (the prompt caching the Ultralytics glossary "Chunked
+ * Prefill" lists among related serving techniques): copy positions
+ * [0, len) of every KV head from slot src_slot to slot dst_slot of the same
+ * cache and set seqlens_k[dst_slot] = len; a chunked prefill of the rest of
+ * the prompt then starts at past_len = len and never recomputes the prefix.
+ * (A paged cache shares prefix blocks between block tables instead.)
+ * CPK_EINVAL if a slot is out of range, src == dst, or len is outside
+ * [0, capacity].
+ */
+int cpk_kv_copy_prefix(const cpk_kv_cache *cache, int src_slot, int dst_slot, int len,
+                       void *stream);
+
+/*
  * One padded prefill forward in a single call (ONNX GenAI Wiki "Chunked
  * Prefill", section 4): round real_rows up the ladder of W (pad != 0) or
  * not (pad == 0, the page's switch that turns padding off); widen q, k and

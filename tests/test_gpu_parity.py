@@ -226,6 +226,39 @@ def test_fused_append_matches_two_launches(kernel, dtype, Hq, Hkv, D, past, real
     check(outs[0], ref, TOL[dtype], "fused vs oracle")
 
 
+@pytest.mark.parametrize("kernel", ["narrow", "wide"])
+def test_prefix_reuse(kernel):
+    """Prompt-prefix reuse: prompt A = prefix + suffix A is prefilled in slot
+    0; prompt B = the same prefix + suffix B reuses A's prefix (copied to
+    slot 1) and prefills only its suffix.  B's suffix rows and slot 1's
+    cache equal a full chunked prefill of B in slot 2 bit for bit, and the
+    oracle within tolerance."""
+    say(f"case: prefix reuse [{kernel}]: prefix 700, suffixes 400 / 333, W=256")
+    Hq, Hkv, D, W, P = 16, 4, 128, 256, 700
+    pre = si.gqa_prompt(L=P, Hq=Hq, Hkv=Hkv, D=D, seed=560)
+    sa = si.gqa_prompt(L=400, Hq=Hq, Hkv=Hkv, D=D, seed=561)
+    sb = si.gqa_prompt(L=333, Hq=Hq, Hkv=Hkv, D=D, seed=562)
+    A = [torch.cat([x, y]).cuda() for x, y in zip(pre, sa)]
+    Bt = [torch.cat([x, y]) for x, y in zip(pre, sb)]
+    B = [x.cuda() for x in Bt]
+    cache = cpk.KVCache(3, Hkv, 2048, D, torch.bfloat16)
+    poison(cache)
+    with cpk.attention_kernel(KERNELS[kernel]):
+        cpk.prefill_chunked(cache, 0, *A, W)
+        out_r, _ = cpk.prefill_with_prefix(cache, 1, 0, P, B[0][P:], B[1][P:], B[2][P:], W)
+        out_f, _ = cpk.prefill_chunked(cache, 2, *B, W)
+        torch.cuda.synchronize()
+    n = P + 333
+    assert int(cache.seqlens_k[1]) == n == int(cache.seqlens_k[2])
+    assert bitwise(out_r, out_f[P:]), "reused-prefix suffix differs from the full prefill"
+    assert bitwise(cache.k[1, :, :n], cache.k[2, :, :n])
+    assert bitwise(cache.v[1, :, :n], cache.v[2, :, :n])
+    qs, ks, vs = (si.storage(x) for x in Bt)
+    rows = np.arange(P, n)
+    ref = oracle_rows(qs, ks, vs, rows, oracle.BF16)
+    check(out_r, ref, 2e-2, "suffix vs oracle")
+
+
 # ---------------------------------------------- workload 2: GQA bf16 W=512
 
 def test_workload2_gqa_bf16_full_size():

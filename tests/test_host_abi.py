@@ -267,3 +267,12 @@ def test_paged_validation():
     assert f(*args(desc(nb=0))) == cpk.CPK_EINVAL
     assert f(*args(desc(table=None))) == cpk.CPK_EINVAL
     assert f(*args(desc(dt=cpk.CPK_F32))) == cpk.CPK_EDTYPE
+
+
+def test_copy_prefix_validation():
+    c = cpk.cpk_kv_cache(FAKE, FAKE * 2, FAKE * 3, 2, 4, 1024, 128, cpk.CPK_BF16)
+    f = cpk._lib.cpk_kv_copy_prefix
+    assert f(ctypes.byref(c), 0, 0, 10, None) == cpk.CPK_EINVAL      # same slot
+    assert f(ctypes.byref(c), 0, 2, 10, None) == cpk.CPK_EINVAL      # slot out of range
+    assert f(ctypes.byref(c), 0, 1, 1025, None) == cpk.CPK_EINVAL    # past capacity
+    assert f(ctypes.byref(c), 0, 1, -1, None) == cpk.CPK_EINVAL
