@@ -87,6 +87,11 @@ def read_traffic(sha, path=TRAFFIC_FILE):
         return None
 
 
+# spin length (GPU clock cycles) that covers the host-side enqueue of one
+# eight-chunk step
+HOST_LEAD_CYCLES = 2_000_000
+
+
 def bench_chunked(cpk, si, torch, steps, warmup):
     L, Hq, Hkv, D, W, CAP = 4000, 32, 8, 128, 512, 8192
     q, k, v = (x.cuda() for x in si.gqa_prompt(L=L, Hq=Hq, Hkv=Hkv, D=D))
@@ -112,14 +117,21 @@ def bench_chunked(cpk, si, torch, steps, warmup):
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in chunks] for _ in range(steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        step(evs[s])
+        step(None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # Per-launch durations: a spin kernel ahead of each step keeps the GPU
+    # busy while the host enqueues the step's launches, so the GPU meets each
+    # event pair with the kernel already queued between them and the events
+    # bracket the kernel rather than the host's launch gaps.
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in chunks] for _ in range(steps)]
+    for s in range(steps):
+        torch.cuda._sleep(HOST_LEAD_CYCLES)
+        step(evs[s])
+        torch.cuda.synchronize()
     per_chunk_ms = [[evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)]
                     for i in range(len(chunks))]
     ms_step = (t1 - t0) * 1e3 / steps
@@ -544,6 +556,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary", default="all",
+                    help="comma list of secondary groups to run: steady, decode, ladder, "
+                         "rolling, mixed (default all)")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain copy of known size (for counter scaling)")
     args = ap.parse_args()
@@ -567,14 +582,21 @@ def main():
     ms_graph = bench_step_graph(cpk, si, torch, args.steps, args.warmup, r["q"], r["k"], r["v"])
     log(f"bench: graph-replayed step {ms_graph:.3f} ms")
     secondary = {}
+    groups = {"steady", "decode", "ladder", "rolling", "mixed"}
+    if args.secondary != "all":
+        groups = set(args.secondary.split(","))
     if not args.no_secondary:
+        secondary["per_chunk"] = r["table"]
+    if not args.no_secondary and "steady" in groups:
         secondary["steady_chunk"] = bench_steady_chunk(cpk, si, torch)
         log(f"bench: steady chunk {secondary['steady_chunk']}")
+    if not args.no_secondary and "decode" in groups:
         secondary["decode_rows"] = bench_decode(cpk, si, torch)
         log(f"bench: decode {secondary['decode_rows']}")
-        secondary["per_chunk"] = r["table"]
+    if not args.no_secondary and "ladder" in groups:
         secondary["ladder"] = bench_ladder(cpk, si, torch)
         log(f"bench: ladder {secondary['ladder']}")
+    if not args.no_secondary and "rolling" in groups:
         secondary["rolling_fp16"] = bench_rolling(cpk, si, torch)
         log(f"bench: rolling {secondary['rolling_fp16']}")
         secondary["rolling_fp16_computed_mask"] = bench_rolling(cpk, si, torch, False)
@@ -584,6 +606,7 @@ def main():
         secondary["rolling_fp16_ring_computed_mask"] = bench_rolling(cpk, si, torch, False,
                                                                      ring=True)
         log(f"bench: rolling {secondary['rolling_fp16_ring_computed_mask']}")
+    if not args.no_secondary and "mixed" in groups:
         for budget, overlap, paged in ((2048, False, False), (2048, True, False),
                                        (2048, False, True), (8192, False, False),
                                        (8192, True, False)):

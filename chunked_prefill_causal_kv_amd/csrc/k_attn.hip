@@ -261,7 +261,7 @@ struct PagedTiles {
     }
 };
 
-template <typename TR, int D>
+template <typename TR, int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_mfma_kernel(AttnArgs a)
 {
@@ -366,7 +366,7 @@ void attn_mfma_kernel(AttnArgs a)
         if (phys0 >= a.cap) phys0 -= a.cap;
         const bool nowrap = phys0 + kBK <= a.cap;
         const char *kt_base, *vt_base;
-        if (a.block_size) {
+        if constexpr (PAGED) {
             // paged pool: the tile lies inside one block
             const int64_t row = ptiles.row(a, sv.slot, g, kt, kBK);
             kt_base = (const char *)((const uint16_t *)a.k + row * D);
@@ -741,7 +741,7 @@ __device__ __forceinline__ uint4 here(uint4 x)
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
-template <typename TR, int D>
+template <typename TR, int D, bool PAGED>
 __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_wide_kernel(AttnArgs a)
 {
@@ -844,7 +844,7 @@ void attn_wide_kernel(AttnArgs a)
     auto issue = [&](const uint16_t *base, int kt, uint16_t *dst, bool is_v) {
         const int key0 = kt * kWBK;
         const char *tb = (const char *)(base + (int64_t)key0 * D);
-        if (a.block_size) {
+        if constexpr (PAGED) {
             // paged pool: the tile lies inside one block
             tb = (const char *)((const uint16_t *)(is_v ? a.v : a.k) + prow * D);
         }
@@ -1048,7 +1048,7 @@ void attn_wide_kernel(AttnArgs a)
     };
     auto refill = [&](int t, uint16_t *slot) {
         if (t <= t_last) {
-            if (a.block_size) prow = ptiles.row(a, sv.slot, g, t, kWBK);
+            if constexpr (PAGED) prow = ptiles.row(a, sv.slot, g, t, kWBK);
             issue(kc, t, slot, false);
             issue(vc, t, slot + TILE, true);
         }
@@ -1345,37 +1345,43 @@ int attn_rows_per_block(int dtype, int group, bool wide)
     return (wide ? kWQC : kQC) / group;
 }
 
+// Launch one instance of a bf16/fp16 kernel template for the dtype, head
+// dim and paging of the call.
+#define CPK_LAUNCH_MFMA(KERNEL, THREADS)                                                      \
+    do {                                                                                    \
+        const bool pg = a.block_size != 0;                                                 \
+        if (dtype == 1) {                                                                  \
+            if (a.D == 64) {                                                               \
+                if (pg) hipLaunchKernelGGL((KERNEL<F16, 64, true>), grid, dim3(THREADS), 0, st, a);   \
+                else hipLaunchKernelGGL((KERNEL<F16, 64, false>), grid, dim3(THREADS), 0, st, a);   \
+            } else {                                                                       \
+                if (pg) hipLaunchKernelGGL((KERNEL<F16, 128, true>), grid, dim3(THREADS), 0, st, a);  \
+                else hipLaunchKernelGGL((KERNEL<F16, 128, false>), grid, dim3(THREADS), 0, st, a);  \
+            }                                                                              \
+        } else {                                                                           \
+            if (a.D == 64) {                                                               \
+                if (pg) hipLaunchKernelGGL((KERNEL<Bf16, 64, true>), grid, dim3(THREADS), 0, st, a);  \
+                else hipLaunchKernelGGL((KERNEL<Bf16, 64, false>), grid, dim3(THREADS), 0, st, a);  \
+            } else {                                                                       \
+                if (pg) hipLaunchKernelGGL((KERNEL<Bf16, 128, true>), grid, dim3(THREADS), 0, st, a); \
+                else hipLaunchKernelGGL((KERNEL<Bf16, 128, false>), grid, dim3(THREADS), 0, st, a); \
+            }                                                                              \
+        }                                                                                  \
+    } while (0)
+
 hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
                             bool wide, hipStream_t st)
 {
     const dim3 grid(row_blocks * a.Hkv, a.n_parts > 1 ? a.n_parts : 1, n_seq_grid);
     if (wide && dtype != 0) {
-        if (dtype == 1) {
-            if (a.D == 64)
-                hipLaunchKernelGGL((attn_wide_kernel<F16, 64>), grid, dim3(kWThreads), 0, st, a);
-            else
-                hipLaunchKernelGGL((attn_wide_kernel<F16, 128>), grid, dim3(kWThreads), 0, st, a);
-        } else {
-            if (a.D == 64)
-                hipLaunchKernelGGL((attn_wide_kernel<Bf16, 64>), grid, dim3(kWThreads), 0, st, a);
-            else
-                hipLaunchKernelGGL((attn_wide_kernel<Bf16, 128>), grid, dim3(kWThreads), 0, st, a);
-        }
+        CPK_LAUNCH_MFMA(attn_wide_kernel, kWThreads);
     } else if (dtype == 0) {
         if (a.D == 64)
             hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, st, a);
         else
             hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, st, a);
-    } else if (dtype == 1) {
-        if (a.D == 64)
-            hipLaunchKernelGGL((attn_mfma_kernel<F16, 64>), grid, dim3(kThreads), 0, st, a);
-        else
-            hipLaunchKernelGGL((attn_mfma_kernel<F16, 128>), grid, dim3(kThreads), 0, st, a);
     } else {
-        if (a.D == 64)
-            hipLaunchKernelGGL((attn_mfma_kernel<Bf16, 64>), grid, dim3(kThreads), 0, st, a);
-        else
-            hipLaunchKernelGGL((attn_mfma_kernel<Bf16, 128>), grid, dim3(kThreads), 0, st, a);
+        CPK_LAUNCH_MFMA(attn_mfma_kernel, kThreads);
     }
     return hipGetLastError();
 }
