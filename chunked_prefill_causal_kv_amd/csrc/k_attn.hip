@@ -62,6 +62,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 struct Bf16 {
     typedef bf16x8_t vec8;
@@ -175,50 +176,45 @@ __device__ __forceinline__ bool resolve_seq(const AttnArgs &a, int z, SeqView &s
 }
 
 // Fused append: the cache rows of one row block and KV head, copied from
-// the new rows in 16-byte pieces.  load() issues the reads (held in
-// registers), store() the writes; callers issue the writes before any tile
-// load, so the kernels' counted waits on tile loads stay exact (loads
-// complete in order; older outstanding stores only make a wait stricter).
+// the new rows in 16-byte pieces, all reads issued before the writes.
+// Callers issue the writes before any tile load, so the kernels' counted
+// waits on tile loads stay exact (loads complete in order; older
+// outstanding stores only make a wait stricter).  The pieces live in
+// registers: the array is local to this one fully unrolled function.
 template <int D, int THREADS, int MAXROWS>
-struct FusedAppend {
-    static constexpr int NCH = D / 8;
-    static constexpr int PER = (MAXROWS * NCH * 2 + THREADS - 1) / THREADS;
-    uint4 val[PER];
-    __device__ __forceinline__ void load(const AttnArgs &a, int g, int r0, int n_rows, int tid)
-    {
-        const int n = n_rows * NCH;
+__device__ __forceinline__ void fused_append(const AttnArgs &a, int g, int r0, int n_rows, int tid)
+{
+    constexpr int NCH = D / 8;
+    constexpr int PER = (MAXROWS * NCH * 2 + THREADS - 1) / THREADS;
+    const int n = n_rows * NCH;
+    u32x4_t val[PER];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int c = tid + j * THREADS;
-            if (c < 2 * n) {
-                const bool isv = c >= n;
-                const int cc = isv ? c - n : c;
-                const int src = min(r0 + cc / NCH, a.new_rows - 1);
-                const uint16_t *sp = (const uint16_t *)(isv ? a.v_new : a.k_new) +
-                                     ((int64_t)src * a.Hkv + g) * D + (cc % NCH) * 8;
-                val[j] = *(const uint4 *)sp;
-            }
+    for (int j = 0; j < PER; ++j) {
+        const int c = tid + j * THREADS;
+        if (c < 2 * n) {
+            const bool isv = c >= n;
+            const int cc = isv ? c - n : c;
+            const int src = min(r0 + cc / NCH, a.new_rows - 1);
+            const uint16_t *sp = (const uint16_t *)(isv ? a.v_new : a.k_new) +
+                                 ((int64_t)src * a.Hkv + g) * D + (cc % NCH) * 8;
+            val[j] = *(const u32x4_t *)sp;
         }
     }
-    __device__ __forceinline__ void store(const AttnArgs &a, int g, int r0, int n_rows, int tid)
-    {
-        const int n = n_rows * NCH;
-        uint16_t *ck = (uint16_t *)a.k + ((int64_t)a.slot * a.Hkv + g) * a.cap * D;
-        uint16_t *cv = (uint16_t *)a.v + ((int64_t)a.slot * a.Hkv + g) * a.cap * D;
+    uint16_t *ck = (uint16_t *)a.k + ((int64_t)a.slot * a.Hkv + g) * a.cap * D;
+    uint16_t *cv = (uint16_t *)a.v + ((int64_t)a.slot * a.Hkv + g) * a.cap * D;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int c = tid + j * THREADS;
-            if (c < 2 * n) {
-                const bool isv = c >= n;
-                const int cc = isv ? c - n : c;
-                uint16_t *dp = (isv ? cv : ck) + (int64_t)(a.new_base + r0 + cc / NCH) * D +
-                               (cc % NCH) * 8;
-                *(uint4 *)dp = val[j];
-            }
+    for (int j = 0; j < PER; ++j) {
+        const int c = tid + j * THREADS;
+        if (c < 2 * n) {
+            const bool isv = c >= n;
+            const int cc = isv ? c - n : c;
+            uint16_t *dp = (isv ? cv : ck) + (int64_t)(a.new_base + r0 + cc / NCH) * D +
+                           (cc % NCH) * 8;
+            *(u32x4_t *)dp = val[j];
         }
-        if (blockIdx.x == 0 && tid == 0) a.seqlens[a.slot] = a.len_after;
     }
-};
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) a.seqlens[a.slot] = a.len_after;
+}
 
 // Source of one 16-byte piece of a K or V tile: the cache row of logical
 // key `key` of this KV head (physical row (ring_start + key) mod cap), or
@@ -302,10 +298,7 @@ void attn_mfma_kernel(AttnArgs a)
     // keys at or past new_lo come from the new rows (never from the cache)
     const int new_lo = fused ? a.new_base : INT_MAX;
     if (fused) {
-        FusedAppend<D, kThreads, kQC> ap;
-        const int n_rows = min(r0 + BR, sv.rows) - r0;
-        ap.load(a, g, r0, n_rows, tid);
-        ap.store(a, g, r0, n_rows, tid);
+        fused_append<D, kThreads, kQC>(a, g, r0, min(r0 + BR, sv.rows) - r0, tid);
     }
 
     // ---- query fragment (B operand of S^T = K Q^T): column qc
@@ -722,7 +715,6 @@ __device__ __forceinline__ float half_sum(float x)
 // Keep a value in accumulation registers: the matrix instructions read
 // their A/B operands from them directly, which leaves the vector registers
 // to the softmax.  (An empty asm with an "a" constraint; no instruction.)
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 in_agprs(uint4 x)
 {
     u32x4_t t = {x.x, x.y, x.z, x.w};
@@ -796,10 +788,7 @@ void attn_wide_kernel(AttnArgs a)
     const uint16_t *vc = (const uint16_t *)a.v + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
     const bool fused = a.k_new != nullptr;
     if (fused) {
-        FusedAppend<D, kWThreads, kWQC> ap;
-        const int n_rows = min(r0 + BR, sv.rows) - r0;
-        ap.load(a, g, r0, n_rows, tid);
-        ap.store(a, g, r0, n_rows, tid);
+        fused_append<D, kWThreads, kWQC>(a, g, r0, min(r0 + BR, sv.rows) - r0, tid);
     }
 
     // ---- query fragments (B operand of S^T = K Q^T) of the two column blocks
