@@ -318,8 +318,9 @@ def bench_ladder(cpk, si, torch, reps=2):
 def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=5):
     """Rolling right-aligned cache: 4096 fp16 tokens, 16 heads, C = 2048,
     c = 256; per chunk roll_append (out of place, double-buffered: C rows
-    moved) then roll_attention, or with ring=True ring_append (c rows moved)
-    then ring_attention; with the explicit (c, C) additive mask (0 visible,
+    moved) then roll_attention, or with ring=True one cpk_ring_step (the c
+    new rows written into the ring by the attention launch); with the
+    explicit (c, C) additive mask (0 visible,
     -32768 masked) or visibility computed in the kernel.  Median of reps
     timed passes over the 16 chunks."""
     L, H, D, C, c = 4096, 16, 128, 2048, 256
@@ -343,10 +344,9 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=5):
             sl = slice(j * c, (j + 1) * c)
             m = masks[j] if explicit_mask else None
             if ring:
-                start = cpk.cpk_ring_append(k[sl].unsqueeze(0), v[sl].unsqueeze(0), bufs[0],
-                                            bufs[1], start)
-                cpk.cpk_ring_attention(q[sl], bufs[0][0], bufs[1][0], (j + 1) * c, 0, start,
-                                       mask=m, out=out[sl])
+                # the append runs inside the attention launch
+                _, start = cpk.cpk_ring_step(q[sl], k[sl], v[sl], bufs[0][0], bufs[1][0],
+                                             (j + 1) * c, 0, start, mask=m, out=out[sl])
                 continue
             ko, vo = bufs[2 * cur], bufs[2 * cur + 1]
             kn, vn = bufs[2 * (1 - cur)], bufs[2 * (1 - cur) + 1]
@@ -383,7 +383,7 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=5):
     ms = statistics.median(times)
     f = 4 * D * H * pairs
     how = "the explicit (c, C) mask" if explicit_mask else "visibility computed in the kernel"
-    what = "ring_append + ring_attention" if ring else "roll_append + roll_attention"
+    what = "ring_step (append fused into the attention)" if ring else "roll_append + roll_attention"
     return {"chunks": n, "gflop": round(f / 1e9, 2), "ms": round(ms, 4), "ms_min": round(min(times), 4),
             "tflops": round(f / (ms * 1e-3) / 1e12, 1), "dtype": "fp16",
             "note": f"{what} with {how}, per chunk; 16 chunks replayed as a HIP graph, "

@@ -84,6 +84,7 @@ def _load() -> ctypes.CDLL:
         "cpk_roll_workspace_size": ([I, I, I, I, I, I], Z),
         "cpk_ring_append": ([P, P, P, P, I, I, I, I, I, I, I, P], I),
         "cpk_ring_attention": ([P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, Z, P], I),
+        "cpk_ring_step": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, Z, P], I),
         "cpk_ring_view": ([P, P, P, P, I, I, I, I, I, I, P], I),
     }
     for name, (args, res) in sig.items():
@@ -473,6 +474,27 @@ def cpk_ring_attention(q, k_ring, v_ring, abs_end: int, n_leftpad: int, start: i
     return out
 
 
+def cpk_ring_step(q, k_chunk, v_chunk, k_ring, v_ring, abs_end: int, n_leftpad: int,
+                  start: int, mask=None, scale: float = 0.0, out=None, stream=None,
+                  split: bool = True):
+    """cpk_ring_append then cpk_ring_attention at the advanced start, in one
+    launch (bf16/fp16): chunk rows [c, Hkv, D], rings [Hkv, C, D].  Returns
+    (out, new start)."""
+    c, Hq, D = q.shape
+    Hkv, C, _ = k_ring.shape
+    if out is None:
+        out = torch.empty_like(q)
+    ws = None
+    if split:
+        ws = _roll_workspace(cpk_roll_workspace_size(Hq, Hkv, C, c, D, q.dtype), q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * 4
+    _check(_lib.cpk_ring_step(_ptr(q), _ptr(k_chunk), _ptr(v_chunk), _ptr(k_ring), _ptr(v_ring),
+                              _ptr(mask), abs_end, n_leftpad, Hq, Hkv, C, c, D,
+                              DTYPE_CODE[q.dtype], float(scale), start, _ptr(out), _ptr(ws),
+                              ws_bytes, _stream(stream)))
+    return out, (start + c) % C
+
+
 def cpk_ring_view(k_ring, v_ring, start: int, k_out=None, v_out=None, stream=None):
     """The logical (literal-shift) view of rings [B, H, C, D]."""
     B, H, C, D = k_ring.shape
@@ -532,10 +554,12 @@ def roll_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream
 
 
 def ring_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream=None,
-                 split: bool = True):
-    """roll_prefill over a ring buffer: per chunk, cpk_ring_append (c rows
-    moved) and cpk_ring_attention.  Same outputs, bit for bit.  Returns
-    (out over the padded sequence, n_leftpad, k ring, v ring, start)."""
+                 split: bool = True, fused: bool = True):
+    """roll_prefill over a ring buffer: per chunk, cpk_ring_step (append of
+    the c rows fused into the attention launch), or with fused=False
+    cpk_ring_append then cpk_ring_attention.  Same outputs, bit for bit.
+    Returns (out over the padded sequence, n_leftpad, k ring, v ring,
+    start)."""
     L, Hq, D = q.shape
     Hkv = k.shape[1]
     n_left = (-L) % c
@@ -550,8 +574,13 @@ def ring_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream
     start = 0
     for j in range(Lp // c):
         sl = slice(j * c, (j + 1) * c)
-        start = cpk_ring_append(k[sl].unsqueeze(0), v[sl].unsqueeze(0), kr, vr, start, stream)
         m = None if masks is None else masks[j]
+        if fused:
+            _, start = cpk_ring_step(q[sl], k[sl], v[sl], kr[0], vr[0], (j + 1) * c, n_left,
+                                     start, mask=m, scale=scale, out=out[sl], stream=stream,
+                                     split=split)
+            continue
+        start = cpk_ring_append(k[sl].unsqueeze(0), v[sl].unsqueeze(0), kr, vr, start, stream)
         cpk_ring_attention(q[sl], kr[0], vr[0], (j + 1) * c, n_left, start, mask=m, scale=scale,
                            out=out[sl], stream=stream, split=split)
     return out, n_left, kr[0], vr[0], start

@@ -118,7 +118,7 @@ bool use_wide(int dtype, int group, int kv_heads, int rows)
 
 extern "C" {
 
-int cpk_version(void) { return 101; }
+int cpk_version(void) { return 102; }
 
 int cpk_set_attention_kernel(int kind)
 {
@@ -570,10 +570,10 @@ size_t cpk_roll_workspace_size(int Hq, int Hkv, int C, int c, int head_dim, int 
     return (size_t)parts * (size_t)c * (size_t)Hq * (size_t)(head_dim + 4) * sizeof(float);
 }
 
-static int roll_attention_impl(const void *q, const void *k, const void *v, const void *mask,
-                               int abs_end, int n_leftpad, int Hq, int Hkv, int C, int c, int D,
-                               int dtype, float scale, int ring_start, void *out, void *ws,
-                               size_t ws_bytes, void *stream)
+// Every check of a rolling attention call, before anything is launched.
+static int roll_check(const void *q, const void *k, const void *v, const void *mask, int abs_end,
+                      int n_leftpad, int Hq, int Hkv, int C, int c, int D, int dtype, void *out,
+                      void *ws, size_t ws_bytes)
 {
     int r = check_dtype_dim(dtype, D);
     if (r) return r;
@@ -585,6 +585,29 @@ static int roll_attention_impl(const void *q, const void *k, const void *v, cons
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(CPK_EALIGN, "roll_attention: buffer not aligned");
     if (mask && ((uintptr_t)mask & 3u)) return fail(CPK_EALIGN, "roll_attention: mask not aligned");
+    if (ws) {
+        const size_t need = cpk_roll_workspace_size(Hq, Hkv, C, c, D, dtype);
+        if (ws_bytes < need)
+            return fail(CPK_EWORKSPACE, "roll_attention: workspace %zu bytes, need %zu", ws_bytes,
+                        need);
+        if (!aligned16(ws)) return fail(CPK_EALIGN, "roll_attention: workspace not aligned");
+    }
+    return ok();
+}
+
+// Rolling attention over k/v (a literal shifted cache, or a ring whose
+// logical slot 0 is ring_start).  With k_chunk / v_chunk set (bf16/fp16),
+// the kernel also appends the chunk: its rows are the keys of the last c
+// slots, read from the chunk and written to their ring slots.
+static int roll_attention_impl(const void *q, const void *k, const void *v, const void *mask,
+                               int abs_end, int n_leftpad, int Hq, int Hkv, int C, int c, int D,
+                               int dtype, float scale, int ring_start, void *out, void *ws,
+                               size_t ws_bytes, void *stream, const void *k_chunk = nullptr,
+                               const void *v_chunk = nullptr)
+{
+    int r = roll_check(q, k, v, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D, dtype, out, ws,
+                       ws_bytes);
+    if (r) return r;
     cpk::AttnArgs a = {};
     a.q = q; a.k = k; a.v = v; a.out = out; a.mask = mask;
     a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.cap = C; a.mask_ld = C;
@@ -603,18 +626,15 @@ static int roll_attention_impl(const void *q, const void *k, const void *v, cons
         a.causal_base = C - c;
     }
     int parts = 1, pt = 0;
-    if (ws) {
-        roll_split(Hq, Hkv, C, c, dtype, &parts, &pt);
-        const size_t need = cpk_roll_workspace_size(Hq, Hkv, C, c, D, dtype);
-        if (ws_bytes < need)
-            return fail(CPK_EWORKSPACE, "roll_attention: workspace %zu bytes, need %zu", ws_bytes,
-                        need);
-        if (!aligned16(ws)) return fail(CPK_EALIGN, "roll_attention: workspace not aligned");
-    }
+    if (ws) roll_split(Hq, Hkv, C, c, dtype, &parts, &pt);
     a.n_parts = parts;
     a.part_tiles = pt;
     a.part_ws = (float *)ws;
     a.ring_start = ring_start;
+    if (k_chunk) {
+        a.k_new = k_chunk; a.v_new = v_chunk; a.new_base = C - c; a.new_rows = c;
+        a.seqlens = nullptr;
+    }
     const int br = cpk::attn_rows_per_block(dtype, Hq / Hkv, false);
     r = hip_status(
         cpk::launch_attention(a, dtype, (c + br - 1) / br, 1, false, (hipStream_t)stream),
@@ -667,6 +687,42 @@ int cpk_ring_append(const void *k_chunk, const void *v_chunk, void *k_ring, void
     return hip_status(cpk::launch_ring_append(k_chunk, v_chunk, k_ring, v_ring, B, H, C, c,
                                               D * elem_size(dtype), start, (hipStream_t)stream),
                       "ring_append launch");
+}
+
+int cpk_ring_step(const void *q, const void *k_chunk, const void *v_chunk, void *k_ring,
+                  void *v_ring, const void *mask, int abs_end, int n_leftpad, int Hq, int Hkv,
+                  int C, int c, int D, int dtype, float scale, int start, void *out, void *ws,
+                  size_t ws_bytes, void *stream)
+{
+    int r = roll_check(q, k_ring, v_ring, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D, dtype, out,
+                       ws, ws_bytes);
+    if (r) return r;
+    if (start < 0 || start >= C)
+        return fail(CPK_EINVAL, "ring_step: start=%d outside [0, C=%d)", start, C);
+    if (!k_chunk || !v_chunk) return fail(CPK_EINVAL, "ring_step: NULL chunk");
+    if (!aligned16(k_chunk) || !aligned16(v_chunk))
+        return fail(CPK_EALIGN, "ring_step: chunk not aligned");
+    const size_t ring_bytes = (size_t)Hkv * C * D * elem_size(dtype);
+    const size_t chunk_bytes = (size_t)c * Hkv * D * elem_size(dtype);
+    const void *srcs[2] = {k_chunk, v_chunk};
+    for (int i = 0; i < 2; ++i)
+        if (overlaps(srcs[i], chunk_bytes, k_ring, ring_bytes) ||
+            overlaps(srcs[i], chunk_bytes, v_ring, ring_bytes))
+            return fail(CPK_EINVAL, "ring_step: a chunk overlaps a ring");
+    if (overlaps(k_ring, ring_bytes, v_ring, ring_bytes))
+        return fail(CPK_EINVAL, "ring_step: k_ring and v_ring overlap");
+    const int next = (start + c) % C;
+    if (dtype == CPK_F32) {
+        // fp32 has no fused form: the append, then the attention
+        r = hip_status(cpk::launch_ring_append(k_chunk, v_chunk, k_ring, v_ring, 1, Hkv, C, c,
+                                               D * elem_size(dtype), start, (hipStream_t)stream),
+                       "ring_step append");
+        if (r) return r;
+        return roll_attention_impl(q, k_ring, v_ring, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D,
+                                   dtype, scale, next, out, ws, ws_bytes, stream);
+    }
+    return roll_attention_impl(q, k_ring, v_ring, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D,
+                               dtype, scale, next, out, ws, ws_bytes, stream, k_chunk, v_chunk);
 }
 
 int cpk_ring_view(const void *k_ring, const void *v_ring, void *k_out, void *v_out, int B, int H,

@@ -57,12 +57,14 @@ struct AttnArgs {
     int part_tiles;
     float *part_ws;
 
-    // fused append (scalar mode, bf16/fp16, no split): with k_new set, keys
-    // at or past new_base are read from k_new / v_new (token-major
+    // fused append (scalar mode, bf16/fp16): with k_new set, keys at or
+    // past new_base are read from k_new / v_new (token-major
     // [new_rows][Hkv][D]; key new_base + i is row min(i, new_rows - 1), so a
     // padded tail repeats the last real row) instead of the cache, and the
-    // workgroup of a row block writes the cache rows new_base + (its rows)
-    // of its KV head from them; one workgroup sets seqlens[slot] = len_after.
+    // part-0 workgroup of a row block writes the cache rows new_base + (its
+    // rows) of its KV head from them (physical rows (ring_start + position)
+    // mod cap in a ring buffer); with seqlens set, one workgroup sets
+    // seqlens[slot] = len_after.
     const void *k_new;
     const void *v_new;
     int new_base;

@@ -176,7 +176,8 @@ __device__ __forceinline__ bool resolve_seq(const AttnArgs &a, int z, SeqView &s
 }
 
 // Fused append: the cache rows of one row block and KV head, copied from
-// the new rows in 16-byte pieces, all reads issued before the writes.
+// the new rows in 16-byte pieces, all reads issued before the writes (by
+// part 0 alone when the key range is split).
 // Callers issue the writes before any tile load, so the kernels' counted
 // waits on tile loads stay exact (loads complete in order; older
 // outstanding stores only make a wait stricter).  The pieces live in
@@ -208,12 +209,16 @@ __device__ __forceinline__ void fused_append(const AttnArgs &a, int g, int r0, i
         if (c < 2 * n) {
             const bool isv = c >= n;
             const int cc = isv ? c - n : c;
-            uint16_t *dp = (isv ? cv : ck) + (int64_t)(a.new_base + r0 + cc / NCH) * D +
-                           (cc % NCH) * 8;
+            // physical row of logical position new_base + r0 + cc/NCH (a
+            // ring buffer starts at ring_start; the identity otherwise)
+            int row = a.new_base + r0 + cc / NCH + a.ring_start;
+            if (row >= a.cap) row -= a.cap;
+            uint16_t *dp = (isv ? cv : ck) + (int64_t)row * D + (cc % NCH) * 8;
             *(u32x4_t *)dp = val[j];
         }
     }
-    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) a.seqlens[a.slot] = a.len_after;
+    if (a.seqlens && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0)
+        a.seqlens[a.slot] = a.len_after;
 }
 
 // Source of one 16-byte piece of a K or V tile: the cache row of logical
@@ -297,7 +302,7 @@ void attn_mfma_kernel(AttnArgs a)
     const bool fused = a.k_new != nullptr;
     // keys at or past new_lo come from the new rows (never from the cache)
     const int new_lo = fused ? a.new_base : INT_MAX;
-    if (fused) {
+    if (fused && blockIdx.y == 0) {
         fused_append<D, kThreads, kQC>(a, g, r0, min(r0 + BR, sv.rows) - r0, tid);
     }
 
@@ -787,7 +792,7 @@ void attn_wide_kernel(AttnArgs a)
     const uint16_t *kc = (const uint16_t *)a.k + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
     const uint16_t *vc = (const uint16_t *)a.v + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
     const bool fused = a.k_new != nullptr;
-    if (fused) {
+    if (fused && blockIdx.y == 0) {
         fused_append<D, kWThreads, kWQC>(a, g, r0, min(r0 + BR, sv.rows) - r0, tid);
     }
 

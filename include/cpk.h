@@ -373,6 +373,25 @@ int cpk_ring_attention(const void *q, const void *k_ring, const void *v_ring,
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * One rolling chunk over a ring in one launch (batch 1): the result of
+ * cpk_ring_append(k_chunk, v_chunk, k_ring, v_ring, 1, Hkv, C, c, D, dtype,
+ * start) followed by cpk_ring_attention(..., start = (start + c) mod C),
+ * bit for bit in the output and in both rings.  The chunk's rows
+ * (token-major [c][Hkv][D]) are the keys of the last c logical slots: the
+ * attention kernel reads them from the chunk and writes them over the c
+ * oldest ring slots, which no query of this chunk sees, so the write and
+ * the reads never meet.  The caller advances start by c afterwards.  fp32
+ * runs the append and the attention as two launches.  The rolling cache
+ * step and its attention: Horizon developer blog "Chunk Prefill", sections
+ * 3 and 4.  Errors: those of both calls, all checked before anything is
+ * launched (CPK_EINVAL if a chunk overlaps a ring or the rings overlap).
+ */
+int cpk_ring_step(const void *q, const void *k_chunk, const void *v_chunk, void *k_ring,
+                  void *v_ring, const void *mask, int abs_end, int n_leftpad, int Hq, int Hkv,
+                  int C, int c, int D, int dtype, float scale, int start, void *out, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/*
  * The logical view of a ring as a contiguous cache: out slot s = physical
  * slot (start + s) mod C, for K and V, [B][H][C][D] each (interoperation
  * and checks; not on the per-chunk path).  CPK_EINVAL if start is outside

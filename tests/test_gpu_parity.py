@@ -482,6 +482,48 @@ def test_ring_matches_literal_shift(L, C, c, H, D):
     check(out_r[n_left:], ref[n_left:], 2e-2, "ring prefill vs oracle (real rows)")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("C,c,Hq,Hkv,D", [
+    (512, 128, 4, 4, 128),       # start walks 0, 128, 256, 384 and wraps
+    (300, 96, 4, 2, 64),         # C not a multiple of the key tile, GQA
+    (256, 256, 2, 2, 128),       # c == C: the chunk replaces the whole ring
+])
+def test_ring_step_fused_matches_two_calls(dtype, C, c, Hq, Hkv, D):
+    """cpk_ring_step (the append fused into the attention launch) equals
+    cpk_ring_append followed by cpk_ring_attention bit for bit: the output
+    of every chunk and both rings after it, split and unsplit, with the
+    computed visibility and with the explicit mask."""
+    say(f"case: fused ring step {dtype} C={C} c={c} heads {Hq}/{Hkv} D={D}")
+    tdt = si.TORCH_DTYPE[dtype]
+    g = si.generator(470 + C)
+    n = 5
+    q = si.randn((n * c, Hq, D), dtype, g).cuda()
+    k = si.randn((n * c, Hkv, D), dtype, g).cuda()
+    v = si.randn((n * c, Hkv, D), dtype, g).cuda()
+    L = n * c
+    for split in (True, False):
+        for explicit in (False, True):
+            ka = torch.zeros((1, Hkv, C, D), dtype=tdt, device="cuda")
+            va = torch.zeros_like(ka)
+            kb, vb = ka.clone(), va.clone()
+            sa = sb = 0
+            for j in range(n):
+                sl = slice(j * c, (j + 1) * c)
+                m = None
+                if explicit:
+                    m = torch.from_numpy(oracle.chunk_mask(L, 0, j, c, C)).to(tdt).cuda()
+                sa = cpk.cpk_ring_append(k[sl].unsqueeze(0), v[sl].unsqueeze(0), ka, va, sa)
+                ref = cpk.cpk_ring_attention(q[sl], ka[0], va[0], (j + 1) * c, 0, sa, mask=m,
+                                             split=split)
+                got, sb = cpk.cpk_ring_step(q[sl], k[sl], v[sl], kb[0], vb[0], (j + 1) * c, 0,
+                                            sb, mask=m, split=split)
+                torch.cuda.synchronize()
+                assert sb == sa
+                tag = f"chunk {j} split={split} mask={explicit}"
+                assert bitwise(got, ref), f"{tag}: output differs"
+                assert bitwise(kb, ka) and bitwise(vb, va), f"{tag}: rings differ"
+
+
 def test_workload4_ring_full_size():
     L, C, c, H, D = 4096, 2048, 256, 16, 128
     say(f"case: workload 4 on the ring buffer, L={L} C={C} c={c} H={H}: bit-equal to the shift")
