@@ -1210,27 +1210,50 @@ void attn_wide_kernel(AttnArgs a)
 
 // Merge of the split parts of a key range: for each (row, query head), in
 // part order, M = max_p M_p, f_p = 2^(M_p - M), out = sum_p f_p O_p /
-// sum_p f_p den_p.  One thread per output element d.
+// sum_p f_p den_p.  Each thread produces 8 consecutive outputs of one
+// (row, head): two 16-byte record loads per part and one 16-byte store.
+constexpr int kCombineThreads = 256;
+
 template <typename TR, int D>
-__global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a)
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a)
 {
-    const int row = blockIdx.x;
-    const int head = blockIdx.y;
-    const int d = threadIdx.x;
+    constexpr int TPP = D / 8;                       // threads per (row, head)
+    const int pair = blockIdx.x * (kCombineThreads / TPP) + threadIdx.x / TPP;
+    if (pair >= a.out_rows * a.Hq) return;
+    const int row = pair / a.Hq;
+    const int head = pair % a.Hq;
+    const int d0 = (threadIdx.x % TPP) * 8;
     const int64_t stride = (int64_t)a.out_rows * a.Hq * (D + 4);
-    const float *rec = a.part_ws + ((int64_t)row * a.Hq + head) * (D + 4);
+    const float *rec = a.part_ws + (int64_t)pair * (D + 4);
     float M = -INFINITY;
     for (int p = 0; p < a.n_parts; ++p) M = fmaxf(M, rec[p * stride]);
-    float num = 0.f, den = 0.f;
+    float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
     for (int p = 0; p < a.n_parts; ++p) {
         const float *r = rec + p * stride;
-        const float f = (r[0] == -INFINITY) ? 0.f : exp2f(r[0] - M);
-        num = __builtin_fmaf(f, r[4 + d], num);
-        den = __builtin_fmaf(f, r[1], den);
+        const float2 md = *(const float2 *)r;
+        const float f = (md.x == -INFINITY) ? 0.f : exp2f(md.x - M);
+        const float4 x0 = *(const float4 *)(r + 4 + d0);
+        const float4 x1 = *(const float4 *)(r + 8 + d0);
+        num[0] = __builtin_fmaf(f, x0.x, num[0]);
+        num[1] = __builtin_fmaf(f, x0.y, num[1]);
+        num[2] = __builtin_fmaf(f, x0.z, num[2]);
+        num[3] = __builtin_fmaf(f, x0.w, num[3]);
+        num[4] = __builtin_fmaf(f, x1.x, num[4]);
+        num[5] = __builtin_fmaf(f, x1.y, num[5]);
+        num[6] = __builtin_fmaf(f, x1.z, num[6]);
+        num[7] = __builtin_fmaf(f, x1.w, num[7]);
+        den = __builtin_fmaf(f, md.y, den);
     }
-    const float o = den > 0.f ? num / den : 0.f;
-    uint16_t *op = (uint16_t *)a.out + ((int64_t)(a.out_row0 + row) * a.Hq + head) * D;
-    op[d] = (uint16_t)TR::from_f32(o);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float o0 = den > 0.f ? num[2 * i] / den : 0.f;
+        const float o1 = den > 0.f ? num[2 * i + 1] / den : 0.f;
+        w[i] = TR::pack(o0, o1);
+    }
+    uint16_t *op = (uint16_t *)a.out + ((int64_t)(a.out_row0 + row) * a.Hq + head) * D + d0;
+    *(uint4 *)op = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -1382,13 +1405,16 @@ hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_
 
 hipError_t launch_attention_combine(const AttnArgs &a, int dtype, hipStream_t st)
 {
-    const dim3 grid(a.out_rows, a.Hq);
+    const int per_block = kCombineThreads / (a.D / 8);
+    const int pairs = a.out_rows * a.Hq;
+    const dim3 grid((pairs + per_block - 1) / per_block);
+    const dim3 block(kCombineThreads);
     if (dtype == 1) {
-        if (a.D == 64) hipLaunchKernelGGL((attn_combine_kernel<F16, 64>), grid, dim3(64), 0, st, a);
-        else hipLaunchKernelGGL((attn_combine_kernel<F16, 128>), grid, dim3(128), 0, st, a);
+        if (a.D == 64) hipLaunchKernelGGL((attn_combine_kernel<F16, 64>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attn_combine_kernel<F16, 128>), grid, block, 0, st, a);
     } else {
-        if (a.D == 64) hipLaunchKernelGGL((attn_combine_kernel<Bf16, 64>), grid, dim3(64), 0, st, a);
-        else hipLaunchKernelGGL((attn_combine_kernel<Bf16, 128>), grid, dim3(128), 0, st, a);
+        if (a.D == 64) hipLaunchKernelGGL((attn_combine_kernel<Bf16, 64>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attn_combine_kernel<Bf16, 128>), grid, block, 0, st, a);
     }
     return hipGetLastError();
 }
