@@ -245,6 +245,29 @@ def test_ring_validation():
     assert vw(FAKE, FAKE * 2, FAKE, big * 2, 1, 2, 8, 64, F16, 0, None) == cpk.CPK_EINVAL
 
 
+def test_ring_step_validation():
+    """cpk_ring_step checks the append's and the attention's arguments on
+    the host before anything is launched (fake aligned pointers)."""
+    F16 = cpk.CPK_F16
+    st = cpk._lib.cpk_ring_step
+    big = FAKE * 64
+    q, kc, vc, out = FAKE, FAKE * 2, FAKE * 3, FAKE * 4
+
+    def call(q=q, kc=kc, vc=vc, kr=big, vr=big * 2, c=4, C=8, D=64, start=0, abs_end=8):
+        return st(q, kc, vc, kr, vr, None, abs_end, 0, 2, 2, C, c, D, F16, 0.0, start, out,
+                  None, 0, None)
+
+    assert call(start=8) == cpk.CPK_EINVAL           # start outside [0, C)
+    assert call(start=-1) == cpk.CPK_EINVAL
+    assert call(kc=None) == cpk.CPK_EINVAL            # no chunk
+    assert call(kc=big) == cpk.CPK_EINVAL             # a chunk overlapping a ring
+    assert call(vr=big) == cpk.CPK_EINVAL             # the rings overlap
+    assert call(vc=FAKE * 3 + 8) == cpk.CPK_EALIGN    # unaligned chunk
+    assert call(c=9) == cpk.CPK_EINVAL                # c > C
+    assert call(D=96) == cpk.CPK_EDTYPE               # unsupported head dim
+    assert call(abs_end=3) == cpk.CPK_EINVAL          # abs_end < c
+
+
 def test_varlen_phases_validation():
     """cpk_varlen_step_phases takes a nonzero subset of the three phases."""
     f = cpk._lib.cpk_varlen_step_phases
