@@ -392,8 +392,9 @@ int cpk_paged_varlen_step(const void *q, const void *k_new, const void *v_new,
     if (pc->block_size < 256 || pc->block_size % 256 != 0)
         return fail(CPK_EINVAL, "paged: block_size %d must be a positive multiple of 256",
                     pc->block_size);
-    if (pc->n_blocks < 1 || pc->max_blocks < 1)
-        return fail(CPK_EINVAL, "paged: n_blocks=%d max_blocks=%d", pc->n_blocks, pc->max_blocks);
+    if (pc->n_blocks < 1 || pc->max_blocks < 1 || pc->max_blocks > cpk::kMaxTableBlocks)
+        return fail(CPK_EINVAL, "paged: n_blocks=%d max_blocks=%d (at most %d blocks per sequence)",
+                    pc->n_blocks, pc->max_blocks, cpk::kMaxTableBlocks);
     if ((int64_t)pc->max_blocks * pc->block_size > INT32_MAX / 2)
         return fail(CPK_EINVAL, "paged: max_blocks x block_size too large");
     if (pc->dtype == CPK_F32) return fail(CPK_EDTYPE, "paged: bf16 or fp16 only");

@@ -157,6 +157,9 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int max_segs, hipStream
 // Key tile of the bf16/fp16 attention kernel, and the merge of split parts
 // (a.n_parts > 1) into a.out.
 constexpr int kAttnTileKeys = 128;
+// most block-table entries per sequence in a paged attention call (the
+// attention kernels stage a workgroup's entries in LDS)
+constexpr int kMaxTableBlocks = 512;
 hipError_t launch_attention_combine(const AttnArgs &a, int dtype, hipStream_t st);
 bool decode_supported(int dtype, int D, int group, int capacity);
 

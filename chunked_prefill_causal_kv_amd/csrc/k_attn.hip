@@ -238,27 +238,34 @@ __device__ __forceinline__ const char *kv_src(const uint16_t *cache_head, const 
     return (const char *)(cache_head + (int64_t)phys * D + chunk_elem);
 }
 
-// Block rows of a paged pool for consecutive key tiles of one workgroup:
-// the block id of the tile after the current one is read one tile ahead,
-// so the table lookup is off the path of the tile loads that need it.
+// Block rows of a paged pool for one workgroup's key tiles.  At the start
+// the workgroup stages the block ids of its key range (clamped into the
+// pool) in LDS; a tile's lookup is then an LDS read, so no extra global
+// load sits among the tile loads, whose waits count them.  A barrier must
+// separate stage() from the first row().
 struct PagedTiles {
-    int t_next = -1;
-    int blk_next = 0;
-    __device__ __forceinline__ int lookup(const AttnArgs &a, int slot, int key) const
+    int b0 = 0;      // first block of the range
+    int nb = 0;      // staged entries - 1
+    const int *tab = nullptr;
+    __device__ __forceinline__ void stage(const AttnArgs &a, int slot, int key_first,
+                                          int key_last, int *lds, int tid, int nthreads)
     {
-        if (key >= a.max_blocks * a.block_size) return 0;   // past the table: unused
-        int b = a.block_table[(int64_t)slot * a.max_blocks + key / a.block_size];
-        return b < 0 ? 0 : (b >= a.n_blocks ? a.n_blocks - 1 : b);
+        const int last = a.max_blocks - 1;
+        b0 = min(max(key_first / a.block_size, 0), last);
+        const int b1 = min(max(key_last / a.block_size, b0), last);
+        nb = min(b1 - b0, kMaxTableBlocks - 1);
+        tab = lds;
+        for (int i = tid; i <= nb; i += nthreads) {
+            const int b = a.block_table[(int64_t)slot * a.max_blocks + b0 + i];
+            lds[i] = b < 0 ? 0 : (b >= a.n_blocks ? a.n_blocks - 1 : b);
+        }
     }
-    // element offset of tile kt's first row (head g), and prefetch of kt + 1
-    __device__ __forceinline__ int64_t row(const AttnArgs &a, int slot, int g, int kt,
-                                           int tile_keys)
+    // element offset of tile kt's first row (head g); the tile lies in one block
+    __device__ __forceinline__ int64_t row(const AttnArgs &a, int g, int kt, int tile_keys) const
     {
         const int key0 = kt * tile_keys;
-        const int b = kt == t_next ? blk_next : lookup(a, slot, key0);
-        t_next = kt + 1;
-        blk_next = lookup(a, slot, key0 + tile_keys);
-        return ((int64_t)b * a.Hkv + g) * a.block_size + key0 % a.block_size;
+        const int i = min(max(key0 / a.block_size - b0, 0), nb);
+        return ((int64_t)tab[i] * a.Hkv + g) * a.block_size + key0 % a.block_size;
     }
 };
 
@@ -277,6 +284,7 @@ void attn_mfma_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t buf0[TL::STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t buf1[TL::STAGE];
     __shared__ float ml[2 * 4 * kQC];
+    __shared__ int ptab[PAGED ? kMaxTableBlocks : 1];
 
     SeqView sv;
     if (!resolve_seq(a, blockIdx.z, sv)) return;
@@ -366,7 +374,7 @@ void attn_mfma_kernel(AttnArgs a)
         const char *kt_base, *vt_base;
         if constexpr (PAGED) {
             // paged pool: the tile lies inside one block
-            const int64_t row = ptiles.row(a, sv.slot, g, kt, kBK);
+            const int64_t row = ptiles.row(a, g, kt, kBK);
             kt_base = (const char *)((const uint16_t *)a.k + row * D);
             vt_base = (const char *)((const uint16_t *)a.v + row * D);
         } else {
@@ -561,6 +569,10 @@ void attn_mfma_kernel(AttnArgs a)
         __builtin_amdgcn_s_setprio(0);
     };
 
+    if constexpr (PAGED) {
+        ptiles.stage(a, sv.slot, t_first * kBK, (t_last + 1) * kBK - 1, ptab, tid, kThreads);
+        __syncthreads();
+    }
     if (t_last >= t_first) issue_tile(t_first, buf0);
     for (int kt = t_first; kt <= t_last; kt += 2) {
         tile_step(kt, buf0, buf1);
@@ -773,6 +785,7 @@ void attn_wide_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t ring2[2 * TILE];
     __shared__ __attribute__((aligned(16))) uint16_t ring3[2 * TILE];
     __shared__ float ml[2 * 2 * kWQC];
+    __shared__ int ptab[PAGED ? kMaxTableBlocks : 1];
 
     SeqView sv;
     if (!resolve_seq(a, blockIdx.z, sv)) return;
@@ -1042,7 +1055,7 @@ void attn_wide_kernel(AttnArgs a)
     };
     auto refill = [&](int t, uint16_t *slot) {
         if (t <= t_last) {
-            if constexpr (PAGED) prow = ptiles.row(a, sv.slot, g, t, kWBK);
+            if constexpr (PAGED) prow = ptiles.row(a, g, t, kWBK);
             issue(kc, t, slot, false);
             issue(vc, t, slot + TILE, true);
         }
@@ -1075,6 +1088,10 @@ void attn_wide_kernel(AttnArgs a)
         probs(scur, pb);
         accumulate(vf, pb);
     };
+    if constexpr (PAGED) {
+        ptiles.stage(a, sv.slot, t_first * kWBK, (t_last + 1) * kWBK - 1, ptab, tid, kWThreads);
+        __syncthreads();
+    }
     if (t_last >= t_first) {
         f32x16_t s0[2], s1[2];
         refill(t_first, ring0);

@@ -311,7 +311,9 @@ int cpk_roll_attention(const void *q, const void *k, const void *v,
  *   seqlens_k   device int32 [batch]
  *   block_size  a positive multiple of 256 (a key tile or decode segment
  *               never crosses a block)
- * A slot's capacity is max_blocks * block_size.  bf16 and fp16 only.
+ * A slot's capacity is max_blocks * block_size; max_blocks is at most 512
+ * (the attention kernels stage a workgroup's table entries on chip).  bf16
+ * and fp16 only.
  */
 typedef struct cpk_paged_cache {
     void *k;
@@ -331,8 +333,8 @@ typedef struct cpk_paged_cache {
  * cpk_varlen_step_phases over a paged cache: same arguments, phases,
  * workspace and results (bit for bit, given the same contents at the same
  * positions) as over a contiguous cache.  CPK_EINVAL for a NULL table,
- * block_size not a positive multiple of 256, or non-positive counts;
- * CPK_EDTYPE for fp32.
+ * block_size not a positive multiple of 256, non-positive counts or
+ * max_blocks above 512; CPK_EDTYPE for fp32.
  */
 int cpk_paged_varlen_step(const void *q, const void *k_new, const void *v_new,
                           const cpk_paged_cache *cache, const int32_t *slots,

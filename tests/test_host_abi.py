@@ -279,7 +279,8 @@ def test_varlen_phases_validation():
 
 def test_paged_validation():
     """Paged caches: block_size a positive multiple of 256, a block table,
-    positive counts, bf16/fp16 only -- rejected on the host."""
+    positive counts, at most 512 blocks per sequence, bf16/fp16 only --
+    rejected on the host."""
     def desc(bs=256, nb=8, mb=4, dt=cpk.CPK_BF16, table=FAKE):
         return cpk.cpk_paged_cache(FAKE, FAKE * 2, table, FAKE * 3, 2, 4, bs, nb, mb, 128, dt)
     f = cpk._lib.cpk_paged_varlen_step
@@ -288,6 +289,7 @@ def test_paged_validation():
     assert f(*args(desc(bs=128))) == cpk.CPK_EINVAL
     assert f(*args(desc(bs=0))) == cpk.CPK_EINVAL
     assert f(*args(desc(nb=0))) == cpk.CPK_EINVAL
+    assert f(*args(desc(mb=513))) == cpk.CPK_EINVAL     # table entries staged on chip
     assert f(*args(desc(table=None))) == cpk.CPK_EINVAL
     assert f(*args(desc(dt=cpk.CPK_F32))) == cpk.CPK_EDTYPE
 
