@@ -435,6 +435,7 @@ static int varlen_impl(const void *q, const void *k_new, const void *v_new,
         return fail(CPK_EINVAL, "varlen: cu_rows must run from 0 to total_rows");
     std::vector<char> used((size_t)cache->batch, 0);
     int max_ctx = 0, max_rows = 0, n_dec = 0, n_pre = 0;
+    int pre_lo = n_seqs, pre_hi = 0;   // range of the sequences with prompt rows
     const int G = q_heads / cache->kv_heads;
     const bool dec_ok = cpk::decode_supported(cache->dtype, cache->head_dim, G, cache->capacity);
     for (int s = 0; s < n_seqs; ++s) {
@@ -455,6 +456,8 @@ static int varlen_impl(const void *q, const void *k_new, const void *v_new,
         } else {
             ++n_pre;
             if (rows > max_rows) max_rows = rows;
+            if (s < pre_lo) pre_lo = s;
+            pre_hi = s + 1;
         }
     }
     const int max_segs = (max_ctx + cpk::kDecodeSeg - 1) / cpk::kDecodeSeg;
@@ -495,17 +498,20 @@ static int varlen_impl(const void *q, const void *k_new, const void *v_new,
         a.q = q; a.k = cache->k; a.v = cache->v; a.out = out; a.mask = nullptr;
         a.Hq = q_heads; a.Hkv = cache->kv_heads; a.D = cache->head_dim; a.cap = cache->capacity;
         fill_scale(a, sc);
-        a.varlen = 1; a.cu_rows = cu_rows; a.past_lens = past_lens; a.slots = slots;
-        a.n_seqs = n_seqs; a.min_rows = dec_ok ? 2 : 1;
+        // the launch covers only the range of sequences with prompt rows
+        // (row offsets stay absolute); a decode row inside the range is
+        // skipped by its workgroups
+        a.varlen = 1; a.cu_rows = cu_rows + pre_lo; a.past_lens = past_lens + pre_lo;
+        a.slots = slots + pre_lo; a.n_seqs = pre_hi - pre_lo; a.min_rows = dec_ok ? 2 : 1;
         if (pg) {
             a.block_table = pg->table; a.max_blocks = pg->max_blocks;
             a.block_size = pg->block_size; a.n_blocks = pg->n_blocks;
         }
         const bool wide = use_wide(cache->dtype, G, cache->kv_heads, max_rows);
         const int br = cpk::attn_rows_per_block(cache->dtype, G, wide);
-        r = hip_status(
-            cpk::launch_attention(a, cache->dtype, (max_rows + br - 1) / br, n_seqs, wide, st),
-            "varlen prefill");
+        r = hip_status(cpk::launch_attention(a, cache->dtype, (max_rows + br - 1) / br,
+                                             pre_hi - pre_lo, wide, st),
+                       "varlen prefill");
         if (r) return r;
     }
     return ok();

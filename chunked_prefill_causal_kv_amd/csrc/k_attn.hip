@@ -750,9 +750,11 @@ __device__ __forceinline__ uint4 here(uint4 x)
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// One work item of the 128-column kernel: row block and KV head bx, split
+// part by, sequence bz (the launch grid's coordinates, or an item of a
+// persistent launch).
 template <typename TR, int D, bool PAGED>
-__global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_wide_kernel(AttnArgs a)
+__device__ __forceinline__ void attn_wide_item(const AttnArgs &a, int bx, int by, int bz)
 {
     using TL = Tile<D>;
     constexpr int NCH = TL::NCH;
@@ -788,11 +790,11 @@ void attn_wide_kernel(AttnArgs a)
     __shared__ int ptab[PAGED ? kMaxTableBlocks : 1];
 
     SeqView sv;
-    if (!resolve_seq(a, blockIdx.z, sv)) return;
+    if (!resolve_seq(a, bz, sv)) return;
     const int G = a.Hq / a.Hkv;
     const int BR = kWQC / G;                // rows per workgroup
-    const int g = blockIdx.x % a.Hkv;       // KV head fastest: one KV head per XCD
-    const int r0 = (blockIdx.x / a.Hkv) * BR;
+    const int g = bx % a.Hkv;       // KV head fastest: one KV head per XCD
+    const int r0 = (bx / a.Hkv) * BR;
     if (r0 >= sv.rows) return;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -805,7 +807,7 @@ void attn_wide_kernel(AttnArgs a)
     const uint16_t *kc = (const uint16_t *)a.k + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
     const uint16_t *vc = (const uint16_t *)a.v + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
     const bool fused = a.k_new != nullptr;
-    if (fused && blockIdx.y == 0) {
+    if (fused && by == 0) {
         fused_append<D, kWThreads, kWQC>(a, g, r0, min(r0 + BR, sv.rows) - r0, tid);
     }
 
@@ -834,8 +836,8 @@ void attn_wide_kernel(AttnArgs a)
     int t_last = (key_end - 1) / kWBK;
     if (a.n_parts > 1) {
         constexpr int R = kAttnTileKeys / kWBK;
-        t_first = max(t_first, (int)blockIdx.y * a.part_tiles * R);
-        t_last = min(t_last, ((int)blockIdx.y + 1) * a.part_tiles * R - 1);
+        t_first = max(t_first, by * a.part_tiles * R);
+        t_last = min(t_last, (by + 1) * a.part_tiles * R - 1);
     }
 
     // ---- direct global->LDS tile loads: load i of this wave fills LDS
@@ -1187,7 +1189,7 @@ void attn_wide_kernel(AttnArgs a)
         if (oc < BR * G && row < sv.out_rows && a.n_parts > 1) {
             const int head = g * G + oc % G;
             float *rec =
-                a.part_ws + (((int64_t)blockIdx.y * sv.out_rows + row) * a.Hq + head) * (D + 4);
+                a.part_ws + (((int64_t)by * sv.out_rows + row) * a.Hq + head) * (D + 4);
             if (part == 0) {
                 const float m0 = Ms[oc], m1 = Ms[kWQC + oc];
                 const float M = fmaxf(m0, m1);
@@ -1221,6 +1223,26 @@ void attn_wide_kernel(AttnArgs a)
                 }
                 *(uint4 *)(op + d8) = make_uint4(w[0], w[1], w[2], w[3]);
             }
+        }
+    }
+}
+
+// The 128-column kernel.  The persistent form's grid is smaller than the
+// work: each workgroup takes items blockIdx.x, + gridDim.x, ... of
+// persist_items (row block and KV head fastest, then sequence), so the
+// launch holds only gridDim.x compute units and leaves the rest to work on
+// other streams.  A grid that is a multiple of the XCD count keeps every
+// item of a workgroup on its KV head.
+template <typename TR, int D, bool PAGED, bool PERSIST = false>
+__global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_wide_kernel(AttnArgs a)
+{
+    if constexpr (!PERSIST) {
+        attn_wide_item<TR, D, PAGED>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    } else {
+        for (int item = blockIdx.x; item < a.persist_items; item += gridDim.x) {
+            attn_wide_item<TR, D, PAGED>(a, item % a.persist_nx, 0, item / a.persist_nx);
+            __syncthreads();   // the item's LDS is free for the next one
         }
     }
 }
@@ -1404,10 +1426,34 @@ int attn_rows_per_block(int dtype, int group, bool wide)
     } while (0)
 
 hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
-                            bool wide, hipStream_t st)
+                            bool wide, hipStream_t st, int persist_wgs)
 {
     const dim3 grid(row_blocks * a.Hkv, a.n_parts > 1 ? a.n_parts : 1, n_seq_grid);
-    if (wide && dtype != 0) {
+    if (wide && dtype != 0 && persist_wgs > 0 && a.n_parts <= 1) {
+        // persistent: persist_wgs workgroups loop over the grid's items
+        AttnArgs p = a;
+        p.persist_nx = row_blocks * a.Hkv;
+        p.persist_items = p.persist_nx * n_seq_grid;
+        const dim3 pg(min(persist_wgs, p.persist_items));
+        const bool pgd = a.block_size != 0;
+        if (dtype == 1) {
+            if (a.D == 64) {
+                if (pgd) hipLaunchKernelGGL((attn_wide_kernel<F16, 64, true, true>), pg, dim3(kWThreads), 0, st, p);
+                else hipLaunchKernelGGL((attn_wide_kernel<F16, 64, false, true>), pg, dim3(kWThreads), 0, st, p);
+            } else {
+                if (pgd) hipLaunchKernelGGL((attn_wide_kernel<F16, 128, true, true>), pg, dim3(kWThreads), 0, st, p);
+                else hipLaunchKernelGGL((attn_wide_kernel<F16, 128, false, true>), pg, dim3(kWThreads), 0, st, p);
+            }
+        } else {
+            if (a.D == 64) {
+                if (pgd) hipLaunchKernelGGL((attn_wide_kernel<Bf16, 64, true, true>), pg, dim3(kWThreads), 0, st, p);
+                else hipLaunchKernelGGL((attn_wide_kernel<Bf16, 64, false, true>), pg, dim3(kWThreads), 0, st, p);
+            } else {
+                if (pgd) hipLaunchKernelGGL((attn_wide_kernel<Bf16, 128, true, true>), pg, dim3(kWThreads), 0, st, p);
+                else hipLaunchKernelGGL((attn_wide_kernel<Bf16, 128, false, true>), pg, dim3(kWThreads), 0, st, p);
+            }
+        }
+    } else if (wide && dtype != 0) {
         CPK_LAUNCH_MFMA(attn_wide_kernel, kWThreads);
     } else if (dtype == 0) {
         if (a.D == 64)

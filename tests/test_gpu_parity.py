@@ -652,6 +652,54 @@ def _run_mixed(n_dec, ctx_lo, ctx_hi, prompt, budget, Hq, Hkv, D, seed, cap, che
 
 
 @pytest.mark.parametrize("kernel", ["narrow", "wide"])
+def test_varlen_interleaved_order(kernel):
+    """Prompt and decode sequences interleaved in the pack (prompts first,
+    between and after decodes) give, sequence by sequence, the same bits as
+    the same step packed decodes-first, and the prompt rows match the
+    oracle: the prefill launch covers only the range of prompt sequences
+    and skips the decode rows inside it."""
+    say(f"case: varlen interleaved order [{kernel}]: 2 prompts, 3 decodes, G=4")
+    Hq, Hkv, D, cap = 8, 2, 128, 1024
+    # slot: (past, rows)
+    seqs = {0: (100, 300), 1: (50, 1), 2: (700, 1), 3: (0, 200), 4: (10, 1)}
+    g = si.generator(540)
+    data = {}
+    for sl, (past, rows) in seqs.items():
+        data[sl] = tuple(si.randn((rows, h, D), "bf16", g).cuda() for h in (Hq, Hkv, Hkv))
+    caches = []
+    for _ in range(2):
+        c = cpk.KVCache(5, Hkv, cap, D, torch.bfloat16)
+        si.fill_seeded(c.k, 541)
+        si.fill_seeded(c.v, 542)
+        c.lens = [seqs[s][0] for s in range(5)]
+        caches.append(c)
+    outs = []
+    with cpk.attention_kernel(KERNELS[kernel]):
+        for order, cache in zip(([0, 1, 2, 3, 4], [1, 2, 4, 0, 3]), caches):
+            q = torch.cat([data[s][0] for s in order])
+            kn = torch.cat([data[s][1] for s in order])
+            vn = torch.cat([data[s][2] for s in order])
+            cu = [0]
+            for s in order:
+                cu.append(cu[-1] + seqs[s][1])
+            out = cpk.cpk_varlen_step(q, kn, vn, cache, order, cu, [seqs[s][0] for s in order])
+            torch.cuda.synchronize()
+            outs.append({s: out[cu[i]:cu[i + 1]] for i, s in enumerate(order)})
+    for s in seqs:
+        assert bitwise(outs[0][s], outs[1][s]), f"slot {s}: order changes the output"
+    assert bitwise(caches[0].k, caches[1].k) and bitwise(caches[0].v, caches[1].v)
+    for s in (0, 3):
+        past, rows = seqs[s]
+        n = past + rows
+        kk = oracle.widen(si.storage(caches[0].k[s, :, :n]), oracle.BF16)
+        vv = oracle.widen(si.storage(caches[0].v[s, :, :n]), oracle.BF16)
+        qq = oracle.widen(si.storage(data[s][0]), oracle.BF16)
+        lim = (past + np.arange(rows)).astype(np.int32)
+        ref = oracle.attention(qq, kk, vv, np.zeros(rows, np.int32), lim, 1.0 / math.sqrt(D))
+        check(outs[0][s], ref, 2e-2, f"prompt slot {s}")
+
+
+@pytest.mark.parametrize("kernel", ["narrow", "wide"])
 def test_mixed_step_small_full_compare(kernel):
     say(f"case: mixed step small [{kernel}]: 5 decodes ctx 20..300, prompt 700, budget 128, G=4")
     with cpk.attention_kernel(KERNELS[kernel]):
