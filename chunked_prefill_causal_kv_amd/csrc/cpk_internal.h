@@ -72,11 +72,6 @@ struct AttnArgs {
     int32_t *seqlens;
     int len_after;
 
-    // persistent launch of the 128-column kernel (0: one item per
-    // workgroup): persist_items items, persist_nx of them per sequence
-    int persist_items;
-    int persist_nx;
-
     // rolling ring buffer (64-column kernel): logical key s of the rolling
     // view sits at physical row (ring_start + s) mod cap; 0 = no ring
     int ring_start;
@@ -154,10 +149,8 @@ hipError_t launch_ring_view(const void *k_ring, const void *v_ring, void *k_out,
 // takes the explicit additive mask, so both of its forms stay bit-equal).
 constexpr int kWideMinGroups = 256;   // auto choice: wide once its grid fills the CUs
 int attn_rows_per_block(int dtype, int group, bool wide);
-// persist_wgs > 0 (128-column kernel, no split): that many workgroups loop
-// over the grid's items instead of one workgroup per item
 hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
-                            bool wide, hipStream_t st, int persist_wgs = 0);
+                            bool wide, hipStream_t st);
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int max_segs, hipStream_t st);
 

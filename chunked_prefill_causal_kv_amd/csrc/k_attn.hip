@@ -751,8 +751,7 @@ __device__ __forceinline__ uint4 here(uint4 x)
 }
 
 // One work item of the 128-column kernel: row block and KV head bx, split
-// part by, sequence bz (the launch grid's coordinates, or an item of a
-// persistent launch).
+// part by, sequence bz.
 template <typename TR, int D, bool PAGED>
 __device__ __forceinline__ void attn_wide_item(const AttnArgs &a, int bx, int by, int bz)
 {
@@ -1227,24 +1226,12 @@ __device__ __forceinline__ void attn_wide_item(const AttnArgs &a, int bx, int by
     }
 }
 
-// The 128-column kernel.  The persistent form's grid is smaller than the
-// work: each workgroup takes items blockIdx.x, + gridDim.x, ... of
-// persist_items (row block and KV head fastest, then sequence), so the
-// launch holds only gridDim.x compute units and leaves the rest to work on
-// other streams.  A grid that is a multiple of the XCD count keeps every
-// item of a workgroup on its KV head.
-template <typename TR, int D, bool PAGED, bool PERSIST = false>
+// The 128-column kernel: one work item per workgroup.
+template <typename TR, int D, bool PAGED>
 __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_wide_kernel(AttnArgs a)
 {
-    if constexpr (!PERSIST) {
-        attn_wide_item<TR, D, PAGED>(a, blockIdx.x, blockIdx.y, blockIdx.z);
-    } else {
-        for (int item = blockIdx.x; item < a.persist_items; item += gridDim.x) {
-            attn_wide_item<TR, D, PAGED>(a, item % a.persist_nx, 0, item / a.persist_nx);
-            __syncthreads();   // the item's LDS is free for the next one
-        }
-    }
+    attn_wide_item<TR, D, PAGED>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Merge of the split parts of a key range: for each (row, query head), in
@@ -1426,34 +1413,10 @@ int attn_rows_per_block(int dtype, int group, bool wide)
     } while (0)
 
 hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
-                            bool wide, hipStream_t st, int persist_wgs)
+                            bool wide, hipStream_t st)
 {
     const dim3 grid(row_blocks * a.Hkv, a.n_parts > 1 ? a.n_parts : 1, n_seq_grid);
-    if (wide && dtype != 0 && persist_wgs > 0 && a.n_parts <= 1) {
-        // persistent: persist_wgs workgroups loop over the grid's items
-        AttnArgs p = a;
-        p.persist_nx = row_blocks * a.Hkv;
-        p.persist_items = p.persist_nx * n_seq_grid;
-        const dim3 pg(min(persist_wgs, p.persist_items));
-        const bool pgd = a.block_size != 0;
-        if (dtype == 1) {
-            if (a.D == 64) {
-                if (pgd) hipLaunchKernelGGL((attn_wide_kernel<F16, 64, true, true>), pg, dim3(kWThreads), 0, st, p);
-                else hipLaunchKernelGGL((attn_wide_kernel<F16, 64, false, true>), pg, dim3(kWThreads), 0, st, p);
-            } else {
-                if (pgd) hipLaunchKernelGGL((attn_wide_kernel<F16, 128, true, true>), pg, dim3(kWThreads), 0, st, p);
-                else hipLaunchKernelGGL((attn_wide_kernel<F16, 128, false, true>), pg, dim3(kWThreads), 0, st, p);
-            }
-        } else {
-            if (a.D == 64) {
-                if (pgd) hipLaunchKernelGGL((attn_wide_kernel<Bf16, 64, true, true>), pg, dim3(kWThreads), 0, st, p);
-                else hipLaunchKernelGGL((attn_wide_kernel<Bf16, 64, false, true>), pg, dim3(kWThreads), 0, st, p);
-            } else {
-                if (pgd) hipLaunchKernelGGL((attn_wide_kernel<Bf16, 128, true, true>), pg, dim3(kWThreads), 0, st, p);
-                else hipLaunchKernelGGL((attn_wide_kernel<Bf16, 128, false, true>), pg, dim3(kWThreads), 0, st, p);
-            }
-        }
-    } else if (wide && dtype != 0) {
+    if (wide && dtype != 0) {
         CPK_LAUNCH_MFMA(attn_wide_kernel, kWThreads);
     } else if (dtype == 0) {
         if (a.D == 64)
