@@ -439,38 +439,51 @@ void attn_mfma_kernel(AttnArgs a)
 
     // one tile: wait for its loads, start the next tile's loads into the
     // other buffer, then compute on this one
+    // Explicit additive mask.  With an 8-byte aligned mask whose row length
+    // is a multiple of 4, the lane's 16 keys of a tile are 4 runs of 4
+    // consecutive keys: one 8-byte load per run (a run starting at or past
+    // the row's end is re-read from the row's last run; those keys are
+    // masked out whatever the values).  Those words are loaded one tile
+    // ahead, behind the next tile's loads, so the wait at the start of a
+    // tile covers them.
+    const uint16_t *mrow = maskp ? maskp + (int64_t)qrow * a.mask_ld : nullptr;
+    const bool mfast = maskp && (a.mask_ld & 3) == 0 && ((uintptr_t)maskp & 7u) == 0;
+    uint2 mnext[4];
+    auto load_mask = [&](int kt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key0 = min(kt * kBK + ks * 32 + 8 * r + 4 * hi, a.mask_ld - 4);
+            mnext[r] = *(const uint2 *)(mrow + key0);
+        }
+    };
+    if (mfast && t_last >= t_first) load_mask(t_first);
+
     auto tile_step = [&](int kt, const uint16_t *Kb, uint16_t *next) {
         __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of tile kt have landed
         __syncthreads();                   // ... and every wave's; `next` is free again
-        // explicit additive mask values of this tile (loaded before the next
-        // tile's loads, so waiting for them does not wait for those)
         const int kbase = kt * kBK + ks * 32;
         float mvals[16];
-        if (maskp) {
-            const uint16_t *mrow = maskp + (int64_t)qrow * a.mask_ld;
-            if ((a.mask_ld & 3) == 0 && ((uintptr_t)maskp & 7u) == 0) {
-                // the lane's 16 keys are 4 runs of 4 consecutive keys: one
-                // 8-byte load per run (a run starting at or past the row's
-                // end is re-read from the row's last run; those keys are
-                // masked out below whatever the values)
+        if (mfast) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key0 = min(kbase + 8 * r + 4 * hi, a.mask_ld - 4);
-                    const uint2 w = *(const uint2 *)(mrow + key0);
-                    mvals[4 * r + 0] = TR::to_f32(w.x & 0xffffu);
-                    mvals[4 * r + 1] = TR::to_f32(w.x >> 16);
-                    mvals[4 * r + 2] = TR::to_f32(w.y & 0xffffu);
-                    mvals[4 * r + 3] = TR::to_f32(w.y >> 16);
-                }
-            } else {
+            for (int r = 0; r < 4; ++r) {
+                mvals[4 * r + 0] = TR::to_f32(mnext[r].x & 0xffffu);
+                mvals[4 * r + 1] = TR::to_f32(mnext[r].x >> 16);
+                mvals[4 * r + 2] = TR::to_f32(mnext[r].y & 0xffffu);
+                mvals[4 * r + 3] = TR::to_f32(mnext[r].y >> 16);
+            }
+        } else if (maskp) {
+            // other layouts: element loads of this tile (issued before the
+            // next tile's loads, so waiting for them does not wait for those)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
-                    mvals[j] = TR::to_f32(mrow[key < sv.n_keys ? key : sv.n_keys - 1]);
-                }
+            for (int j = 0; j < 16; ++j) {
+                const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
+                mvals[j] = TR::to_f32(mrow[key < sv.n_keys ? key : sv.n_keys - 1]);
             }
         }
-        if (kt < t_last) issue_tile(kt + 1, next);
+        if (kt < t_last) {
+            issue_tile(kt + 1, next);
+            if (mfast) load_mask(kt + 1);
+        }
         const uint16_t *Vb = Kb + kBK * D;
 
         // S^T[32 keys x 32 cols] for this wave's key slice and column group.
