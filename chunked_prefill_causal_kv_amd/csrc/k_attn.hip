@@ -176,35 +176,52 @@ __device__ __forceinline__ bool resolve_seq(const AttnArgs &a, int z, SeqView &s
 }
 
 // Fused append: the cache rows of one row block and KV head, copied from
-// the new rows in 16-byte pieces, all reads issued before the writes (by
-// part 0 alone when the key range is split).
-// Callers issue the writes before any tile load, so the kernels' counted
-// waits on tile loads stay exact (loads complete in order; older
-// outstanding stores only make a wait stricter).  The pieces live in
-// registers: the array is local to this one fully unrolled function.
+// the new rows in 16-byte pieces (by part 0 alone when the key range is
+// split).  append_load reads this workgroup's pieces into registers and
+// append_store writes them, so a kernel can put the loads in flight beside
+// its first tile loads and issue the stores after its first full wait.  No
+// workgroup reads the cache rows being written (keys at or past new_base
+// come from the new rows), so the stores may land at any time.  The pieces
+// live in registers: a local ext_vector array indexed by unrolled constants.
 template <int D, int THREADS, int MAXROWS>
-__device__ __forceinline__ void fused_append(const AttnArgs &a, int g, int r0, int n_rows, int tid)
+constexpr int append_pieces()
+{
+    return (MAXROWS * (D / 8) * 2 + THREADS - 1) / THREADS;
+}
+
+template <int D, int THREADS, int JB, int JE>
+__device__ __forceinline__ void append_load(const AttnArgs &a, int g, int r0, int n_rows, int tid,
+                                            u32x4_t (&val)[JE - JB])
 {
     constexpr int NCH = D / 8;
-    constexpr int PER = (MAXROWS * NCH * 2 + THREADS - 1) / THREADS;
-    const int n = n_rows * NCH;
-    u32x4_t val[PER];
+    const int n = n_rows * NCH;   // pieces per tensor; n_rows >= 1
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int c = tid + j * THREADS;
-        if (c < 2 * n) {
+    for (int j = JB; j < JE; ++j) {
+        // a piece index past the end re-reads the last piece, so the load
+        // needs no branch and the value no merge at a join (which would make
+        // the compiler wait for it at once); only the store is conditional
+        if (j == 0 || j * THREADS < 2 * n) {   // uniform
+            const int c = min(tid + j * THREADS, 2 * n - 1);
             const bool isv = c >= n;
             const int cc = isv ? c - n : c;
             const int src = min(r0 + cc / NCH, a.new_rows - 1);
             const uint16_t *sp = (const uint16_t *)(isv ? a.v_new : a.k_new) +
                                  ((int64_t)src * a.Hkv + g) * D + (cc % NCH) * 8;
-            val[j] = *(const u32x4_t *)sp;
+            val[j - JB] = *(const __attribute__((address_space(1))) u32x4_t *)sp;
         }
     }
+}
+
+template <int D, int THREADS, int JB, int JE>
+__device__ __forceinline__ void append_store(const AttnArgs &a, int g, int r0, int n_rows, int tid,
+                                             const u32x4_t (&val)[JE - JB], bool set_len)
+{
+    constexpr int NCH = D / 8;
+    const int n = n_rows * NCH;
     uint16_t *ck = (uint16_t *)a.k + ((int64_t)a.slot * a.Hkv + g) * a.cap * D;
     uint16_t *cv = (uint16_t *)a.v + ((int64_t)a.slot * a.Hkv + g) * a.cap * D;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
+    for (int j = JB; j < JE; ++j) {
         const int c = tid + j * THREADS;
         if (c < 2 * n) {
             const bool isv = c >= n;
@@ -214,11 +231,27 @@ __device__ __forceinline__ void fused_append(const AttnArgs &a, int g, int r0, i
             int row = a.new_base + r0 + cc / NCH + a.ring_start;
             if (row >= a.cap) row -= a.cap;
             uint16_t *dp = (isv ? cv : ck) + (int64_t)row * D + (cc % NCH) * 8;
-            *(u32x4_t *)dp = val[j];
+            *(u32x4_t *)dp = val[j - JB];
         }
     }
-    if (a.seqlens && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0)
+    if (set_len && a.seqlens && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0)
         a.seqlens[a.slot] = a.len_after;
+}
+
+// Pieces [JB, JE) loaded and stored back to back.  Callers that count
+// their waits on tile loads call this before any tile load: loads complete
+// in order, and older outstanding stores only make a wait stricter.
+template <int D, int THREADS, int JB, int JE>
+__device__ __forceinline__ void fused_append(const AttnArgs &a, int g, int r0, int n_rows, int tid,
+                                             bool set_len)
+{
+    if constexpr (JE > JB) {
+        if (JB * THREADS < 2 * n_rows * (D / 8)) {   // uniform: any piece from JB on
+            u32x4_t val[JE - JB];
+            append_load<D, THREADS, JB, JE>(a, g, r0, n_rows, tid, val);
+            append_store<D, THREADS, JB, JE>(a, g, r0, n_rows, tid, val, set_len);
+        }
+    }
 }
 
 // Source of one 16-byte piece of a K or V tile: the cache row of logical
@@ -310,8 +343,17 @@ void attn_mfma_kernel(AttnArgs a)
     const bool fused = a.k_new != nullptr;
     // keys at or past new_lo come from the new rows (never from the cache)
     const int new_lo = fused ? a.new_base : INT_MAX;
-    if (fused && blockIdx.y == 0) {
-        fused_append<D, kThreads, kQC>(a, g, r0, min(r0 + BR, sv.rows) - r0, tid);
+    // fused append: the first piece of every thread (the whole append once
+    // G >= 4) is loaded now, beside the query and first tile loads, and
+    // stored after the first tile's wait (one round trip less before the
+    // first tile); further pieces (G < 4) are copied at once
+    const bool app_on = fused && blockIdx.y == 0;
+    const int app_rows = min(r0 + BR, sv.rows) - r0;
+    u32x4_t app[1];
+    if (app_on) {
+        append_load<D, kThreads, 0, 1>(a, g, r0, app_rows, tid, app);
+        fused_append<D, kThreads, 1, append_pieces<D, kThreads, kQC>()>(a, g, r0, app_rows, tid,
+                                                                        false);
     }
 
     // ---- query fragment (B operand of S^T = K Q^T): column qc
@@ -461,6 +503,9 @@ void attn_mfma_kernel(AttnArgs a)
     auto tile_step = [&](int kt, const uint16_t *Kb, uint16_t *next) {
         __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of tile kt have landed
         __syncthreads();                   // ... and every wave's; `next` is free again
+        // the append's loads have landed with the first tile's
+        if (kt == t_first && app_on)
+            append_store<D, kThreads, 0, 1>(a, g, r0, app_rows, tid, app, true);
         const int kbase = kt * kBK + ks * 32;
         float mvals[16];
         if (mfast) {
@@ -586,10 +631,14 @@ void attn_mfma_kernel(AttnArgs a)
         ptiles.stage(a, sv.slot, t_first * kBK, (t_last + 1) * kBK - 1, ptab, tid, kThreads);
         __syncthreads();
     }
-    if (t_last >= t_first) issue_tile(t_first, buf0);
-    for (int kt = t_first; kt <= t_last; kt += 2) {
-        tile_step(kt, buf0, buf1);
-        if (kt + 1 <= t_last) tile_step(kt + 1, buf1, buf0);
+    if (t_last >= t_first) {
+        issue_tile(t_first, buf0);
+        for (int kt = t_first; kt <= t_last; kt += 2) {
+            tile_step(kt, buf0, buf1);
+            if (kt + 1 <= t_last) tile_step(kt + 1, buf1, buf0);
+        }
+    } else if (app_on) {
+        append_store<D, kThreads, 0, 1>(a, g, r0, app_rows, tid, app, true);
     }
     __syncthreads();   // all waves are done with the tiles: reuse LDS below
 
@@ -819,11 +868,10 @@ __device__ __forceinline__ void attn_wide_item(const AttnArgs &a, int bx, int by
     const uint16_t *kc = (const uint16_t *)a.k + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
     const uint16_t *vc = (const uint16_t *)a.v + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
     const bool fused = a.k_new != nullptr;
-    if (fused && by == 0) {
-        fused_append<D, kWThreads, kWQC>(a, g, r0, min(r0 + BR, sv.rows) - r0, tid);
-    }
 
-    // ---- query fragments (B operand of S^T = K Q^T) of the two column blocks
+    // ---- query fragments (B operand of S^T = K Q^T) of the two column
+    // blocks, loaded before the fused append's copy so that the two round
+    // trips overlap, and moved to accumulation registers after it
     uint4 qf[2][NS];
     int lim[2];
 #pragma unroll
@@ -838,8 +886,16 @@ __device__ __forceinline__ void attn_wide_item(const AttnArgs &a, int bx, int by
         const uint16_t *qp =
             (const uint16_t *)a.q + ((int64_t)(sv.q_row0 + srow) * a.Hq + head) * D + 8 * hi;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) qf[cb][s] = in_agprs(*(const uint4 *)(qp + 16 * s));
+        for (int s = 0; s < NS; ++s) qf[cb][s] = *(const uint4 *)(qp + 16 * s);
     }
+    if (fused && by == 0) {
+        fused_append<D, kWThreads, 0, append_pieces<D, kWThreads, kWQC>()>(
+            a, g, r0, min(r0 + BR, sv.rows) - r0, tid, true);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qf[cb][s] = in_agprs(qf[cb][s]);
 
     // ---- key range of this workgroup (and of its split part), in tiles
     const int last_row = min(r0 + BR, sv.rows) - 1;
