@@ -568,7 +568,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by KV head or by sequence with no exchange inside "
-              "attention, but this build runs and reports a single MI355X)", file=sys.stderr)
+              "attention, but this benchmark runs and reports a single MI355X)", file=sys.stderr)
         sys.exit(2)
 
     import torch
