@@ -141,6 +141,8 @@ KERNELS = {"narrow": 1, "wide": 2}
     (torch.bfloat16, 24, 8, 128, 260, 100),
     (torch.bfloat16, 12, 4, 128, 290, 97),
     (torch.bfloat16, 32, 2, 64, 200, 64),
+    (torch.float16, 16, 4, 64, 520, 128),
+    (torch.bfloat16, 32, 4, 128, 400, 256),
 ])
 def test_chunked_prefill_full_compare(kernel, dtype, Hq, Hkv, D, L, W):
     say(f"case: chunked prefill [{kernel}] {dtype} Hq={Hq} Hkv={Hkv} D={D} L={L} W={W}")
@@ -865,6 +867,13 @@ def test_workload5_mixed_full_size_budget_2048():
     steps = _run_mixed(64, 512, 16384, 20000, 2048, 32, 8, 128, seed=si.SEEDS["mixed"],
                        cap=20480, check_steps={0, 10}, every=211)
     assert steps == 11
+
+
+def test_workload5_mixed_full_size_budget_8192():
+    say("case: workload 5: 64 decodes ctx U[512,16384], 20000-token prompt, budget 8192")
+    steps = _run_mixed(64, 512, 16384, 20000, 8192, 32, 8, 128, seed=si.SEEDS["mixed"],
+                       cap=20480, check_steps={0, 2}, every=211)
+    assert steps == 3    # 8128, 8128 and 3744 prompt rows
 
 
 # ------------------------------------------------ decode rows, every variant
