@@ -48,15 +48,21 @@ PINS = {
     "attention": "pinned: torch SDPA (library), brute force with math.fsum, "
                  "closed forms (prefix means, first row, uniform, dominant)",
     "kv_append": "pinned: cache prefix invariant and byte equality with inputs",
-    "prefill_chunked": "pinned: equals one-shot (bitwise), demo split 256/256/256/232",
-    "prefill_chunk_padded": "pinned: padded real rows equal unpadded rows (bitwise)",
+    "attend_from_cache / prefill_one_shot": "pinned: torch SDPA in fp64 (library) on the "
+                 "fp32 demo and on GQA bf16 storage; planted scale, key-bound, K/V swap "
+                 "and late-append mistakes break the pin",
+    "prefill_chunked": "pinned: torch SDPA in fp64 (library), equals one-shot (bitwise), "
+                       "demo split 256/256/256/232",
+    "prefill_chunk_padded": "pinned: torch SDPA in fp64 (library); padded real rows equal "
+                            "unpadded rows (bitwise)",
     "ladder": "pinned: printed rungs {171,342,512}, 113->171, 176->342, 311->342",
     "split_chunks": "pinned: printed splits 1137 and 1200 at W=512, demo 1000/256",
     "roll_append": "pinned: torch.cat(...)[:, c:] (library)",
     "roll_prefill": "pinned: C >= L equals plain causal prefill; L > C equals "
                     "a sliding window over absolute positions",
     "plan_step": "pinned: decode-first budget rule, hand-computed step tables",
-    "varlen_step": "pinned: equals per-sequence calls; decode row equals rows=1",
+    "varlen_step": "pinned: torch SDPA with a position mask (library); equals "
+                   "per-sequence calls; decode row equals rows=1",
     "fully-masked rows": "parity unpinned (no defined result; excluded)",
 }
 

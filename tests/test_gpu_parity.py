@@ -1,8 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
 Cache contents are compared byte for byte; outputs element by element
-within the stated tolerances (fp32 max-abs 1e-5, bf16 and fp16 max-abs
-2e-2), at sizes the oracle finishes in seconds and, at the workloads' full
+within the stated tolerances (fp32 max-abs 1e-5, bf16 2e-2, fp16 8.4e-3,
+derived below), at sizes the oracle finishes in seconds and, at the workloads' full
 sizes, on sampled rows.  Bitwise self-checks of the GPU path (chunked ==
 one-shot, padded == unpadded, explicit mask == computed mask) guard the
 properties the pages state exactly.
@@ -24,7 +24,15 @@ if not torch.cuda.is_available():
 
 import chunked_prefill_causal_kv_amd as cpk  # noqa: E402
 
-TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2, torch.float16: 2e-2}
+# Output tolerances (max-abs against the fp64 oracle).  fp32: the demo's
+# allclose bound.  bf16: the stated 2e-2.  fp16 (fp32 accumulation, P and
+# the output rounded to fp16, unit roundoff u = 2^-11): the output is a
+# convex combination of V rows, so rounding it costs at most u*|o| <= u*Vmax,
+# and rounding each weight by a relative u moves the combination by at most
+# u * sum_j w_j |v_j - o| <= 2u*Vmax; with Vmax <= 5.7 (the largest |v| of
+# the fp16 inputs, 5.65 for the 4096x16x128 rolling workload) the bound is
+# 3 * 2^-11 * 5.7 = 8.4e-3.
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2, torch.float16: 8.4e-3}
 ODT = {torch.float32: oracle.F32, torch.bfloat16: oracle.BF16, torch.float16: oracle.F16}
 
 
@@ -377,8 +385,8 @@ def test_rolling_small_with_left_pad_full_compare():
     assert nl == 24
     assert np.array_equal(si.storage(gk), rk) and np.array_equal(si.storage(gv), rv)
     assert np.array_equal(si.storage(gk2), rk)
-    check(out_a[n_left:], ref[n_left:], 2e-2, "computed mask vs oracle (real rows)")
-    check(out_m[n_left:], ref[n_left:], 2e-2, "explicit mask vs oracle (real rows)")
+    check(out_a[n_left:], ref[n_left:], TOL[torch.float16], "computed mask vs oracle (real rows)")
+    check(out_m[n_left:], ref[n_left:], TOL[torch.float16], "explicit mask vs oracle (real rows)")
     assert bitwise(out_a[n_left:], out_m[n_left:]), "explicit != computed mask"
 
 
@@ -400,7 +408,7 @@ def test_rolling_split_vs_unsplit():
         out_a, _, _, _ = cpk.roll_prefill(qd, kd, vd, C, c, split=split)
         out_m, _, _, _ = cpk.roll_prefill(qd, kd, vd, C, c, masks=mk, split=split)
         torch.cuda.synchronize()
-        check(out_a[n_left:], ref[n_left:], 2e-2, f"split={split} vs oracle")
+        check(out_a[n_left:], ref[n_left:], TOL[torch.float16], f"split={split} vs oracle")
         assert bitwise(out_a[n_left:], out_m[n_left:]), f"split={split}: explicit != computed"
         outs[split] = out_a
     d = float((outs[True][n_left:].float() - outs[False][n_left:].float()).abs().max())
@@ -430,7 +438,7 @@ def test_workload4_rolling_full_size():
     vv = oracle.widen(np.ascontiguousarray(vs.transpose(1, 0, 2)), oracle.F16)
     lo = np.maximum(0, (rows // c + 1) * c - C).astype(np.int32)
     ref = oracle.attention(qq, kk, vv, lo, rows.astype(np.int32), 1.0 / math.sqrt(D))
-    check(out[torch.from_numpy(rows).cuda()], ref, 2e-2, f"sliding window ({len(rows)} rows)")
+    check(out[torch.from_numpy(rows).cuda()], ref, TOL[torch.float16], f"sliding window ({len(rows)} rows)")
 
 
 @pytest.mark.parametrize("L,C,c,H,D", [
@@ -481,7 +489,7 @@ def test_ring_matches_literal_shift(L, C, c, H, D):
     assert nl == n_left and st == start
     kview, vview = cpk.cpk_ring_view(gk.unsqueeze(0), gv.unsqueeze(0), st)
     assert np.array_equal(si.storage(kview[0]), rk) and np.array_equal(si.storage(vview[0]), rv)
-    check(out_r[n_left:], ref[n_left:], 2e-2, "ring prefill vs oracle (real rows)")
+    check(out_r[n_left:], ref[n_left:], TOL[torch.float16], "ring prefill vs oracle (real rows)")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
@@ -613,11 +621,14 @@ def _run_mixed(n_dec, ctx_lo, ctx_hi, prompt, budget, Hq, Hkv, D, seed, cap, che
     g = si.generator(seed + 4)
     done, step, lens = 0, 0, list(ctxs)
     prompt_out = torch.empty_like(pqd)
+    appended = []      # host copies of every step's decode K/V rows
     while done < prompt:
         rows = cpk.cpk_plan_step(budget, n_dec, prompt - done)
         dq = si.randn((n_dec, Hq, D), "bf16", g).cuda()
-        dk = si.randn((n_dec, Hkv, D), "bf16", g).cuda()
-        dv = si.randn((n_dec, Hkv, D), "bf16", g).cuda()
+        dk_h = si.randn((n_dec, Hkv, D), "bf16", g)
+        dv_h = si.randn((n_dec, Hkv, D), "bf16", g)
+        appended.append((si.storage(dk_h), si.storage(dv_h)))
+        dk, dv = dk_h.cuda(), dv_h.cuda()
         q = torch.cat([dq, pqd[done:done + rows]])
         kn = torch.cat([dk, pkd[done:done + rows]])
         vn = torch.cat([dv, pvd[done:done + rows]])
@@ -636,7 +647,9 @@ def _run_mixed(n_dec, ctx_lo, ctx_hi, prompt, budget, Hq, Hkv, D, seed, cap, che
                 qq = oracle.widen(si.storage(dq[s:s + 1]), oracle.BF16)
                 ref = oracle.attention(qq, kk, vv, np.zeros(1, np.int32),
                                        np.array([n - 1], np.int32), 1.0 / math.sqrt(D))
+                # the appended rows are checked before the cache feeds the oracle
                 assert np.array_equal(si.storage(cache.k[s, :, n - 1]), si.storage(dk[s]))
+                assert np.array_equal(si.storage(cache.v[s, :, n - 1]), si.storage(dv[s]))
                 err = float(np.max(np.abs(f64(out[s:s + 1]) - ref)))
                 assert err <= 2e-2, f"decode seq {s} ctx {n}: {err}"
             say(f"  step {step}: {n_dec} decode rows ok, prompt rows {done}..{done + rows}")
@@ -650,6 +663,16 @@ def _run_mixed(n_dec, ctx_lo, ctx_hi, prompt, budget, Hq, Hkv, D, seed, cap, che
     check(prompt_out[torch.from_numpy(rows_idx).cuda()], ref, 2e-2,
           f"prompt rows across {step} budgeted steps")
     assert np.array_equal(si.storage(cache.k[n_dec, :, :prompt]), ks.transpose(1, 0, 2))
+    assert np.array_equal(si.storage(cache.v[n_dec, :, :prompt]), vs.transpose(1, 0, 2))
+    # every step's decode rows (checked steps or not) sit at ctx + step
+    ck = si.storage(cache.k[:n_dec])
+    cv = si.storage(cache.v[:n_dec])
+    for i, (ak, av) in enumerate(appended):
+        pos = np.array(ctxs) + i
+        got_k = ck[np.arange(n_dec), :, pos]
+        got_v = cv[np.arange(n_dec), :, pos]
+        assert np.array_equal(got_k, ak) and np.array_equal(got_v, av), f"step {i} append"
+    assert cache.seqlens_k.cpu().tolist() == [c + step for c in ctxs] + [prompt]
     return step
 
 
@@ -728,6 +751,8 @@ def test_mixed_step_two_streams_bit_equal():
     g = si.generator(524)
     side = torch.cuda.Stream()
     done, lens, steps = 0, list(ctxs), 0
+    prompt_out = torch.empty_like(pq)
+    worst = 0.0
     while done < prompt:
         rows = cpk.cpk_plan_step(budget, n_dec, prompt - done)
         dq = si.randn((n_dec, Hq, D), "bf16", g).cuda()
@@ -743,12 +768,32 @@ def test_mixed_step_two_streams_bit_equal():
         o2 = cpk.varlen_step_overlapped(q, kn, vn, caches[1], slots, cu, past, side)
         torch.cuda.synchronize()
         assert bitwise(o1, o2), f"step {steps}: two-stream output differs"
+        prompt_out[done:done + rows] = o2[n_dec:]
+        # every decode row of the two-stream step against the oracle over
+        # its sequence's cache (whose new row is checked first)
+        for s in range(n_dec):
+            n = lens[s] + 1
+            assert np.array_equal(si.storage(caches[1].k[s, :, n - 1]), si.storage(dk[s]))
+            assert np.array_equal(si.storage(caches[1].v[s, :, n - 1]), si.storage(dv[s]))
+            kk = oracle.widen(si.storage(caches[1].k[s, :, :n]), oracle.BF16)
+            vv = oracle.widen(si.storage(caches[1].v[s, :, :n]), oracle.BF16)
+            qq = oracle.widen(si.storage(dq[s:s + 1]), oracle.BF16)
+            ref = oracle.attention(qq, kk, vv, np.zeros(1, np.int32), np.array([n - 1], np.int32),
+                                   1.0 / math.sqrt(D))
+            err = float(np.max(np.abs(f64(o2[s:s + 1]) - ref)))
+            worst = max(worst, err)
+            assert err <= TOL[torch.bfloat16], f"step {steps} decode seq {s} ctx {n}: {err}"
         lens = [x + 1 for x in lens]
         done += rows
         steps += 1
     assert bitwise(caches[0].k, caches[1].k) and bitwise(caches[0].v, caches[1].v)
     assert torch.equal(caches[0].seqlens_k, caches[1].seqlens_k)
-    say(f"  {steps} steps bit-identical")
+    say(f"  {steps} steps bit-identical; decode rows vs oracle worst {worst:.3e}")
+    qs, ks, vs = (si.storage(x.cpu()) for x in (pq, pk, pv))
+    rows_idx = sample_rows(prompt, [(0, prompt)], every=7)
+    ref = oracle_rows(qs, ks, vs, rows_idx, oracle.BF16)
+    check(prompt_out[torch.from_numpy(rows_idx).cuda()], ref, TOL[torch.bfloat16],
+          f"two-stream prompt rows across {steps} steps")
 
 
 def _to_paged(cont: "cpk.KVCache", paged: "cpk.PagedKVCache", n_pos):
@@ -803,6 +848,20 @@ def test_paged_varlen_matches_contiguous(kernel):
             o2 = cpk.cpk_paged_varlen_step(q, kn, vn, paged, slots, cu, past)
             torch.cuda.synchronize()
             assert bitwise(o1, o2), f"step {steps}: paged output differs"
+            # the paged decode rows (block-table path of the decode kernel)
+            # against the oracle over positions gathered through the table
+            for s in range(n_dec):
+                n = lens[s] + 1
+                gk, gv = paged.gather(s, n)
+                assert np.array_equal(si.storage(gk[:, n - 1]), si.storage(dk[s]))
+                assert np.array_equal(si.storage(gv[:, n - 1]), si.storage(dv[s]))
+                kk = oracle.widen(si.storage(gk), oracle.BF16)
+                vv = oracle.widen(si.storage(gv), oracle.BF16)
+                qq = oracle.widen(si.storage(dq[s:s + 1]), oracle.BF16)
+                ref = oracle.attention(qq, kk, vv, np.zeros(1, np.int32),
+                                       np.array([n - 1], np.int32), 1.0 / math.sqrt(D))
+                err = float(np.max(np.abs(f64(o2[s:s + 1]) - ref)))
+                assert err <= TOL[torch.bfloat16], f"paged step {steps} seq {s}: {err}"
             lens = [x + 1 for x in lens]
             done += rows
             steps += 1
@@ -926,7 +985,8 @@ def test_decode_rows_every_variant(dtype, D, G):
                                1.0 / math.sqrt(D))
         g64 = f64(out[s:s + 1])
         assert np.isfinite(g64).all(), f"past {p}: non-finite"
+        assert np.abs(vv).max() <= 5.7, "the fp16 tolerance assumes |v| <= 5.7"
         err = float(np.max(np.abs(g64 - ref)))
         worst = max(worst, err)
-        assert err <= 2e-2, f"past {p}: max-abs {err}"
-    say(f"  {n} decode rows: worst max-abs err {worst:.3e} (tol 2e-2)")
+        assert err <= TOL[dtype], f"past {p}: max-abs {err}"
+    say(f"  {n} decode rows: worst max-abs err {worst:.3e} (tol {TOL[dtype]:g})")

@@ -67,35 +67,93 @@ def test_demo_split_matches_printed_chunks():
     assert [r for _, r in chunks] == g["chunk_rows"]
 
 
-def test_demo_runs_as_printed_in_torch():
-    """The page's own demo, on CPU torch: four chunks, chunked == one-shot
-    within atol 1e-5."""
+def _sdpa64(q, k, v, vis=None):
+    """Library reference: torch's scaled_dot_product_attention in fp64 on
+    token-major arrays q [n_q, Hq, D] and k/v [n_k, Hkv, D] (numpy or torch),
+    KV heads repeated to the query heads in contiguous groups.  vis is an
+    optional [n_q, n_k] boolean visibility; without it the rows are the
+    causal one-shot rows 0..n_q-1 over keys 0..n_k-1."""
+    q, k, v = (torch.as_tensor(x).double() for x in (q, k, v))
+    G = q.shape[1] // k.shape[1]
+    tq = q.permute(1, 0, 2)[None]
+    tk = k.permute(1, 0, 2)[None].repeat_interleave(G, dim=1)
+    tv = v.permute(1, 0, 2)[None].repeat_interleave(G, dim=1)
+    if vis is None:
+        out = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    else:
+        out = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.as_tensor(vis))
+    return out[0].permute(1, 0, 2).numpy()
+
+
+def test_oracle_entry_points_match_sdpa_on_demo():
+    """Library pin of the oracle's own cache-driven entry points on the
+    glossary demo (fp32, 8 heads x 64, 1000 tokens, chunk 256): one-shot
+    prefill and chunked prefill, each appending into a Cache and attending
+    from it, equal torch's causal SDPA in fp64 to rounding and the demo's
+    own fp32 SDPA within the page's 1e-5; the chunk split is the printed
+    256/256/256/232."""
     g = GOLD["demo_split"]
-    (q, k, v), _ = si.demo_qkv()
-    full = F.scaled_dot_product_attention(q, k, v, is_causal=True)
-    outs = []
-    L, W = g["prompt_len"], g["chunk"]
-    for start in range(0, L, W):
-        end = min(start + W, L)
-        mask = torch.ones(end - start, end, dtype=torch.bool).tril(diagonal=start)
-        outs.append(F.scaled_dot_product_attention(q[..., start:end, :], k[..., :end, :],
-                                                   v[..., :end, :], attn_mask=mask))
-    chunked = torch.cat(outs, dim=2)
-    assert len(outs) == g["n_chunks"]
-    assert torch.allclose(full, chunked, atol=g["allclose_atol"]) == g["chunked_equals_one_shot"]
+    (q4, k4, v4), (qt, kt, vt) = si.demo_qkv()
+    q, k, v = (si.storage(x) for x in (qt, kt, vt))
+    ref64 = _sdpa64(qt, kt, vt)
+    ref32 = F.scaled_dot_product_attention(q4, k4, v4, is_causal=True)[0].permute(1, 0, 2)
+    ref32 = ref32.double().numpy()
+    one = oracle.prefill_one_shot(oracle.Cache(oracle.F32, 1, 8, 1024, 64), 0, q, k, v)
+    chunked, chunks = oracle.prefill_chunked(oracle.Cache(oracle.F32, 1, 8, 1024, 64), 0,
+                                             q, k, v, g["chunk"])
+    assert len(chunks) == g["n_chunks"]
+    assert [r for _, r in chunks] == g["chunk_rows"]
+    for got in (one, chunked):
+        assert np.max(np.abs(got - ref64)) < 1e-12
+        assert np.max(np.abs(got - ref32)) < g["allclose_atol"]
 
 
-def test_oracle_matches_sdpa_on_demo():
-    """Library pin: the oracle's one-shot result on the demo equals torch's
-    causal SDPA in fp64 to rounding, and the demo's fp32 SDPA within the
-    page's 1e-5."""
-    (q, k, v), (qt, kt, vt) = si.demo_qkv()
-    orc = _causal_oracle(qt.double().numpy(), kt.double().numpy(), vt.double().numpy())
-    ref64 = F.scaled_dot_product_attention(q.double(), k.double(), v.double(), is_causal=True)
-    ref64 = ref64[0].permute(1, 0, 2).numpy()
-    assert np.max(np.abs(orc - ref64)) < 1e-12
-    ref32 = F.scaled_dot_product_attention(q, k, v, is_causal=True)[0].permute(1, 0, 2).double().numpy()
-    assert np.max(np.abs(orc - ref32)) < 1e-5
+@pytest.mark.parametrize("W", [64, 100, 128])
+def test_oracle_cache_path_gqa_bf16_matches_sdpa(W):
+    """Library pin of the cache path on GQA bf16 storage (8 query heads over
+    2 KV heads, head dim 64, 300 tokens): one-shot, chunked and padded
+    chunked prefill read K/V back from the oracle's bf16 cache; each equals
+    fp64 SDPA over K/V repeated per group (widened by torch, not by the
+    oracle) to rounding."""
+    qt, kt, vt = si.gqa_prompt(L=300, Hq=8, Hkv=2, D=64, seed=23)
+    q, k, v = (si.storage(x) for x in (qt, kt, vt))
+    ref = _sdpa64(qt, kt, vt)
+    outs = [oracle.prefill_one_shot(oracle.Cache(oracle.BF16, 2, 2, 512, 64), 1, q, k, v)]
+    outs.append(oracle.prefill_chunked(oracle.Cache(oracle.BF16, 2, 2, 512, 64), 1,
+                                       q, k, v, W)[0])
+    outs.append(oracle.prefill_chunked_padded(oracle.Cache(oracle.BF16, 2, 2, 512, 64), 1,
+                                              q, k, v, W)[0])
+    for got in outs:
+        assert got.shape == ref.shape
+        assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_oracle_varlen_step_matches_sdpa_with_position_mask():
+    """Library pin of the packed step: two decode rows (contexts 37 and 5)
+    and a 70-row prompt chunk at past 30, each sequence's rows against fp64
+    SDPA with a boolean mask built from absolute positions (key j visible
+    to row i when j <= past + i)."""
+    Hq, Hkv, D = 4, 2, 32
+    gen = si.generator(24)
+    ctx = {0: 37, 1: 5, 2: 30}
+    rows = {0: 1, 1: 1, 2: 70}
+    full = {s: tuple(si.randn((ctx[s] + rows[s], h, D), "bf16", gen) for h in (Hq, Hkv, Hkv))
+            for s in ctx}
+    cache = oracle.Cache(oracle.BF16, 3, Hkv, 128, D)
+    for s in ctx:
+        _, kf, vf = full[s]
+        if ctx[s]:
+            cache.append(s, si.storage(kf[:ctx[s]]), si.storage(vf[:ctx[s]]), 0)
+    pack = [torch.cat([full[s][i][ctx[s]:] for s in ctx]) for i in range(3)]
+    cu = np.cumsum([0] + [rows[s] for s in ctx])
+    outs = oracle.varlen_step(cache, [(s, ctx[s]) for s in ctx],
+                              *(si.storage(x) for x in pack), cu)
+    for s in ctx:
+        qf, kf, vf = full[s]
+        n = ctx[s] + rows[s]
+        vis = (np.arange(n)[None, :] <= ctx[s] + np.arange(rows[s])[:, None])
+        ref = _sdpa64(qf[ctx[s]:], kf, vf, vis)
+        assert np.max(np.abs(outs[s] - ref)) < 1e-12
 
 
 def test_oracle_chunked_equals_one_shot_demo_bitwise():
@@ -382,6 +440,8 @@ def test_rolling_with_room_equals_plain_causal_prefill():
     ref = _causal_oracle(oracle.widen(q, oracle.F16), oracle.widen(k, oracle.F16),
                          oracle.widen(v, oracle.F16))
     assert np.array_equal(out[n_left:], ref)
+    qt, kt, vt = si.rolling_inputs(L=200, H=2, D=16, seed=32)
+    assert np.max(np.abs(out[n_left:] - _sdpa64(qt, kt, vt))) < 1e-12
 
 
 def test_rolling_past_capacity_is_a_sliding_window():
@@ -398,6 +458,11 @@ def test_rolling_past_capacity_is_a_sliding_window():
     lo = np.maximum(0, (p // c + 1) * c - C).astype(np.int32)
     ref = oracle.attention(qd, kk, vv, lo, p.astype(np.int32), oracle.default_scale(D))
     assert np.max(np.abs(out - ref)) < 1e-14
+    # the same window as a boolean mask for torch's SDPA (library pin)
+    qt, kt, vt = si.rolling_inputs(L=L, H=H, D=D, seed=33)
+    a = np.arange(L)[None, :]
+    vis = (a <= p[:, None]) & (a >= lo[:, None])
+    assert np.max(np.abs(out - _sdpa64(qt, kt, vt, vis))) < 1e-12
     # the final cache holds the last C positions, right-aligned
     assert np.array_equal(kc, k[L - C:].transpose(1, 0, 2))
 
@@ -536,3 +601,55 @@ def test_planted_wrong_roll_slice_is_caught():
     wrong = torch.cat([t_old, t_new], dim=2)[:, :, :C][0].numpy().astype(np.uint16)
     assert not np.array_equal(wrong, ref)
     assert np.array_equal(oracle.roll_append(old, chunk, oracle.F16), ref)
+
+
+# planted mistakes in the cache-driven entry points (the reference the GPU
+# tests compare against): each must break the SDPA pin
+
+def _entry_point_error():
+    qt, kt, vt = si.gqa_prompt(L=96, Hq=4, Hkv=2, D=32, seed=25)
+    q, k, v = (si.storage(x) for x in (qt, kt, vt))
+    ref = _sdpa64(qt, kt, vt)
+    outs = [oracle.prefill_one_shot(oracle.Cache(oracle.BF16, 1, 2, 128, 32), 0, q, k, v),
+            oracle.prefill_chunked(oracle.Cache(oracle.BF16, 1, 2, 128, 32), 0, q, k, v, 40)[0]]
+    return max(float(np.nanmax(np.abs(o - ref))) if not np.isnan(o).any() else np.inf
+               for o in outs)
+
+
+def test_entry_point_pin_is_clean():
+    assert _entry_point_error() < 1e-12
+
+
+def test_planted_cache_path_scale_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "default_scale", lambda D: 1.0 / D)
+    assert _entry_point_error() > 1e-5
+
+
+@pytest.mark.parametrize("shift", [-1, 1])
+def test_planted_cache_path_key_bound_is_caught(monkeypatch, shift):
+    real = oracle.attention
+
+    def shifted(q, k, v, lo, hi, scale, addmask=None):
+        hi = np.clip(np.asarray(hi) + shift, 0, k.shape[1] - 1).astype(np.int32)
+        return real(q, k, v, lo, hi, scale, addmask)
+
+    monkeypatch.setattr(oracle, "attention", shifted)
+    assert _entry_point_error() > 1e-5
+
+
+def test_planted_cache_append_swapping_k_and_v_is_caught(monkeypatch):
+    real = oracle.Cache.append
+    monkeypatch.setattr(oracle.Cache, "append",
+                        lambda self, b, k, v, past: real(self, b, v, k, past))
+    assert _entry_point_error() > 1e-5
+
+
+def test_planted_cache_append_one_row_late_is_caught(monkeypatch):
+    real = oracle.Cache.append
+
+    def late(self, b, k, v, past):
+        real(self, b, k, v, past + 1)
+        self.lens[b] = past + k.shape[0]
+
+    monkeypatch.setattr(oracle.Cache, "append", late)
+    assert _entry_point_error() > 1e-5
