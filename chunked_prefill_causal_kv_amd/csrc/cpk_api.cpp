@@ -103,15 +103,19 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 
 std::atomic<int> g_attn_kernel{CPK_ATTN_AUTO};
 
-// Whether the 128-column kernel serves a bf16/fp16 chunk or varlen
-// attention launch of `rows` rows (the longest sequence's, in varlen).
-bool use_wide(int dtype, int group, int kv_heads, int rows)
+// The kernel serving a bf16/fp16 chunk or varlen attention launch of `rows`
+// rows (the longest sequence's, in varlen): the 128-column kernel once its
+// grid fills the CUs, else the 64-column one (unless overridden).
+int pick_kernel(int dtype, int group, int kv_heads, int rows)
 {
-    if (dtype == CPK_F32) return false;
+    if (dtype == CPK_F32) return cpk::kAttnNarrow;
     const int k = g_attn_kernel.load(std::memory_order_relaxed);
-    if (k != CPK_ATTN_AUTO) return k == CPK_ATTN_WIDE;
+    if (k == CPK_ATTN_WIDE) return cpk::kAttnWide;
+    if (k == CPK_ATTN_NARROW) return cpk::kAttnNarrow;
+    if (k == CPK_ATTN_NARROW_GENERAL) return cpk::kAttnNarrowGeneral;
     const int br = cpk::attn_rows_per_block(dtype, group, true);
-    return (int64_t)((rows + br - 1) / br) * kv_heads >= cpk::kWideMinGroups;
+    return (int64_t)((rows + br - 1) / br) * kv_heads >= cpk::kWideMinGroups ? cpk::kAttnWide
+                                                                              : cpk::kAttnNarrow;
 }
 
 }  // namespace
@@ -122,7 +126,8 @@ int cpk_version(void) { return 102; }
 
 int cpk_set_attention_kernel(int kind)
 {
-    if (kind != CPK_ATTN_AUTO && kind != CPK_ATTN_NARROW && kind != CPK_ATTN_WIDE)
+    if (kind != CPK_ATTN_AUTO && kind != CPK_ATTN_NARROW && kind != CPK_ATTN_WIDE &&
+        kind != CPK_ATTN_NARROW_GENERAL)
         return fail(CPK_EINVAL, "set_attention_kernel: unknown kind %d", kind);
     return g_attn_kernel.exchange(kind);
 }
@@ -240,9 +245,10 @@ static int attention_common(const void *q, const cpk_kv_cache *cache, int b, int
         a.k_new = k_new; a.v_new = v_new; a.new_base = past_len; a.new_rows = real_rows;
         a.seqlens = cache->seqlens_k; a.len_after = past_len + real_rows;
     }
-    const bool wide = use_wide(cache->dtype, q_heads / cache->kv_heads, cache->kv_heads, rows);
-    const int br = cpk::attn_rows_per_block(cache->dtype, q_heads / cache->kv_heads, wide);
-    return hip_status(cpk::launch_attention(a, cache->dtype, (rows + br - 1) / br, 1, wide, st),
+    const int kern = pick_kernel(cache->dtype, q_heads / cache->kv_heads, cache->kv_heads, rows);
+    const int br = cpk::attn_rows_per_block(cache->dtype, q_heads / cache->kv_heads,
+                                            kern == cpk::kAttnWide);
+    return hip_status(cpk::launch_attention(a, cache->dtype, (rows + br - 1) / br, 1, kern, st),
                       "attention launch");
 }
 
@@ -507,10 +513,10 @@ static int varlen_impl(const void *q, const void *k_new, const void *v_new,
             a.block_table = pg->table; a.max_blocks = pg->max_blocks;
             a.block_size = pg->block_size; a.n_blocks = pg->n_blocks;
         }
-        const bool wide = use_wide(cache->dtype, G, cache->kv_heads, max_rows);
-        const int br = cpk::attn_rows_per_block(cache->dtype, G, wide);
+        const int kern = pick_kernel(cache->dtype, G, cache->kv_heads, max_rows);
+        const int br = cpk::attn_rows_per_block(cache->dtype, G, kern == cpk::kAttnWide);
         r = hip_status(cpk::launch_attention(a, cache->dtype, (max_rows + br - 1) / br,
-                                             pre_hi - pre_lo, wide, st),
+                                             pre_hi - pre_lo, kern, st),
                        "varlen prefill");
         if (r) return r;
     }
@@ -644,7 +650,7 @@ static int roll_attention_impl(const void *q, const void *k, const void *v, cons
     }
     const int br = cpk::attn_rows_per_block(dtype, Hq / Hkv, false);
     r = hip_status(
-        cpk::launch_attention(a, dtype, (c + br - 1) / br, 1, false, (hipStream_t)stream),
+        cpk::launch_attention(a, dtype, (c + br - 1) / br, 1, cpk::kAttnNarrow, (hipStream_t)stream),
         "roll_attention launch");
     if (r || parts <= 1) return r;
     return hip_status(cpk::launch_attention_combine(a, dtype, (hipStream_t)stream),

@@ -149,8 +149,13 @@ hipError_t launch_ring_view(const void *k_ring, const void *v_ring, void *k_out,
 // takes the explicit additive mask, so both of its forms stay bit-equal).
 constexpr int kWideMinGroups = 256;   // auto choice: wide once its grid fills the CUs
 int attn_rows_per_block(int dtype, int group, bool wide);
+// bf16/fp16 kernel of a launch: the 64-column kernel (its latency-scheduled
+// form wherever the call has no additive mask, ring buffer, paging or key
+// split), the 128-column kernel, or the 64-column kernel's general form
+// everywhere (diagnostics)
+enum AttnKernel { kAttnNarrow = 0, kAttnWide = 1, kAttnNarrowGeneral = 2 };
 hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
-                            bool wide, hipStream_t st);
+                            int kernel, hipStream_t st);
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int max_segs, hipStream_t st);
 

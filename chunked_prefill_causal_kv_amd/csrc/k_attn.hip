@@ -1303,6 +1303,358 @@ void attn_wide_kernel(AttnArgs a)
     attn_wide_item<TR, D, PAGED>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
+// ------------------------------------------------------- scheduled kernel
+//
+// attn_sched_kernel: the 64-column kernel's work split (8 waves = 2 column
+// groups x 4 key slices of 128-key tiles, tiles double-buffered in LDS) for
+// the plain causal form only (no additive mask, ring buffer, paging or key
+// split), scheduled for latency:
+// * all eight K fragment reads of a tile are issued before its first
+//   matrix instruction, so the QK^T chain is not broken by LDS round trips;
+// * the V^T fragments of the tile are read right after the QK^T
+//   instructions, so those reads complete while the vector unit runs the
+//   softmax (whose cross-half exchange is a register permute, not an LDS
+//   operation that would have to wait for them);
+// * P V accumulates into four independent register blocks per k-step, so
+//   consecutive matrix instructions do not depend on each other;
+// * tiles that lie entirely inside the chunk's new rows (fused append) are
+//   loaded with per-lane offsets precomputed for the new rows' stride,
+//   without per-row source selection.
+// Arithmetic, fragment layouts, swizzles, the lazy maximum, the epilogue
+// merge and the fused append are those of attn_mfma_kernel, so results are
+// bit-identical to it.
+template <typename TR, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_sched_kernel(AttnArgs a)
+{
+    using TL = Tile<D>;
+    constexpr int NCH = TL::NCH;
+    constexpr int NS = D / 16;      // k-steps of the QK^T contraction
+    constexpr int NDB = D / 32;     // 32-wide d blocks of O^T
+
+    __shared__ __attribute__((aligned(16))) uint16_t buf0[TL::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t buf1[TL::STAGE];
+    __shared__ float ml[2 * 4 * kQC];
+
+    SeqView sv;
+    if (!resolve_seq(a, blockIdx.z, sv)) return;
+    const int G = a.Hq / a.Hkv;
+    const int BR = kQC / G;                 // rows per workgroup
+    const int g = blockIdx.x % a.Hkv;       // KV head fastest: one KV head per XCD
+    const int r0 = (blockIdx.x / a.Hkv) * BR;
+    if (r0 >= sv.rows) return;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c32 = lane & 31;
+    const int hi = lane >> 5;
+    const int qg = wave >> 2;               // query-column group
+    const int ks = wave & 3;                // key slice of every tile
+    const int qc = qg * 32 + c32;
+
+    const uint16_t *kc = (const uint16_t *)a.k + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
+    const uint16_t *vc = (const uint16_t *)a.v + ((int64_t)sv.slot * a.Hkv + g) * a.cap * D;
+    const bool fused = a.k_new != nullptr;
+    const int new_lo = fused ? a.new_base : INT_MAX;
+    // new rows usable without clamping: keys [new_base, new_hi)
+    const int new_hi = fused ? min(sv.n_keys, a.new_base + a.new_rows) : INT_MIN;
+    const bool app_on = fused && blockIdx.y == 0;
+    const int app_rows = min(r0 + BR, sv.rows) - r0;
+    u32x4_t app[1];
+    if (app_on) {
+        append_load<D, kThreads, 0, 1>(a, g, r0, app_rows, tid, app);
+        fused_append<D, kThreads, 1, append_pieces<D, kThreads, kQC>()>(a, g, r0, app_rows, tid,
+                                                                        false);
+    }
+
+    // ---- query fragment (B operand of S^T = K Q^T): column qc
+    uint4 qf[NS];
+    int lim;
+    {
+        const int row = r0 + qc / G;
+        const bool ok = (qc < BR * G) && (row < sv.rows);
+        const int rr = ok ? row : r0;
+        const int srow = rr < sv.q_src_rows ? rr : sv.q_src_rows - 1;
+        const int head = g * G + (ok ? qc % G : 0);
+        lim = min(sv.causal_base + rr, sv.n_keys - 1);
+        const uint16_t *qp =
+            (const uint16_t *)a.q + ((int64_t)(sv.q_row0 + srow) * a.Hq + head) * D + 8 * hi;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qf[s] = *(const uint4 *)(qp + 16 * s);
+    }
+
+    const int last_row = min(r0 + BR, sv.rows) - 1;
+    const int key_end = min(sv.n_keys, sv.causal_base + last_row + 1);   // exclusive
+    const int t_first = sv.key_lo / kBK;
+    const int t_last = (key_end - 1) / kBK;
+
+    // ---- tile loads: load i of this wave fills LDS chunks
+    // [(i*WAVES + wave)*64, +64), one 16-byte chunk per lane: tile row
+    // i*RSTEP + row0 (RSTEP = WAVES*64/NCH rows apart), chunk pos.  The
+    // swizzles depend on the row modulo NCH, which RSTEP leaves unchanged,
+    // so one per-lane offset serves every load of the tile and load i adds
+    // a uniform i*RSTEP rows to the (scalar) base: byte offsets for cache
+    // rows (stride D) and for the new rows (stride Hkv*D).
+    constexpr int RSTEP = TL::WAVES * 64 / NCH;
+    static_assert(RSTEP % NCH == 0, "row step keeps the swizzle");
+    const int row0 = (wave * 64 + lane) / NCH;
+    const int pos0 = lane % NCH;
+    const uint32_t kch = (uint32_t)((pos0 ^ TL::swz_k(row0)) * 8);
+    const uint32_t vch = (uint32_t)((pos0 ^ TL::swz_v(row0)) * 8);
+    const uint32_t koff = ((uint32_t)row0 * D + kch) * 2u;
+    const uint32_t voff = ((uint32_t)row0 * D + vch) * 2u;
+    const uint32_t nkoff = ((uint32_t)row0 * a.Hkv * D + kch) * 2u;
+    const uint32_t nvoff = ((uint32_t)row0 * a.Hkv * D + vch) * 2u;
+    auto load16 = [](const char *src, uint16_t *dst) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    };
+    auto issue_tile = [&](int kt, uint16_t *Kb) {
+        uint16_t *Vb = Kb + kBK * D;
+        const int key0 = kt * kBK;
+        if (key0 + kBK <= sv.n_keys && key0 + kBK <= new_lo) {
+            // cache rows
+#pragma unroll
+            for (int i = 0; i < TL::LOADS; ++i) {
+                const int blk = i * TL::WAVES + wave;
+                const int64_t e = (int64_t)(key0 + i * RSTEP) * D;
+                load16((const char *)(kc + e) + koff, Kb + blk * 64 * 8);
+                load16((const char *)(vc + e) + voff, Vb + blk * 64 * 8);
+            }
+        } else if (key0 >= new_lo && key0 + kBK <= new_hi) {
+            // new rows of the chunk (fused append), no clamping needed
+#pragma unroll
+            for (int i = 0; i < TL::LOADS; ++i) {
+                const int blk = i * TL::WAVES + wave;
+                const int64_t e = ((int64_t)(key0 - a.new_base + i * RSTEP) * a.Hkv + g) * D;
+                load16((const char *)((const uint16_t *)a.k_new + e) + nkoff, Kb + blk * 64 * 8);
+                load16((const char *)((const uint16_t *)a.v_new + e) + nvoff, Vb + blk * 64 * 8);
+            }
+        } else {
+            // per-row sources: rows past the last valid key re-read it;
+            // keys at or past new_base come from the new rows (fused)
+#pragma unroll
+            for (int i = 0; i < TL::LOADS; ++i) {
+                const int blk = i * TL::WAVES + wave;
+                const int key = min(key0 + i * RSTEP + row0, sv.n_keys - 1);
+                const char *ks_, *vs_;
+                if (key >= new_lo) {
+                    const int64_t e = ((int64_t)min(key - a.new_base, a.new_rows - 1) * a.Hkv + g) * D;
+                    ks_ = (const char *)((const uint16_t *)a.k_new + e + kch);
+                    vs_ = (const char *)((const uint16_t *)a.v_new + e + vch);
+                } else {
+                    ks_ = (const char *)(kc + (int64_t)key * D + kch);
+                    vs_ = (const char *)(vc + (int64_t)key * D + vch);
+                }
+                load16(ks_, Kb + blk * 64 * 8);
+                load16(vs_, Vb + blk * 64 * 8);
+            }
+        }
+    };
+
+    f32x16_t oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    const float c = a.scale_log2;
+
+    const int g16 = (lane >> 4) & 1;
+    const int si = lane & 15;
+    const int vrow_off = ks * 32 + 4 * hi + (si >> 2);   // + 16*s2 + 8*j2
+    const int vcol = 16 * g16 + 4 * (si & 3);            // + 32*db
+    const int krow = ks * 32 + c32;
+
+    auto tile_step = [&](int kt, const uint16_t *Kb, uint16_t *next) {
+        __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of tile kt have landed
+        __syncthreads();                   // ... and every wave's; `next` is free again
+        if (kt == t_first && app_on)
+            append_store<D, kThreads, 0, 1>(a, g, r0, app_rows, tid, app, true);
+        if (kt < t_last) issue_tile(kt + 1, next);
+        const uint16_t *Vb = Kb + kBK * D;
+
+        // S^T[32 keys x 32 cols]: every K fragment read, then the chain
+        __builtin_amdgcn_s_setprio(1);
+        uint4 kf[NS];
+        {
+            const uint16_t *kr = Kb + krow * D;
+            const int sk = TL::swz_k(krow);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) kf[s] = *(const uint4 *)(kr + ((2 * s + hi) ^ sk) * 8);
+        }
+        f32x16_t sacc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) sacc = TR::mfma(kf[s], qf[s], sacc);
+        // V^T fragments of this wave's 32 keys, in flight during the softmax
+        uint4 vf[NDB][2];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                uint2 half[2];
+#pragma unroll
+                for (int j2 = 0; j2 < 2; ++j2) {
+                    const int vrow = vrow_off + 16 * s2 + 8 * j2;
+                    const int dd = 32 * db + vcol;
+                    const uint16_t *vp =
+                        Vb + vrow * D + (((dd >> 3) ^ TL::swz_v(vrow)) << 3) + (dd & 7);
+                    const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)vp);
+                    half[j2] = __builtin_bit_cast(uint2, r);
+                }
+                vf[db][s2] = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
+            }
+        // issue order: the K fragment reads, then each matrix instruction
+        // followed by two of the V^T fragment reads
+        __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDB / NS, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // register j of lane (c32, hi): key kbase + 8*(j/4) + 4*hi + (j%4)
+        const int kbase = kt * kBK + ks * 32;
+        const bool full = (kt * kBK >= sv.key_lo) && ((kt + 1) * kBK <= sv.n_keys) &&
+                          ((kt + 1) * kBK - 1 <= sv.causal_base + r0);
+        if (!full) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
+                sacc[j] = (key >= sv.key_lo && key <= lim) ? sacc[j] : -INFINITY;
+            }
+        }
+        float mx = sacc[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[j]);
+        mx = half_max(mx);
+        const float mt = mx * c;
+        const bool need = mt > m_run + kLazyLog2;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            const float alpha = need ? exp2f(m_run - mt) : 1.0f;
+            m_run = need ? mt : m_run;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+        }
+        const float mu = m_run == -INFINITY ? 0.f : m_run;
+        uint4 pb[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * s2 + 2 * i], c, -mu));
+                const float p1 =
+                    __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * s2 + 2 * i + 1], c, -mu));
+                w[i] = TR::pack(p0, p1);
+                l_run = TR::dot2(w[i], TR::kOnes, l_run);
+            }
+            pb[s2] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // O^T[d x cols] += V^T[d x 32 keys] P^T[32 keys x cols]
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] = TR::mfma(vf[db][s2], pb[s2], oacc[db]);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    if (t_last >= t_first) {
+        issue_tile(t_first, buf0);
+        for (int kt = t_first; kt <= t_last; kt += 2) {
+            tile_step(kt, buf0, buf1);
+            if (kt + 1 <= t_last) tile_step(kt + 1, buf1, buf0);
+        }
+    } else if (app_on) {
+        append_store<D, kThreads, 0, 1>(a, g, r0, app_rows, tid, app, true);
+    }
+    __syncthreads();   // all waves are done with the tiles: reuse LDS below
+
+    // ---- merge the four key slices' partial states, normalise, write rows
+    float *Ms = ml;
+    float *Ls = ml + 4 * kQC;
+    auto orow = [&](int slice, int col) -> float * {
+        float *base = (float *)(slice < 2 ? buf0 : buf1);
+        return base + ((slice & 1) * kQC + col) * D;
+    };
+    {
+        const float lt = half_sum(l_run);
+        if (hi == 0) {
+            Ms[ks * kQC + qc] = m_run;
+            Ls[ks * kQC + qc] = lt;
+        }
+    }
+    __syncthreads();
+    {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, Ms[w * kQC + qc]);
+        float den = 0.f, mine = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float mw = Ms[w * kQC + qc];
+            const float e = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+            den += e * Ls[w * kQC + qc];
+            if (w == ks) mine = e;
+        }
+        const float f = den > 0.f ? mine / den : 0.f;
+        float *dst = orow(ks, qc);
+        const int sw = TL::swz_o(qc);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const int d4 = db * 8 + 2 * j4 + hi;
+                float4 v4 = make_float4(oacc[db][4 * j4] * f, oacc[db][4 * j4 + 1] * f,
+                                        oacc[db][4 * j4 + 2] * f, oacc[db][4 * j4 + 3] * f);
+                *(float4 *)(dst + 4 * (d4 ^ sw)) = v4;
+            }
+    }
+    __syncthreads();
+    {
+        constexpr int PARTS = kThreads / kQC;
+        constexpr int DP = D / PARTS;
+        const int oc = tid / PARTS;
+        const int part = tid % PARTS;
+        const int row = r0 + oc / G;
+        if (oc < BR * G && row < sv.out_rows) {
+            const int head = g * G + oc % G;
+            uint16_t *op = (uint16_t *)a.out + ((int64_t)(sv.out_row0 + row) * a.Hq + head) * D +
+                           part * DP;
+            const int sw = TL::swz_o(oc);
+#pragma unroll
+            for (int d8 = 0; d8 < DP; d8 += 8) {
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x0 = 0.f, x1 = 0.f;
+                    const int d = part * DP + d8 + 2 * i;
+                    const int off = 4 * ((d >> 2) ^ sw) + (d & 3);
+#pragma unroll
+                    for (int w4 = 0; w4 < 4; ++w4) {
+                        const float *src = orow(w4, oc);
+                        x0 += src[off];
+                        x1 += src[off + 1];
+                    }
+                    w[i] = TR::pack(x0, x1);
+                }
+                *(uint4 *)(op + d8) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    }
+}
+
 // Merge of the split parts of a key range: for each (row, query head), in
 // part order, M = max_p M_p, f_p = 2^(M_p - M), out = sum_p f_p O_p /
 // sum_p f_p den_p.  Each thread produces 8 consecutive outputs of one
@@ -1482,16 +1834,26 @@ int attn_rows_per_block(int dtype, int group, bool wide)
     } while (0)
 
 hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
-                            bool wide, hipStream_t st)
+                            int kernel, hipStream_t st)
 {
     const dim3 grid(row_blocks * a.Hkv, a.n_parts > 1 ? a.n_parts : 1, n_seq_grid);
-    if (wide && dtype != 0) {
+    // the scheduled form covers the plain causal launch
+    const bool plain = !a.mask && a.ring_start == 0 && a.block_size == 0 && a.n_parts <= 1;
+    if (kernel == kAttnWide && dtype != 0) {
         CPK_LAUNCH_MFMA(attn_wide_kernel, kWThreads);
     } else if (dtype == 0) {
         if (a.D == 64)
             hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, st, a);
         else
             hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, st, a);
+    } else if (kernel == kAttnNarrow && plain) {
+        if (dtype == 1) {
+            if (a.D == 64) hipLaunchKernelGGL((attn_sched_kernel<F16, 64>), grid, dim3(kThreads), 0, st, a);
+            else hipLaunchKernelGGL((attn_sched_kernel<F16, 128>), grid, dim3(kThreads), 0, st, a);
+        } else {
+            if (a.D == 64) hipLaunchKernelGGL((attn_sched_kernel<Bf16, 64>), grid, dim3(kThreads), 0, st, a);
+            else hipLaunchKernelGGL((attn_sched_kernel<Bf16, 128>), grid, dim3(kThreads), 0, st, a);
+        }
     } else {
         CPK_LAUNCH_MFMA(attn_mfma_kernel, kThreads);
     }

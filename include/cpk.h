@@ -65,6 +65,8 @@ enum cpk_attention_kernel {
     CPK_ATTN_AUTO = 0,     /* by launch size (the default)                  */
     CPK_ATTN_NARROW = 1,   /* 64 query columns per workgroup, 8 waves       */
     CPK_ATTN_WIDE = 2,     /* 128 query columns per workgroup, 4 waves      */
+    CPK_ATTN_NARROW_GENERAL = 3, /* the 64-column kernel's general form even
+                                    where its latency-scheduled form applies */
 };
 
 /*
@@ -428,8 +430,12 @@ int cpk_version(void);
  * gives a row the same bits whether its prompt runs in one pass or in
  * chunks.  CPK_ATTN_AUTO takes the wide kernel when its launch has at
  * least as many workgroups as the GPU has compute units (256), else the
- * narrow one.  The setting is process-wide and meant for diagnostics and
- * tests; it returns the previous setting, or CPK_EINVAL for an unknown kind.
+ * narrow one.  The narrow kernel runs in a latency-scheduled form wherever
+ * the launch is the plain causal one (no additive mask, ring buffer, paging
+ * or key split) and in its general form otherwise; the two forms give
+ * identical bits, and CPK_ATTN_NARROW_GENERAL forces the general form.  The
+ * setting is process-wide and meant for diagnostics and tests; it returns
+ * the previous setting, or CPK_EINVAL for an unknown kind.
  */
 int cpk_set_attention_kernel(int kind);
 

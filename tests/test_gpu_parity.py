@@ -137,10 +137,47 @@ def test_fp32_demo_chunked_and_one_shot():
 
 # ----------------------------------------------- GQA shapes, full compare
 
-KERNELS = {"narrow": 1, "wide": 2}
+# narrow: the 64-column kernel (its latency-scheduled form wherever the launch
+# is plain causal), wide: the 128-column kernel, general: the 64-column
+# kernel's general form everywhere
+KERNELS = {"narrow": 1, "wide": 2, "general": 3}
 
 
-@pytest.mark.parametrize("kernel", ["narrow", "wide"])
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,past,real,W,pad", [
+    (torch.bfloat16, 32, 8, 128, 3584, 416, 512, True),    # workload 2's last chunk
+    (torch.bfloat16, 32, 8, 128, 0, 512, 512, True),       # its first chunk
+    (torch.float16, 8, 2, 64, 300, 77, 128, True),
+    (torch.bfloat16, 12, 4, 128, 129, 200, 256, False),    # tiles straddle the new rows
+    (torch.bfloat16, 16, 16, 128, 64, 1, 171, True),
+])
+def test_scheduled_form_bit_equal_to_general(dtype, Hq, Hkv, D, past, real, W, pad):
+    """The latency-scheduled form of the 64-column kernel gives the general
+    form's bits: outputs, every cache byte written (padded rows included)
+    and seqlens_k, for one fused prefill chunk after a cached prefix."""
+    dn = {torch.bfloat16: "bf16", torch.float16: "f16"}[dtype]
+    say(f"case: scheduled vs general {dn} heads {Hq}/{Hkv} D={D} past={past} real={real} W={W}")
+    g = si.generator(610 + past + real)
+    pre = [si.randn((past, Hkv, D), dn, g).cuda() for _ in range(2)]
+    q, k, v = (si.randn((real, h, D), dn, g).cuda() for h in (Hq, Hkv, Hkv))
+    res = []
+    for kind in ("general", "narrow"):
+        cache = cpk.KVCache(1, Hkv, past + W + 8, D, dtype)
+        poison(cache)
+        if past:
+            cpk.cpk_kv_append(cache, 0, pre[0], pre[1], 0)
+        with cpk.attention_kernel(KERNELS[kind]):
+            out, width = cpk.cpk_prefill_chunk(q, k, v, cache, 0, past, W, pad=pad)
+        torch.cuda.synchronize()
+        res.append((out, width, cache))
+    (o1, w1, c1), (o2, w2, c2) = res
+    assert w1 == w2
+    assert bitwise(o1, o2), "outputs differ"
+    n = past + w1
+    assert bitwise(c1.k[:, :, :n], c2.k[:, :, :n]) and bitwise(c1.v[:, :, :n], c2.v[:, :, :n])
+    assert torch.equal(c1.seqlens_k, c2.seqlens_k)
+
+
+@pytest.mark.parametrize("kernel", ["narrow", "wide", "general"])
 @pytest.mark.parametrize("dtype,Hq,Hkv,D,L,W", [
     (torch.bfloat16, 8, 2, 128, 700, 256),
     (torch.bfloat16, 16, 2, 64, 333, 128),
@@ -183,7 +220,7 @@ def _chunked_prefill_full_compare(dtype, Hq, Hkv, D, L, W):
     assert np.array_equal(si.storage(c1.v[0, :, :L]), vs.transpose(1, 0, 2))
 
 
-@pytest.mark.parametrize("kernel", ["narrow", "wide"])
+@pytest.mark.parametrize("kernel", ["narrow", "wide", "general"])
 @pytest.mark.parametrize("dtype,Hq,Hkv,D,past,real,W", [
     (torch.bfloat16, 32, 8, 128, 512, 416, 512),
     (torch.bfloat16, 12, 4, 128, 77, 150, 512),
@@ -344,7 +381,7 @@ def test_workload3_ladder_twice_on_dirty_cache():
         check(outs[0][torch.from_numpy(rows).cuda()], ref, 2e-2, f"L={L} widths={widths}")
 
 
-@pytest.mark.parametrize("kernel", ["narrow", "wide"])
+@pytest.mark.parametrize("kernel", ["narrow", "wide", "general"])
 def test_rows_equal_capacity_and_single_row_chunks(kernel):
     say(f"case: [{kernel}] W=1 chunks and a prompt filling the cache exactly")
     with cpk.attention_kernel(KERNELS[kernel]):
@@ -552,7 +589,7 @@ def test_workload4_ring_full_size():
 
 # ------------------------------------------------ HIP graph replay
 
-@pytest.mark.parametrize("kernel", ["narrow", "wide"])
+@pytest.mark.parametrize("kernel", ["narrow", "wide", "general"])
 def test_graph_replay_of_chunked_prefill(kernel):
     """A chunked prefill (rewind, then cpk_prefill_chunk per chunk with the
     padded tail) captured once as a HIP graph: every replay, with eager work
@@ -724,7 +761,7 @@ def test_varlen_interleaved_order(kernel):
         check(outs[0][s], ref, 2e-2, f"prompt slot {s}")
 
 
-@pytest.mark.parametrize("kernel", ["narrow", "wide"])
+@pytest.mark.parametrize("kernel", ["narrow", "wide", "general"])
 def test_mixed_step_small_full_compare(kernel):
     say(f"case: mixed step small [{kernel}]: 5 decodes ctx 20..300, prompt 700, budget 128, G=4")
     with cpk.attention_kernel(KERNELS[kernel]):
