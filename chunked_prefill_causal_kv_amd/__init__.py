@@ -189,12 +189,13 @@ def cpk_version() -> int:
     return _lib.cpk_version()
 
 
-ATTN_AUTO, ATTN_NARROW, ATTN_WIDE = 0, 1, 2
+ATTN_AUTO, ATTN_NARROW, ATTN_WIDE, ATTN_NARROW_GENERAL = 0, 1, 2, 3
 
 
 def cpk_set_attention_kernel(kind: int) -> int:
-    """Process-wide bf16/fp16 attention kernel choice (ATTN_AUTO, ATTN_NARROW
-    or ATTN_WIDE) for chunk and varlen attention; returns the previous one."""
+    """Process-wide bf16/fp16 attention kernel choice (ATTN_AUTO, ATTN_NARROW,
+    ATTN_WIDE or ATTN_NARROW_GENERAL) for chunk and varlen attention; returns
+    the previous one."""
     r = _lib.cpk_set_attention_kernel(int(kind))
     if r < 0:
         _check(r)

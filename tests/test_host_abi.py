@@ -207,8 +207,10 @@ def test_attention_kernel_setting():
     try:
         assert prev == cpk.ATTN_AUTO
         assert cpk.cpk_set_attention_kernel(cpk.ATTN_NARROW) == cpk.ATTN_WIDE
+        assert cpk.cpk_set_attention_kernel(cpk.ATTN_NARROW_GENERAL) == cpk.ATTN_NARROW
+        assert cpk.cpk_set_attention_kernel(cpk.ATTN_NARROW) == cpk.ATTN_NARROW_GENERAL
         with pytest.raises(cpk.CpkError):
-            cpk.cpk_set_attention_kernel(3)
+            cpk.cpk_set_attention_kernel(4)
         with pytest.raises(cpk.CpkError):
             cpk.cpk_set_attention_kernel(-1)
         with cpk.attention_kernel(cpk.ATTN_WIDE):
