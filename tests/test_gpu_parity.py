@@ -152,8 +152,9 @@ KERNELS = {"narrow": 1, "wide": 2, "general": 3}
 ])
 def test_scheduled_form_bit_equal_to_general(dtype, Hq, Hkv, D, past, real, W, pad):
     """The latency-scheduled form of the 64-column kernel gives the general
-    form's bits: outputs, every cache byte written (padded rows included)
-    and seqlens_k, for one fused prefill chunk after a cached prefix."""
+    form's bits (same arithmetic in the same order): outputs, every cache
+    byte written (padded rows included) and seqlens_k, for one fused prefill
+    chunk after a cached prefix; both match the oracle."""
     dn = {torch.bfloat16: "bf16", torch.float16: "f16"}[dtype]
     say(f"case: scheduled vs general {dn} heads {Hq}/{Hkv} D={D} past={past} real={real} W={W}")
     g = si.generator(610 + past + real)
@@ -175,6 +176,13 @@ def test_scheduled_form_bit_equal_to_general(dtype, Hq, Hkv, D, past, real, W, p
     n = past + w1
     assert bitwise(c1.k[:, :, :n], c2.k[:, :, :n]) and bitwise(c1.v[:, :, :n], c2.v[:, :, :n])
     assert torch.equal(c1.seqlens_k, c2.seqlens_k)
+    odt = ODT[dtype]
+    kk = oracle.widen(si.storage(c1.k[0, :, :past + real]), odt)
+    vv = oracle.widen(si.storage(c1.v[0, :, :past + real]), odt)
+    qq = oracle.widen(si.storage(q), odt)
+    lim = (past + np.arange(real)).astype(np.int32)
+    ref = oracle.attention(qq, kk, vv, np.zeros(real, np.int32), lim, 1.0 / math.sqrt(D))
+    check(o2, ref, TOL[dtype], "scheduled form vs oracle")
 
 
 @pytest.mark.parametrize("kernel", ["narrow", "wide", "general"])
