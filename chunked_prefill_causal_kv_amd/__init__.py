@@ -79,6 +79,7 @@ def _load() -> ctypes.CDLL:
         "cpk_varlen_step": ([P, P, P, CP, P, P, P, I32P, I32P, I32P, I, I, I, F, P, P, Z, P], I),
         "cpk_paged_varlen_step": ([P, P, P, PCP, P, P, P, I32P, I32P, I32P, I, I, I, F, P, P, Z, I, P], I),
         "cpk_varlen_step_phases": ([P, P, P, CP, P, P, P, I32P, I32P, I32P, I, I, I, F, P, P, Z, I, P], I),
+        "cpk_varlen_step_noalloc": ([P, P, P, CP, P, P, P, I32P, I32P, I32P, I, I, I, F, P, P], I),
         "cpk_roll_append": ([P, P, P, P, P, P, I, I, I, I, I, I, P], I),
         "cpk_roll_attention": ([P, P, P, P, I, I, I, I, I, I, I, I, F, P, P, Z, P], I),
         "cpk_roll_workspace_size": ([I, I, I, I, I, I], Z),
@@ -353,6 +354,37 @@ def cpk_varlen_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, c
     if phases & PHASE_APPEND:
         for s, slot in enumerate(slots):
             cache.lens[slot] = past_lens[s] + cu_rows[s + 1] - cu_rows[s]
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20
+
+
+def cpk_varlen_step_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                            cache: KVCache, slots: Sequence[int], cu_rows: Sequence[int],
+                            past_lens: Sequence[int], scale: float = 0.0,
+                            out: Optional[torch.Tensor] = None, dev_meta: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """cpk_varlen_step with the decode partials in the library's static
+    device scratch (no workspace, no allocation inside the call; out and
+    dev_meta, if given, are the caller's)."""
+    n = len(slots)
+    total, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    h_slots = (ctypes.c_int32 * n)(*slots)
+    h_cu = (ctypes.c_int32 * (n + 1))(*cu_rows)
+    h_past = (ctypes.c_int32 * n)(*past_lens)
+    if dev_meta is None:
+        dev_meta = torch.tensor(list(slots) + list(cu_rows) + list(past_lens),
+                                dtype=torch.int32).to(q.device)
+    base = dev_meta.data_ptr()
+    d_slots, d_cu, d_past = base, base + 4 * n, base + 4 * (2 * n + 1)
+    _check(_lib.cpk_varlen_step_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(cache.desc),
+                                        d_slots, d_cu, d_past, h_slots, h_cu, h_past, n, total, Hq,
+                                        float(scale), _ptr(out), _stream(stream)))
+    for s, slot in enumerate(slots):
+        cache.lens[slot] = past_lens[s] + cu_rows[s + 1] - cu_rows[s]
     return out
 
 

@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcpk.so")
-SOURCES = ["cpk_api.cpp", "k_copy.hip", "k_attn.hip", "k_decode.hip"]
+SOURCES = ["cpk_api.cpp", "k_copy.hip", "k_attn.hip", "k_decode.hip", "cpk_noalloc.hip"]
 ARCH = "gfx950"
 
 

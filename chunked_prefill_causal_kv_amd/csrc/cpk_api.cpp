@@ -39,6 +39,13 @@ int hip_status(hipError_t e, const char *what)
     return ok();
 }
 
+}  // namespace
+
+// status and message for the other translation units' entry points
+int cpk::fail_status(int code, const char *msg) { return fail(code, "%s", msg); }
+
+namespace {
+
 int elem_size(int dtype)
 {
     return dtype == CPK_F32 ? 4 : (dtype == CPK_F16 || dtype == CPK_BF16) ? 2 : 0;

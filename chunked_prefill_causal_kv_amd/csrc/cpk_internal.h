@@ -168,4 +168,7 @@ constexpr int kMaxTableBlocks = 512;
 hipError_t launch_attention_combine(const AttnArgs &a, int dtype, hipStream_t st);
 bool decode_supported(int dtype, int D, int group, int capacity);
 
+// Sets the calling thread's error message (cpk_last_error) and returns code.
+int fail_status(int code, const char *msg);
+
 }  // namespace cpk

@@ -236,6 +236,27 @@ int cpk_varlen_step(const void *q, const void *k_new, const void *v_new,
                     size_t ws_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * step as cpk_varlen_step, with the same arguments, validation and results
+ * bit for bit, but the decode partials go to a static device array of
+ * CPK_NOALLOC_SCRATCH_BYTES (96 MiB) that the library holds on every GPU it
+ * runs on until the process ends, instead of a caller workspace.  The call
+ * allocates nothing.  CPK_EWORKSPACE if the step's decode partials
+ * (cpk_varlen_workspace_size) exceed that size; CPK_EHIP if the array's
+ * address cannot be taken on the current device.  Every call on one GPU
+ * shares its array, so calls that overlap on one GPU (two streams or two
+ * threads) race; serialize them.
+ */
+#define CPK_NOALLOC_SCRATCH_BYTES (96ull << 20)
+int cpk_varlen_step_noalloc(const void *q, const void *k_new, const void *v_new,
+                            const cpk_kv_cache *cache, const int32_t *slots,
+                            const int32_t *cu_rows, const int32_t *past_lens,
+                            const int32_t *h_slots, const int32_t *h_cu_rows,
+                            const int32_t *h_past_lens, int n_seqs, int total_rows,
+                            int q_heads, float scale, void *out, void *stream);
+
+/*
  * cpk_varlen_step restricted to the given phases (a nonzero subset of
  * CPK_PHASE_ALL), with the same arguments, validation and errors.  The
  * decode and prefill phases read the cache after the append and write
