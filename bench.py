@@ -16,16 +16,20 @@ value  = algorithmic attention TFLOP/s of the whole step: 4*D*Hq flops per
 roofline = the attention kernel alone (each cpk_prefill_chunk launch):
          per-launch algorithmic flops over its average launch duration (HIP
          events on the launch stream), against the bf16 dense MFMA peak of
-         2.5 PFLOP/s.
-secondary = decode rows of the mixed-step workload (64 sequences, contexts
-         uniform in [512, 16384]) as a decode-only packed step: KV bytes read
-         per second against the 8 TB/s HBM peak; a steady-state W=512 chunk
-         at past_len 7680; the ladder prompts (useful and issued TFLOP/s);
-         the rolling fp16 cache; the mixed decode + prefill step at budgets
-         2048 and 8192 against its sum and max bounds.
-cpu_baseline = the fp64 CPU oracle timed on this host on a bounded sample of
-         the same workload (query rows of the prompt in seeded random order),
-         same flop accounting.
+         2.5 PFLOP/s; the GPU's kernel timestamps of one profiled eager step
+         give the kernel's name and a second average beside it.
+secondary = the fp32 demo (time only); decode rows of the mixed-step
+         workload (64 sequences, contexts uniform in [512, 16384]) as a
+         decode-only packed step: KV bytes read per second against the 8 TB/s
+         HBM peak, for the whole step and for the decode kernel alone; a
+         steady-state W=512 chunk at past_len 7680; the ladder prompts (useful
+         and issued TFLOP/s); the rolling fp16 cache against the larger of its
+         HBM and MFMA bounds; the mixed decode + prefill step at budgets 2048
+         and 8192 against its sum and max bounds.
+cpu_baseline = the fp64 CPU oracle timed on this host on bounded samples of
+         every workload (the headline figure: query rows of the GQA prompt in
+         seeded random order), at all its threads and, for the demo and one
+         GQA chunk, at one thread; same flop and byte accounting.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -87,6 +91,39 @@ def read_traffic(sha, path=TRAFFIC_FILE):
         return None
 
 
+def profile_kernels(torch, fn):
+    """Kernel names, launch counts and average durations (us) of what fn
+    runs, from the GPU's own kernel timestamps (torch.profiler over the ROCm
+    tracer, the source rocprofv3 reads too).  None if the profiler is
+    unavailable."""
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        torch.cuda.synchronize()
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            fn()
+            torch.cuda.synchronize()
+        out = {}
+        for e in prof.key_averages():
+            total = getattr(e, "device_time_total", None)
+            if total is None:
+                total = getattr(e, "cuda_time_total", 0.0)
+            if e.count and total:
+                out[e.key] = (e.count, total / e.count)
+        return out or None
+    except Exception as exc:   # the profiler is optional instrumentation
+        log(f"bench: kernel profiler unavailable ({exc})")
+        return None
+
+
+def pick_kernel_time(prof, *needles):
+    """(name, launches, average us) of the profiled kernel whose name holds
+    every needle and that ran the most launches, or None."""
+    if not prof:
+        return None
+    cands = [(n, c, t) for n, (c, t) in prof.items() if all(x in n for x in needles)]
+    return max(cands, key=lambda x: x[1]) if cands else None
+
+
 # spin length (GPU clock cycles) that covers the host-side enqueue of one
 # eight-chunk step
 HOST_LEAD_CYCLES = 2_000_000
@@ -134,6 +171,7 @@ def bench_chunked(cpk, si, torch, steps, warmup):
         torch.cuda.synchronize()
     per_chunk_ms = [[evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)]
                     for i in range(len(chunks))]
+    prof = profile_kernels(torch, lambda: step(None))
     ms_step = (t1 - t0) * 1e3 / steps
     total_flops = sum(flops)
     kern_ms = [sum(c) / len(c) for c in per_chunk_ms]
@@ -142,9 +180,10 @@ def bench_chunked(cpk, si, torch, steps, warmup):
               "ms": round(m, 4), "ms_median": round(statistics.median(c), 4),
               "ms_min": round(min(c), 4), "tflops": round(f / (m * 1e-3) / 1e12, 1)}
              for (p, r), f, m, c in zip(chunks, flops, kern_ms, per_chunk_ms)]
+    attn = pick_kernel_time(prof, "attn_")
     return dict(ms_step=ms_step, total_flops=total_flops, achieved=achieved,
                 kern_ms_avg=sum(kern_ms) / len(kern_ms), table=table, chunks=chunks,
-                q=q, k=k, v=v)
+                q=q, k=k, v=v, attn_kernel=attn)
 
 
 def bench_step_graph(cpk, si, torch, steps, warmup, q, k, v):
@@ -197,6 +236,41 @@ def bench_step_graph(cpk, si, torch, steps, warmup, q, k, v):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return (t1 - t0) * 1e3 / steps
+
+
+def bench_demo_fp32(cpk, si, torch, reps=20):
+    """The fp32 demo workload on the GPU: 1000 tokens, 8 heads, D 64, chunk
+    256 (4 chunks: 256/256/256/232), unpadded, into an fp32 cache of
+    capacity 1024; rewind + 4 cpk_prefill_chunk calls per pass.  A
+    correctness workload: its time is reported, with no roofline target."""
+    _, (q, k, v) = si.demo_qkv()
+    q, k, v = (x.cuda() for x in (q, k, v))
+    cache = cpk.KVCache(1, 8, 1024, 64, torch.float32)
+    out = torch.empty_like(q)
+    chunks = cpk.cpk_split_chunks(1000, 256)
+
+    def run():
+        if cache.lens[0]:
+            cpk.cpk_rewind(cache, 0, 0)
+        for past, rows in chunks:
+            sl = slice(past, past + rows)
+            cpk.cpk_prefill_chunk(q[sl], k[sl], v[sl], cache, 0, past, 256, pad=False, out=out[sl])
+
+    for _ in range(3):
+        run()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    f = 4 * 64 * 8 * sum(p + 1 for p in range(1000))
+    return {"chunks": [list(c) for c in chunks], "gflop": round(f / 1e9, 3), "ms": round(ms, 4),
+            "tflops": round(f / (ms * 1e-3) / 1e12, 2), "dtype": "fp32",
+            "note": "eager calls (rewind + 4 chunk launches), HIP events over 20 passes"}
 
 
 def bench_steady_chunk(cpk, si, torch, reps=20):
@@ -255,14 +329,30 @@ def bench_decode(cpk, si, torch, reps=10):
     io_bytes = n * Hq * D * 2 * 2 + n * Hkv * D * 2 * 2 * 2
     gbps = (kv_bytes + io_bytes) / (ms * 1e-3) / 1e9
     sha = src_sha(DECODE_SRC)
+    prof = profile_kernels(torch, lambda: [cpk.cpk_varlen_step(q, kn, vn, cache, slots, cu, ctxs,
+                                                               out=out, ws=ws, dev_meta=meta)
+                                           for _ in range(reps)])
+    dk = pick_kernel_time(prof, "decode_kernel")
+    dc = pick_kernel_time(prof, "decode_combine")
+    own = None
+    if dk:
+        kg = (kv_bytes + io_bytes) / (dk[2] * 1e-6) / 1e9
+        own = {"bound": "hbm", "achieved": round(kg, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+               "frac": round(kg / PEAK_HBM_GBPS, 4), "kernel": dk[0][:90],
+               "avg_us": round(dk[2], 2), "launches": dk[1],
+               "combine_avg_us": round(dc[2], 2) if dc else None,
+               "timer": "GPU kernel timestamps (torch.profiler over the ROCm tracer)"}
     return {"sequences": n, "kv_gb": round(kv_bytes / 1e9, 3), "ms": round(ms, 4),
             "GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-            "note": "whole packed step (append + split-KV decode + combine)",
+            "note": "whole packed step (split-KV decode with the new rows' append fused, "
+                    "then the combine)",
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
                          "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
                          "traffic": read_traffic(sha, DECODE_TRAFFIC_FILE),
                          "kernel": "decode_kernel<bf16,128,4> + decode_combine (whole step)",
-                         "kernel_source_sha": sha}}
+                         "timer": "HIP events around 10 back-to-back steps on the launch stream",
+                         "kernel_source_sha": sha},
+            "kernel_roofline": own}
 
 
 def issued_pairs(past, width):
@@ -382,10 +472,27 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=5):
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "replay differs"
     ms = statistics.median(times)
     f = 4 * D * H * pairs
+    # algorithmic bytes per chunk: q and out, K/V of the keys in the window
+    # read once, the c new K/V rows written once, the mask if one is passed
+    row = H * D * 2
+    nbytes = sum(2 * c * row + 2 * min(C, (j + 1) * c) * row + 2 * c * row +
+                 (c * C * 2 if explicit_mask else 0) for j in range(n))
+    t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9) * 1e3
+    t_mma = f / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+    if t_hbm >= t_mma:
+        roof = {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(f / (ms * 1e-3) / 1e12, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roof.update({"frac": round(max(t_hbm, t_mma) / ms, 4), "algorithmic_bytes": nbytes,
+                 "hbm_bound_ms": round(t_hbm, 4), "mfma_bound_ms": round(t_mma, 4),
+                 "note": "whole 16-chunk schedule against the larger of its HBM and fp16 "
+                         "MFMA bounds"})
     how = "the explicit (c, C) mask" if explicit_mask else "visibility computed in the kernel"
     what = "ring_step (append fused into the attention)" if ring else "roll_append + roll_attention"
     return {"chunks": n, "gflop": round(f / 1e9, 2), "ms": round(ms, 4), "ms_min": round(min(times), 4),
-            "tflops": round(f / (ms * 1e-3) / 1e12, 1), "dtype": "fp16",
+            "tflops": round(f / (ms * 1e-3) / 1e12, 1), "dtype": "fp16", "roofline": roof,
             "note": f"{what} with {how}, per chunk; 16 chunks replayed as a HIP graph, "
                     f"median of {reps} replays"}
 
@@ -499,6 +606,8 @@ def bench_mixed(cpk, si, torch, budget, overlap=False, reps=3, paged=False):
             "ms_total_eager_calls": round(tot, 3),
             "sum_bound_ms_total": round(sum(t["sum_bound_ms"] for t in table), 3),
             "max_bound_ms_total": round(sum(t["max_bound_ms"] for t in table), 3),
+            "frac_of_max_bound": round(sum(t["max_bound_ms"] for t in table) / g_tot, 4),
+            "frac_of_sum_bound": round(sum(t["sum_bound_ms"] for t in table) / g_tot, 4),
             "per_step_eager": table}
 
 
@@ -517,27 +626,21 @@ def calibrate_copy(cpk, torch, reps=3):
     return nbytes
 
 
-def cpu_baseline(si, budget_s=10.0):
-    """The fp64 oracle on rows of the 4000-token prompt drawn in a seeded
-    random order, in batches, until about budget_s seconds of CPU work have
-    been spent (a pass over all rows takes about 1 s on 16 host threads, so
-    the sample repeats whole passes and ends inside one)."""
-    import numpy as np
-
-    import oracle
+def _oracle_rows_sample(oracle, np, si, threads, budget_s):
+    """fp64 oracle on rows of the 4000-token GQA prompt drawn in a seeded
+    random order, in batches of 64, until about budget_s seconds of CPU work
+    have been spent (whole passes repeat; the sample ends inside one)."""
     L, Hq, Hkv, D = 4000, 32, 8, 128
     q, k, v = si.gqa_prompt(L=L, Hq=Hq, Hkv=Hkv, D=D)
     qs, ks, vs = (si.storage(x) for x in (q, k, v))
     kk = oracle.widen(np.ascontiguousarray(ks.transpose(1, 0, 2)), oracle.BF16)
     vv = oracle.widen(np.ascontiguousarray(vs.transpose(1, 0, 2)), oracle.BF16)
-    rows_all = np.arange(0, L)
-    rng = np.random.default_rng(0)
-    rows_all = rng.permutation(rows_all)
+    rows_all = np.random.default_rng(0).permutation(np.arange(0, L))
     done_rows, flops, t_total = 0, 0, 0.0
-    batch = 64
+    oracle.set_num_threads(threads)
     while t_total < budget_s:
         start = done_rows % len(rows_all)
-        rows = np.sort(rows_all[start:start + batch])
+        rows = np.sort(rows_all[start:start + 64])
         qq = oracle.widen(np.ascontiguousarray(qs[rows]), oracle.BF16)
         t0 = time.perf_counter()
         oracle.attention(qq, kk, vv, np.zeros(len(rows), np.int32), rows.astype(np.int32),
@@ -545,11 +648,125 @@ def cpu_baseline(si, budget_s=10.0):
         t_total += time.perf_counter() - t0
         flops += sum(4 * D * Hq * (int(r) + 1) for r in rows)
         done_rows += len(rows)
-    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{done_rows} query rows ({done_rows / len(rows_all):.2f} passes over the "
-                      f"4000 rows of the prompt, seeded random order), all 32 heads, causal over "
-                      f"the cache, fp64; {t_total:.1f} s"}
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "threads": threads,
+            "seconds": round(t_total, 2),
+            "sample": f"{done_rows} query rows ({done_rows / L:.2f} passes over the 4000 rows "
+                      f"of the prompt, seeded random order), all 32 heads, causal over the "
+                      f"cache"}
+
+
+def cpu_baseline(si, budget_s=6.0):
+    """The fp64 CPU oracle (as it stands) timed on this host on a bounded
+    sample of every workload, at all of the oracle's OpenMP threads and, for
+    the fp32 demo and one chunk of the GQA prompt, at one thread.  Each
+    entry counts only the work of the rows it evaluates (same flop and byte
+    accounting as the GPU figures).  The headline entry is the GQA prompt
+    sample."""
+    import numpy as np
+
+    import oracle
+    n_all = oracle.num_threads()
+    table = {}
+
+    def run_timed(fn, threads):
+        oracle.set_num_threads(threads)
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    # workload 1: the fp32 demo in full (4 chunks of 256 over 1000 tokens)
+    _, (dq, dk, dv) = si.demo_qkv()
+    dq, dk, dv = (si.storage(x) for x in (dq, dk, dv))
+    f_demo = 4 * 64 * 8 * sum(p + 1 for p in range(1000))
+    for threads in (n_all, 1):
+        t = run_timed(lambda: oracle.prefill_chunked(oracle.Cache(oracle.F32, 1, 8, 1024, 64), 0,
+                                                     dq, dk, dv, 256), threads)
+        table[f"demo_fp32_threads_{threads}"] = {
+            "value": round(f_demo / t / 1e12, 6), "unit": "TFLOP/s", "threads": threads,
+            "seconds": round(t, 3), "sample": "whole demo: 1000 tokens, 8 heads, D 64, W 256"}
+
+    # workload 2: sampled rows at all threads (headline), and chunk 0 in
+    # full at one thread
+    head = _oracle_rows_sample(oracle, np, si, n_all, budget_s)
+    table[f"gqa_w512_rows_threads_{n_all}"] = head
+    q, k, v = si.gqa_prompt()
+    qs, ks, vs = (si.storage(x) for x in (q, k, v))
+
+    def chunk0():
+        c = oracle.Cache(oracle.BF16, 1, 8, 8192, 128)
+        c.append(0, ks[:512], vs[:512], 0)
+        oracle.attend_from_cache(c, 0, qs[:512], 0)
+    t = run_timed(chunk0, 1)
+    f0 = 4 * 128 * 32 * (512 * 513 // 2)
+    table["gqa_w512_chunk0_threads_1"] = {
+        "value": round(f0 / t / 1e12, 6), "unit": "TFLOP/s", "threads": 1, "seconds": round(t, 3),
+        "sample": "chunk 0 of the 4000-token prompt in full (append + 512 rows x 32 heads)"}
+
+    # workload 3: the 1137-token ladder prompt, padded forwards as the
+    # oracle runs them (every padded row attended, real rows kept)
+    useful = sum(issued_pairs(p, r) for p, r in oracle.split_chunks(1137, 512))
+    issued = sum(issued_pairs(p, oracle.ladder_width(512, r))
+                 for p, r in oracle.split_chunks(1137, 512))
+    t = run_timed(lambda: oracle.prefill_chunked_padded(
+        oracle.Cache(oracle.BF16, 1, 8, 8192, 128), 0, qs[:1137], ks[:1137], vs[:1137], 512),
+        n_all)
+    table[f"ladder_1137_threads_{n_all}"] = {
+        "value": round(4 * 128 * 32 * useful / t / 1e12, 6), "unit": "TFLOP/s (useful)",
+        "issued_tflops": round(4 * 128 * 32 * issued / t / 1e12, 6), "threads": n_all,
+        "seconds": round(t, 3), "sample": "the 1137-token prompt, W 512, ladder-padded forwards"}
+
+    # workload 4: the rolling fp16 cache in full (16 chunks)
+    rq, rk, rv = (si.storage(x) for x in si.rolling_inputs())
+    t = run_timed(lambda: oracle.roll_prefill(rq, rk, rv, 2048, 256, oracle.F16), n_all)
+    pairs = sum(min(2048, (j + 1) * 256) * 256 - (256 * 255) // 2 for j in range(16))
+    table[f"rolling_fp16_threads_{n_all}"] = {
+        "value": round(4 * 128 * 16 * pairs / t / 1e12, 6), "unit": "TFLOP/s", "threads": n_all,
+        "seconds": round(t, 3),
+        "sample": "4096 tokens, 16 heads, C 2048, c 256: roll + masked attention over C slots"}
+
+    # workload 5: decode rows (8 of the 64 sequences, KV bytes per second)
+    # and one budget-2048 mixed step (those 8 decode rows plus 128 sampled
+    # rows of the first 1984 prompt rows)
+    ctxs = si.mixed_contexts()[:8]
+    cap = max(ctxs) + 1 + 1984
+    g = si.generator(41)
+    n = len(ctxs)
+    dcache = oracle.Cache(oracle.BF16, n + 1, 8, cap, 128)
+    for i, c in enumerate(ctxs):
+        dcache.k[i, :, :c] = si.storage(si.randn((8, c, 128), "bf16", g))
+        dcache.v[i, :, :c] = si.storage(si.randn((8, c, 128), "bf16", g))
+        dcache.lens[i] = c
+    dq_ = si.storage(si.randn((n, 32, 128), "bf16", g))
+    dk_ = si.storage(si.randn((n, 8, 128), "bf16", g))
+    dv_ = si.storage(si.randn((n, 8, 128), "bf16", g))
+    seqs = [(i, c) for i, c in enumerate(ctxs)]
+    t = run_timed(lambda: oracle.varlen_step(dcache, seqs, dq_, dk_, dv_, list(range(n + 1))),
+                  n_all)
+    kvb = sum((c + 1) * 8 * 128 * 2 * 2 for c in ctxs) + n * 32 * 128 * 2 * 2
+    table[f"decode_rows_threads_{n_all}"] = {
+        "value": round(kvb / t / 1e9, 4), "unit": "GB/s", "threads": n_all,
+        "seconds": round(t, 3),
+        "sample": f"8 of the 64 decode sequences (contexts {ctxs}), one row each"}
+    pq, pk, pv = (si.storage(x) for x in si.gqa_prompt(L=1984, seed=33))
+    mq = np.concatenate([dq_, pq])
+    mk = np.concatenate([dk_, pk])
+    mv = np.concatenate([dv_, pv])
+    sel = np.sort(np.random.default_rng(1).choice(1984, 128, replace=False))
+    seqs_m = [(i, c + 1) for i, c in enumerate(ctxs)] + [(n, 0)]
+    t = run_timed(lambda: oracle.varlen_step(dcache, seqs_m, mq, mk, mv,
+                                             list(range(n + 1)) + [n + 1984],
+                                             rows_idx={n: sel}), n_all)
+    f_mix = 4 * 128 * 32 * (sum(c + 2 for c in ctxs) + int(sum(int(r) + 1 for r in sel)))
+    table[f"mixed_budget_2048_threads_{n_all}"] = {
+        "value": round(f_mix / t / 1e12, 6), "unit": "TFLOP/s", "threads": n_all,
+        "seconds": round(t, 3),
+        "sample": "one budget-2048 step: 8 decode rows + 128 of the 1984 prompt rows at past 0 "
+                  "(append of all 1992 rows included)"}
+    oracle.set_num_threads(n_all)
+    return {"value": head["value"], "unit": "TFLOP/s", "cores": n_all, "kind": "oracle",
+            "sample": head["sample"] + f", fp64, {head['seconds']} s; per-workload entries in "
+                      "per_config",
+            "per_config": table}
 
 
 def main():
@@ -560,8 +777,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary", default="all",
-                    help="comma list of secondary groups to run: steady, decode, ladder, "
-                         "rolling, mixed (default all)")
+                    help="comma list of secondary groups to run: demo, steady, decode, "
+                         "ladder, rolling, mixed (default all)")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain copy of known size (for counter scaling)")
     args = ap.parse_args()
@@ -585,11 +802,14 @@ def main():
     ms_graph = bench_step_graph(cpk, si, torch, args.steps, args.warmup, r["q"], r["k"], r["v"])
     log(f"bench: graph-replayed step {ms_graph:.3f} ms")
     secondary = {}
-    groups = {"steady", "decode", "ladder", "rolling", "mixed"}
+    groups = {"demo", "steady", "decode", "ladder", "rolling", "mixed"}
     if args.secondary != "all":
         groups = set(args.secondary.split(","))
     if not args.no_secondary:
         secondary["per_chunk"] = r["table"]
+    if not args.no_secondary and "demo" in groups:
+        secondary["demo_fp32"] = bench_demo_fp32(cpk, si, torch)
+        log(f"bench: fp32 demo {secondary['demo_fp32']}")
     if not args.no_secondary and "steady" in groups:
         secondary["steady_chunk"] = bench_steady_chunk(cpk, si, torch)
         log(f"bench: steady chunk {secondary['steady_chunk']}")
@@ -647,8 +867,17 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(r["achieved"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": read_traffic(sha),
-                     "kernel": "attn_mfma_kernel<bf16,128>",
+                     "kernel": (r["attn_kernel"][0][:100] if r["attn_kernel"]
+                                else "attention kernel of cpk_prefill_chunk"),
                      "avg_launch_ms": round(r["kern_ms_avg"], 4),
+                     "timer": "HIP events bracketing each launch on its stream (a spin kernel "
+                              "ahead of each step keeps the host's enqueue ahead), averaged "
+                              "over the 8 chunk launches of each timed step",
+                     "trace_avg_launch_ms": (round(r["attn_kernel"][2] * 1e-3, 4)
+                                             if r["attn_kernel"] else None),
+                     "trace_frac": (round(r["total_flops"] / len(r["chunks"]) /
+                                          (r["attn_kernel"][2] * 1e-6) / 1e12 /
+                                          PEAK_BF16_TFLOPS, 4) if r["attn_kernel"] else None),
                      "kernel_source_sha": sha},
         "secondary": secondary,
     }

@@ -482,12 +482,15 @@ static int varlen_impl(const void *q, const void *k_new, const void *v_new,
     }
     hipStream_t st = (hipStream_t)stream;
     const int rb = cache->head_dim * elem_size(cache->dtype);
-    if (phases & CPK_PHASE_APPEND) {
+    // a call that both appends and decodes leaves the decode rows' append to
+    // the decode kernel (fused); the copy kernel then moves only prompt rows
+    const bool fuse_dec = n_dec > 0 && (phases & CPK_PHASE_APPEND) && (phases & CPK_PHASE_DECODE);
+    if ((phases & CPK_PHASE_APPEND) && (n_pre > 0 || !fuse_dec)) {
         r = hip_status(cpk::launch_kv_append_varlen(
                            k_new, v_new, cache->k, cache->v, cache->seqlens_k, cache->kv_heads,
                            cache->capacity, rb, cu_rows, past_lens, slots, n_seqs, total_rows,
                            pg ? pg->table : nullptr, pg ? pg->max_blocks : 0,
-                           pg ? pg->block_size : 0, pg ? pg->n_blocks : 0, st),
+                           pg ? pg->block_size : 0, pg ? pg->n_blocks : 0, fuse_dec, st),
                        "varlen append");
         if (r) return r;
     }
@@ -499,6 +502,9 @@ static int varlen_impl(const void *q, const void *k_new, const void *v_new,
         d.scale_log2 = (float)((double)sc * 1.4426950408889634);
         d.max_segs = max_segs;
         d.cu_rows = cu_rows; d.past_lens = past_lens; d.slots = slots; d.n_seqs = n_seqs;
+        if (fuse_dec) {
+            d.k_new = k_new; d.v_new = v_new; d.seqlens_k = cache->seqlens_k;
+        }
         if (pg) {
             d.block_table = pg->table; d.max_blocks = pg->max_blocks;
             d.block_size = pg->block_size; d.n_blocks = pg->n_blocks;

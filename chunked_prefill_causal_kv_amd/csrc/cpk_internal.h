@@ -97,8 +97,8 @@ __device__ __forceinline__ int64_t paged_row(const int32_t *table, int max_block
 // Split-KV decode: one query row per sequence.
 struct DecodeArgs {
     const void *q;      // token-major [*, Hq, D]
-    const void *k;      // cache
-    const void *v;
+    void *k;            // cache (written only by the fused append)
+    void *v;
     void *out;
     float *ws;          // partials [n_seqs][Hq][max_segs][D + 4] (m, l, pad, pad, acc[D])
     int Hq, Hkv, D, cap;
@@ -112,6 +112,13 @@ struct DecodeArgs {
     // paged cache, as in AttnArgs (block_size 0: contiguous [batch][Hkv][cap][D])
     const int32_t *block_table;
     int max_blocks, block_size, n_blocks;
+    // fused append (k_new non-null): the workgroup whose segment holds a
+    // sequence's new key writes that row of k_new/v_new (token-major
+    // [*, Hkv, D], row cu_rows[s]) into the cache before reading it, and
+    // sets seqlens_k[slot] to past_len + 1
+    const void *k_new;
+    const void *v_new;
+    int32_t *seqlens_k;
 };
 
 constexpr int kDecodeSeg = 256;   // keys per decode work item (4 waves x 64)
@@ -126,7 +133,7 @@ hipError_t launch_kv_append_varlen(const void *k_new, const void *v_new, void *c
                                    const int32_t *cu_rows, const int32_t *past_lens,
                                    const int32_t *slots, int n_seqs, int total_rows,
                                    const int32_t *block_table, int max_blocks, int block_size,
-                                   int n_blocks, hipStream_t st);
+                                   int n_blocks, bool skip_single, hipStream_t st);
 hipError_t launch_set_len(int32_t *seqlens, int b, int len, hipStream_t st);
 // rows [0, len) of slot src copied to slot dst (every KV head); seqlens[dst] = len
 hipError_t launch_kv_copy_prefix(const void *k, const void *v, int32_t *seqlens, int Hkv,

@@ -39,7 +39,8 @@ __global__ void kv_append_kernel(const vec16 *__restrict__ kn, const vec16 *__re
 
 // Packed step: row t of the packed k_new/v_new belongs to the sequence s with
 // cu_rows[s] <= t < cu_rows[s+1]; it lands at position past_lens[s] + (t -
-// cu_rows[s]) of cache slot slots[s].
+// cu_rows[s]) of cache slot slots[s].  With skip_single, the rows of
+// one-row sequences are left out (the decode kernel appends those itself).
 __global__ void kv_append_varlen_kernel(const vec16 *__restrict__ kn, const vec16 *__restrict__ vn,
                                         vec16 *__restrict__ ck, vec16 *__restrict__ cv,
                                         int32_t *__restrict__ seqlens, int Hkv, int cap, int vpr,
@@ -47,7 +48,7 @@ __global__ void kv_append_varlen_kernel(const vec16 *__restrict__ kn, const vec1
                                         const int32_t *__restrict__ past_lens,
                                         const int32_t *__restrict__ slots, int n_seqs,
                                         int total_rows, const int32_t *__restrict__ table,
-                                        int max_blocks, int bs, int n_blocks)
+                                        int max_blocks, int bs, int n_blocks, int skip_single)
 {
     const int64_t total = (int64_t)total_rows * Hkv * vpr;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -63,6 +64,7 @@ __global__ void kv_append_varlen_kernel(const vec16 *__restrict__ kn, const vec1
             if (cu_rows[mid] <= t) lo = mid; else hi = mid - 1;
         }
         const int s = lo;
+        if (skip_single && cu_rows[s + 1] - cu_rows[s] == 1) continue;
         const int r = t - cu_rows[s];
         const int pos = past_lens[s] + r;
         const int64_t row = bs ? paged_row(table, max_blocks, bs, n_blocks, Hkv, slots[s], h, pos)
@@ -213,14 +215,14 @@ hipError_t launch_kv_append_varlen(const void *k_new, const void *v_new, void *c
                                    const int32_t *cu_rows, const int32_t *past_lens,
                                    const int32_t *slots, int n_seqs, int total_rows,
                                    const int32_t *block_table, int max_blocks, int block_size,
-                                   int n_blocks, hipStream_t st)
+                                   int n_blocks, bool skip_single, hipStream_t st)
 {
     const int vpr = row_bytes / 16;
     const int64_t items = (int64_t)total_rows * Hkv * vpr;
     hipLaunchKernelGGL(kv_append_varlen_kernel, dim3(grid_for(items)), dim3(256), 0, st,
                        (const vec16 *)k_new, (const vec16 *)v_new, (vec16 *)ck, (vec16 *)cv,
                        seqlens, Hkv, cap, vpr, cu_rows, past_lens, slots, n_seqs, total_rows,
-                       block_table, max_blocks, block_size, n_blocks);
+                       block_table, max_blocks, block_size, n_blocks, skip_single ? 1 : 0);
     return hipGetLastError();
 }
 

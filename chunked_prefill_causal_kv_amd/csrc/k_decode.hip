@@ -25,6 +25,9 @@
 //   in fp32; the running sum adds the same rounded P.
 // * Keys at or past the sequence's length are never loaded.
 //
+// * Fused append: in a step that also appends, the workgroup whose segment
+//   holds a sequence's new key writes that K/V row into the cache itself.
+//
 // decode_combine merges the per-segment (max, sum, acc) partials of every
 // (sequence, query head) in a fixed order (deterministic, no atomics).
 #include "cpk_internal.h"
@@ -163,6 +166,25 @@ void decode_kernel(DecodeArgs a)
                       : ((int64_t)slot * a.Hkv + g) * a.cap) * D * 2;
     const char *kbase = (const char *)a.k + head_off;
     const char *vbase = (const char *)a.v + head_off;
+
+    // fused append: the segment holding the new key (position n_keys - 1)
+    // writes this KV head's new K/V row into the cache first; the stores
+    // complete before the barrier, so the workgroup then reads the row back
+    // with the rest of its keys
+    if (a.k_new && sb + kDecodeSeg >= n_keys) {
+        constexpr int V16 = D * 2 / 16;   // 16-byte pieces per row
+        if (tid < 2 * V16) {
+            const int part = tid / V16, c = tid % V16;
+            const uint4 *src = (const uint4 *)(part ? a.v_new : a.k_new) +
+                               ((int64_t)row0 * a.Hkv + g) * V16 + c;
+            char *dst = (char *)(part ? a.v : a.k) + head_off +
+                        (uint32_t)(n_keys - 1 - key_org) * (D * 2) + 16u * c;
+            *(uint4 *)dst = *src;
+        }
+        if (g == 0 && tid == 0) a.seqlens_k[slot] = n_keys;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
 
     uint4 qv[G];
     const uint16_t *qp = (const uint16_t *)a.q + ((int64_t)row0 * a.Hq + g * G) * D + 8 * j;
@@ -318,61 +340,92 @@ void decode_kernel(DecodeArgs a)
     }
 }
 
-// Merge the segment partials of one (sequence, query head).  One thread per
-// output column d.  The maximum over all segments is found with a block
-// reduction; segment weights exp2(m_s - M) and sums l_s are then staged in
-// LDS, kCombineChunk segments at a time, and every thread accumulates its
-// column over the segments in increasing order (deterministic, no atomics).
-constexpr int kCombineChunk = 256;
+// Merge the segment partials of one (sequence, query head).  Four waves:
+// wave w takes segments w, w + 4, w + 8, ... and each lane D/64 columns.  A
+// wave loads kCombBatch of its segments' records at once (all loads in
+// flight, so the merge costs about one memory round trip, not one per
+// segment), folds them in increasing segment order into its running (max,
+// sum, acc), and the four waves' results are then merged in wave order
+// through LDS.  Fixed order throughout: deterministic, no atomics.
+constexpr int kCombThreads = 256;
+constexpr int kCombBatch = 16;
 
 template <typename TR, int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a)
+__global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodeArgs a)
 {
     constexpr int WS = D + 4;
-    constexpr int NW = D / 64;
-    __shared__ float we[kCombineChunk];
-    __shared__ float wl[kCombineChunk];
-    __shared__ float wmax[NW];
+    constexpr int CPL = D / 64;   // columns per lane
+    constexpr int NWV = kCombThreads / 64;
+    __shared__ float wm[NWV], wl[NWV];
+    __shared__ __attribute__((aligned(16))) float wacc[NWV][D];
     const int z = blockIdx.y;
     const int row0 = a.cu_rows[z];
     if (a.cu_rows[z + 1] - row0 != 1) return;
     const int n_keys = a.past_lens[z] + 1;
     const int n_segs = (n_keys + kDecodeSeg - 1) / kDecodeSeg;
     const int head = blockIdx.x;
-    const int d = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const float *rec = a.ws + ((int64_t)z * a.Hq + head) * a.max_segs * WS;
 
-    float M = -INFINITY;
-    for (int s = d; s < n_segs; s += D) M = fmaxf(M, rec[(int64_t)s * WS]);
+    float M = -INFINITY, L = 0.f, acc[CPL];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if ((d & 63) == 0) wmax[d >> 6] = M;
-    __syncthreads();
-    M = wmax[0];
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+    for (int s0 = wave; s0 < n_segs; s0 += NWV * kCombBatch) {
+        float ms[kCombBatch], ls[kCombBatch], xs[kCombBatch][CPL];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, wmax[w]);
-
-    float acc = 0.f, lsum = 0.f;
-    for (int s0 = 0; s0 < n_segs; s0 += kCombineChunk) {
-        const int cnt = min(kCombineChunk, n_segs - s0);
-        __syncthreads();
-        for (int s = d; s < cnt; s += D) {
-            const float *r = rec + (int64_t)(s0 + s) * WS;
-            const float ms = r[0];
-            we[s] = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-            wl[s] = r[1];
+        for (int i = 0; i < kCombBatch; ++i) {
+            // past the last segment: re-read a valid record, weighted 0 below
+            const float *r = rec + (int64_t)min(s0 + NWV * i, n_segs - 1) * WS;
+            ms[i] = r[0];
+            ls[i] = r[1];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) xs[i][c] = r[4 + CPL * lane + c];
         }
-        __syncthreads();
-        const float *col = rec + (int64_t)s0 * WS + 4 + d;
-#pragma unroll 4
-        for (int s = 0; s < cnt; ++s) {
-            acc = __builtin_fmaf(we[s], col[(int64_t)s * WS], acc);
-            lsum = __builtin_fmaf(we[s], wl[s], lsum);
+        float bm = M;
+#pragma unroll
+        for (int i = 0; i < kCombBatch; ++i)
+            if (s0 + NWV * i < n_segs) bm = fmaxf(bm, ms[i]);
+        if (bm != M) {   // M == -inf: nothing merged yet, L and acc are 0
+            const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - bm);
+            L *= alpha;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[c] *= alpha;
+            M = bm;
+        }
+#pragma unroll
+        for (int i = 0; i < kCombBatch; ++i) {
+            const float e = (s0 + NWV * i < n_segs && ms[i] != -INFINITY)
+                                ? __builtin_amdgcn_exp2f(ms[i] - M) : 0.f;
+            L = __builtin_fmaf(e, ls[i], L);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[c] = __builtin_fmaf(e, xs[i][c], acc[c]);
         }
     }
-    const float r = lsum > 0.f ? acc / lsum : 0.f;
-    uint16_t *op = (uint16_t *)a.out + ((int64_t)row0 * a.Hq + head) * D;
-    op[d] = (uint16_t)TR::from_f32(r);
+    if (lane == 0) {
+        wm[wave] = M;
+        wl[wave] = L;
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) wacc[wave][CPL * lane + c] = acc[c];
+    __syncthreads();
+    if (wave != 0) return;
+    float Mt = wm[0];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) Mt = fmaxf(Mt, wm[w]);
+    float Lt = 0.f, at[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) at[c] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+        const float e = wm[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(wm[w] - Mt);
+        Lt = __builtin_fmaf(e, wl[w], Lt);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) at[c] = __builtin_fmaf(e, wacc[w][CPL * lane + c], at[c]);
+    }
+    uint16_t *op = (uint16_t *)a.out + ((int64_t)row0 * a.Hq + head) * D + CPL * lane;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) op[c] = (uint16_t)TR::from_f32(Lt > 0.f ? at[c] / Lt : 0.f);
 }
 
 template <typename TR, int D>
@@ -387,7 +440,8 @@ hipError_t launch_decode_t(const DecodeArgs &a, int G, int max_segs, hipStream_t
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<TR, D>), dim3(a.Hq, a.n_seqs), dim3(D), 0, st, a);
+    hipLaunchKernelGGL((decode_combine_kernel<TR, D>), dim3(a.Hq, a.n_seqs), dim3(kCombThreads), 0,
+                       st, a);
     return hipGetLastError();
 }
 

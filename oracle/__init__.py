@@ -87,6 +87,8 @@ def _load():
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = I
+        lib.orc_set_num_threads.argtypes = [I]
+        lib.orc_set_num_threads.restype = None
         lib.orc_widen.argtypes = [P, I, I64, P]
         lib.orc_widen.restype = I
         lib.orc_attention.argtypes = [P, I, I, P, P, I, I, I, P, P, P, D, P]
@@ -102,6 +104,11 @@ def _load():
 def num_threads() -> int:
     """OpenMP threads the oracle's loops use on this host."""
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's later loops (for timing at one thread)."""
+    _load().orc_set_num_threads(int(n))
 
 
 def _ptr(a: np.ndarray):

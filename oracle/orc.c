@@ -35,6 +35,13 @@ enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
 /* Threads the OpenMP loops use (reported beside the oracle's timings). */
 int orc_num_threads(void) { return omp_get_max_threads(); }
 
+/* Thread count of later OpenMP loops (timing runs at one thread and at all
+   of them); n < 1 is ignored. */
+void orc_set_num_threads(int n)
+{
+    if (n >= 1) omp_set_num_threads(n);
+}
+
 /* IEEE binary16 -> double, exact (subnormals, inf and NaN included). */
 static double orc_half_to_double(uint16_t h)
 {
