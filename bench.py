@@ -95,7 +95,10 @@ def profile_kernels(torch, fn):
     """Kernel names, launch counts and average durations (us) of what fn
     runs, from the GPU's own kernel timestamps (torch.profiler over the ROCm
     tracer, the source rocprofv3 reads too).  None if the profiler is
-    unavailable."""
+    unavailable, or when an outside profiler (rocprofv3) already traces the
+    process: two tracers in one process give wrong durations."""
+    if any(k.startswith(("ROCPROF", "ROCP_")) for k in os.environ):
+        return None
     try:
         from torch.profiler import ProfilerActivity, profile
         torch.cuda.synchronize()
@@ -779,6 +782,12 @@ def main():
     ap.add_argument("--secondary", default="all",
                     help="comma list of secondary groups to run: demo, steady, decode, "
                          "ladder, rolling, mixed (default all)")
+    ap.add_argument("--rolling", default="all",
+                    help="comma list of rolling schedules to run: shift_mask, shift_computed, "
+                         "ring_mask, ring_computed (default all)")
+    ap.add_argument("--mixed", default="all",
+                    help="comma list of mixed steps to run, as budget[_two_streams][_paged] "
+                         "(default all five)")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain copy of known size (for counter scaling)")
     args = ap.parse_args()
@@ -820,22 +829,24 @@ def main():
         secondary["ladder"] = bench_ladder(cpk, si, torch)
         log(f"bench: ladder {secondary['ladder']}")
     if not args.no_secondary and "rolling" in groups:
-        secondary["rolling_fp16"] = bench_rolling(cpk, si, torch)
-        log(f"bench: rolling {secondary['rolling_fp16']}")
-        secondary["rolling_fp16_computed_mask"] = bench_rolling(cpk, si, torch, False)
-        log(f"bench: rolling {secondary['rolling_fp16_computed_mask']}")
-        secondary["rolling_fp16_ring"] = bench_rolling(cpk, si, torch, True, ring=True)
-        log(f"bench: rolling {secondary['rolling_fp16_ring']}")
-        secondary["rolling_fp16_ring_computed_mask"] = bench_rolling(cpk, si, torch, False,
-                                                                     ring=True)
-        log(f"bench: rolling {secondary['rolling_fp16_ring_computed_mask']}")
+        variants = {"shift_mask": ("rolling_fp16", True, False),
+                    "shift_computed": ("rolling_fp16_computed_mask", False, False),
+                    "ring_mask": ("rolling_fp16_ring", True, True),
+                    "ring_computed": ("rolling_fp16_ring_computed_mask", False, True)}
+        names = list(variants) if args.rolling == "all" else args.rolling.split(",")
+        for name in names:
+            key, explicit, ring = variants[name]
+            secondary[key] = bench_rolling(cpk, si, torch, explicit, ring=ring)
+            log(f"bench: rolling {secondary[key]}")
     if not args.no_secondary and "mixed" in groups:
         for budget, overlap, paged in ((2048, False, False), (2048, True, False),
                                        (2048, False, True), (8192, False, False),
                                        (8192, True, False)):
+            tag = f"{budget}" + ("_two_streams" if overlap else "") + ("_paged" if paged else "")
+            if args.mixed != "all" and tag not in args.mixed.split(","):
+                continue
             mixed = bench_mixed(cpk, si, torch, budget, overlap, paged=paged)
-            key = (f"mixed_budget_{budget}" + ("_two_streams" if overlap else "") +
-                   ("_paged" if paged else ""))
+            key = f"mixed_budget_{tag}"
             secondary[key] = mixed
             log(f"bench: mixed budget {budget}, {mixed['streams']} stream(s)"
                 f"{', paged' if paged else ''}: "
