@@ -358,6 +358,20 @@ def bench_decode(cpk, si, torch, reps=10):
             "kernel_roofline": own}
 
 
+def rolling_work(L, H, D, C, c, explicit_mask, elem=2):
+    """(visible pairs, algorithmic bytes) of the rolling schedule: L tokens
+    (a multiple of c) in chunks of c over a C-slot window.  Query row i of
+    chunk j (position j*c + i) sees positions max(0, (j+1)*c - C) .. j*c + i.
+    Bytes per chunk: q and out, the K/V of the keys in the window read once,
+    the c new K/V rows written once, and the (c, C) mask when one is passed."""
+    n = L // c
+    pairs = sum(min(C, (j + 1) * c) * c - c * (c - 1) // 2 for j in range(n))
+    row = H * D * elem
+    nbytes = sum(2 * c * row + 2 * min(C, (j + 1) * c) * row + 2 * c * row +
+                 (c * C * elem if explicit_mask else 0) for j in range(n))
+    return pairs, nbytes
+
+
 def issued_pairs(past, width):
     """(query, key) pairs of `width` rows at past: row i sees past + i + 1 keys."""
     return width * past + width * (width + 1) // 2
@@ -428,6 +442,7 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=5):
         vis = (a >= 0) & (a <= p)
         masks.append(torch.where(vis, 0.0, -32768.0).to(torch.float16).contiguous())
         pairs += int(vis.sum())
+    assert pairs == rolling_work(L, H, D, C, c, explicit_mask)[0]
     bufs = [torch.zeros((1, H, C, D), dtype=torch.float16, device="cuda") for _ in range(4)]
     out = torch.empty_like(q)
 
@@ -475,11 +490,7 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=5):
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "replay differs"
     ms = statistics.median(times)
     f = 4 * D * H * pairs
-    # algorithmic bytes per chunk: q and out, K/V of the keys in the window
-    # read once, the c new K/V rows written once, the mask if one is passed
-    row = H * D * 2
-    nbytes = sum(2 * c * row + 2 * min(C, (j + 1) * c) * row + 2 * c * row +
-                 (c * C * 2 if explicit_mask else 0) for j in range(n))
+    nbytes = rolling_work(L, H, D, C, c, explicit_mask)[1]
     t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9) * 1e3
     t_mma = f / (PEAK_BF16_TFLOPS * 1e12) * 1e3
     if t_hbm >= t_mma:
@@ -721,7 +732,7 @@ def cpu_baseline(si, budget_s=6.0):
     # workload 4: the rolling fp16 cache in full (16 chunks)
     rq, rk, rv = (si.storage(x) for x in si.rolling_inputs())
     t = run_timed(lambda: oracle.roll_prefill(rq, rk, rv, 2048, 256, oracle.F16), n_all)
-    pairs = sum(min(2048, (j + 1) * 256) * 256 - (256 * 255) // 2 for j in range(16))
+    pairs = rolling_work(4096, 16, 128, 2048, 256, False)[0]
     table[f"rolling_fp16_threads_{n_all}"] = {
         "value": round(4 * 128 * 16 * pairs / t / 1e12, 6), "unit": "TFLOP/s", "threads": n_all,
         "seconds": round(t, 3),

@@ -38,3 +38,38 @@ def test_ladder_tail_useful_vs_issued():
     # padded to the 171 rung
     assert bench.issued_pairs(1024, 113) == 122153
     assert bench.issued_pairs(1024, 171) == 189810
+
+
+def brute_rolling_pairs(L, C, c):
+    # chunk j holds the window of the last C positions up to its end; query
+    # position p sees the window positions a with a <= p (Horizon blog
+    # "Chunk Prefill", sections 3-4, no left pad)
+    n = 0
+    for j in range(L // c):
+        end = (j + 1) * c
+        window = range(max(0, end - C), end)
+        for i in range(c):
+            p = j * c + i
+            n += sum(1 for a in window if a <= p)
+    return n
+
+
+def test_rolling_pairs_brute_force_and_workload_total():
+    for L, C, c in [(32, 8, 4), (48, 16, 8), (40, 40, 8), (24, 8, 8)]:
+        assert bench.rolling_work(L, 1, 1, C, c, False)[0] == brute_rolling_pairs(L, C, c)
+    # 4096 fp16 tokens, 16 heads, D 128, C 2048, c 256: 49.41 GFLOP visible
+    pairs, _ = bench.rolling_work(4096, 16, 128, 2048, 256, False)
+    assert round(4 * 128 * 16 * pairs / 1e9, 2) == 49.41
+
+
+def test_rolling_bytes_closed_form():
+    # per chunk: q + out (2 c rows), the window's K and V (2 min(C, end)
+    # rows), the new K and V rows written (2 c rows); rows of H*D*2 bytes;
+    # the explicit mask adds c*C*2 bytes per chunk
+    L, H, D, C, c = 4096, 16, 128, 2048, 256
+    row = H * D * 2
+    rows = sum(4 * c + 2 * min(C, (j + 1) * c) for j in range(L // c))
+    _, b0 = bench.rolling_work(L, H, D, C, c, False)
+    _, b1 = bench.rolling_work(L, H, D, C, c, True)
+    assert b0 == rows * row
+    assert b1 - b0 == (L // c) * c * C * 2
