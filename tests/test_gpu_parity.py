@@ -1018,6 +1018,8 @@ def test_decode_rows_every_variant(dtype, D, G):
     vn = si.randn((n, Hkv, D), sdt, g).cuda()
     out = cpk.cpk_varlen_step(q, kn, vn, cache, list(range(n)), list(range(n + 1)), DECODE_PAST)
     torch.cuda.synchronize()
+    # the decode launch appends the new rows itself and records the lengths
+    assert cache.seqlens_k.tolist() == [p + 1 for p in DECODE_PAST]
     worst = 0.0
     for s, p in enumerate(DECODE_PAST):
         nk = p + 1
