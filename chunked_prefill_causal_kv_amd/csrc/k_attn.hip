@@ -1659,7 +1659,12 @@ void attn_sched_kernel(AttnArgs a)
 // part order, M = max_p M_p, f_p = 2^(M_p - M), out = sum_p f_p O_p /
 // sum_p f_p den_p.  Each thread produces 8 consecutive outputs of one
 // (row, head): two 16-byte record loads per part and one 16-byte store.
+// The records of up to kCombineBatch parts are loaded at once (one memory
+// round trip); more parts are merged batch by batch, rescaling the running
+// sums when a later batch raises the maximum (for at most kCombineBatch
+// parts, exactly the two-pass formula above).
 constexpr int kCombineThreads = 256;
+constexpr int kCombineBatch = 4;
 
 template <typename TR, int D>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a)
@@ -1673,24 +1678,43 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
     const int64_t stride = (int64_t)a.out_rows * a.Hq * (D + 4);
     const float *rec = a.part_ws + (int64_t)pair * (D + 4);
     float M = -INFINITY;
-    for (int p = 0; p < a.n_parts; ++p) M = fmaxf(M, rec[p * stride]);
     float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    for (int p = 0; p < a.n_parts; ++p) {
-        const float *r = rec + p * stride;
-        const float2 md = *(const float2 *)r;
-        const float f = (md.x == -INFINITY) ? 0.f : exp2f(md.x - M);
-        const float4 x0 = *(const float4 *)(r + 4 + d0);
-        const float4 x1 = *(const float4 *)(r + 8 + d0);
-        num[0] = __builtin_fmaf(f, x0.x, num[0]);
-        num[1] = __builtin_fmaf(f, x0.y, num[1]);
-        num[2] = __builtin_fmaf(f, x0.z, num[2]);
-        num[3] = __builtin_fmaf(f, x0.w, num[3]);
-        num[4] = __builtin_fmaf(f, x1.x, num[4]);
-        num[5] = __builtin_fmaf(f, x1.y, num[5]);
-        num[6] = __builtin_fmaf(f, x1.z, num[6]);
-        num[7] = __builtin_fmaf(f, x1.w, num[7]);
-        den = __builtin_fmaf(f, md.y, den);
+    for (int p0 = 0; p0 < a.n_parts; p0 += kCombineBatch) {
+        float2 md[kCombineBatch];
+        float4 x0[kCombineBatch], x1[kCombineBatch];
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) {
+            // past the last part: re-read a valid record, weighted 0 below
+            const float *r = rec + (int64_t)min(p0 + i, a.n_parts - 1) * stride;
+            md[i] = *(const float2 *)r;
+            x0[i] = *(const float4 *)(r + 4 + d0);
+            x1[i] = *(const float4 *)(r + 8 + d0);
+        }
+        float bm = M;
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i)
+            if (p0 + i < a.n_parts) bm = fmaxf(bm, md[i].x);
+        if (bm != M) {   // M == -inf: nothing merged yet, the sums are 0
+            const float alpha = M == -INFINITY ? 0.f : exp2f(M - bm);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) num[e] *= alpha;
+            den *= alpha;
+            M = bm;
+        }
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) {
+            const float f = (p0 + i >= a.n_parts || md[i].x == -INFINITY) ? 0.f : exp2f(md[i].x - M);
+            num[0] = __builtin_fmaf(f, x0[i].x, num[0]);
+            num[1] = __builtin_fmaf(f, x0[i].y, num[1]);
+            num[2] = __builtin_fmaf(f, x0[i].z, num[2]);
+            num[3] = __builtin_fmaf(f, x0[i].w, num[3]);
+            num[4] = __builtin_fmaf(f, x1[i].x, num[4]);
+            num[5] = __builtin_fmaf(f, x1[i].y, num[5]);
+            num[6] = __builtin_fmaf(f, x1[i].z, num[6]);
+            num[7] = __builtin_fmaf(f, x1[i].w, num[7]);
+            den = __builtin_fmaf(f, md[i].y, den);
+        }
     }
     uint32_t w[4];
 #pragma unroll
