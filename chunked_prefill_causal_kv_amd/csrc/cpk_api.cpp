@@ -662,9 +662,12 @@ static int roll_attention_impl(const void *q, const void *k, const void *v, cons
         a.seqlens = nullptr;
     }
     const int br = cpk::attn_rows_per_block(dtype, Hq / Hkv, false);
-    r = hip_status(
-        cpk::launch_attention(a, dtype, (c + br - 1) / br, 1, cpk::kAttnNarrow, (hipStream_t)stream),
-        "roll_attention launch");
+    // the narrow kernel (its general form when that is forced)
+    const int kern = g_attn_kernel.load(std::memory_order_relaxed) == CPK_ATTN_NARROW_GENERAL
+                         ? cpk::kAttnNarrowGeneral
+                         : cpk::kAttnNarrow;
+    r = hip_status(cpk::launch_attention(a, dtype, (c + br - 1) / br, 1, kern, (hipStream_t)stream),
+                   "roll_attention launch");
     if (r || parts <= 1) return r;
     return hip_status(cpk::launch_attention_combine(a, dtype, (hipStream_t)stream),
                       "roll_attention combine");

@@ -1307,8 +1307,9 @@ void attn_wide_kernel(AttnArgs a)
 //
 // attn_sched_kernel: the 64-column kernel's work split (8 waves = 2 column
 // groups x 4 key slices of 128-key tiles, tiles double-buffered in LDS) for
-// the plain causal form only (no additive mask, ring buffer, paging or key
-// split), scheduled for latency:
+// launches over a contiguous cache without an explicit additive mask
+// (causal or computed visibility, a ring buffer, a key-range split into
+// parts), scheduled for latency:
 // * all eight K fragment reads of a tile are issued before its first
 //   matrix instruction, so the QK^T chain is not broken by LDS round trips;
 // * the V^T fragments of the tile are read right after the QK^T
@@ -1385,8 +1386,13 @@ void attn_sched_kernel(AttnArgs a)
 
     const int last_row = min(r0 + BR, sv.rows) - 1;
     const int key_end = min(sv.n_keys, sv.causal_base + last_row + 1);   // exclusive
-    const int t_first = sv.key_lo / kBK;
-    const int t_last = (key_end - 1) / kBK;
+    int t_first = sv.key_lo / kBK;
+    int t_last = (key_end - 1) / kBK;
+    if (a.n_parts > 1) {
+        // this workgroup's part of the key range (absolute tiles), possibly empty
+        t_first = max(t_first, (int)blockIdx.y * a.part_tiles);
+        t_last = min(t_last, ((int)blockIdx.y + 1) * a.part_tiles - 1);
+    }
 
     // ---- tile loads: load i of this wave fills LDS chunks
     // [(i*WAVES + wave)*64, +64), one 16-byte chunk per lane: tile row
@@ -1412,12 +1418,17 @@ void attn_sched_kernel(AttnArgs a)
     auto issue_tile = [&](int kt, uint16_t *Kb) {
         uint16_t *Vb = Kb + kBK * D;
         const int key0 = kt * kBK;
-        if (key0 + kBK <= sv.n_keys && key0 + kBK <= new_lo) {
+        // physical row of the tile's first key (rolling ring buffer; the
+        // identity otherwise), and whether the tile's rows stay contiguous
+        int phys0 = key0 + a.ring_start;
+        if (phys0 >= a.cap) phys0 -= a.cap;
+        const bool nowrap = phys0 + kBK <= a.cap;
+        if (key0 + kBK <= sv.n_keys && key0 + kBK <= new_lo && nowrap) {
             // cache rows
 #pragma unroll
             for (int i = 0; i < TL::LOADS; ++i) {
                 const int blk = i * TL::WAVES + wave;
-                const int64_t e = (int64_t)(key0 + i * RSTEP) * D;
+                const int64_t e = (int64_t)(phys0 + i * RSTEP) * D;
                 load16((const char *)(kc + e) + koff, Kb + blk * 64 * 8);
                 load16((const char *)(vc + e) + voff, Vb + blk * 64 * 8);
             }
@@ -1432,22 +1443,16 @@ void attn_sched_kernel(AttnArgs a)
             }
         } else {
             // per-row sources: rows past the last valid key re-read it;
-            // keys at or past new_base come from the new rows (fused)
+            // keys at or past new_base come from the new rows (fused); a
+            // ring tile that wraps maps each row on its own
 #pragma unroll
             for (int i = 0; i < TL::LOADS; ++i) {
                 const int blk = i * TL::WAVES + wave;
                 const int key = min(key0 + i * RSTEP + row0, sv.n_keys - 1);
-                const char *ks_, *vs_;
-                if (key >= new_lo) {
-                    const int64_t e = ((int64_t)min(key - a.new_base, a.new_rows - 1) * a.Hkv + g) * D;
-                    ks_ = (const char *)((const uint16_t *)a.k_new + e + kch);
-                    vs_ = (const char *)((const uint16_t *)a.v_new + e + vch);
-                } else {
-                    ks_ = (const char *)(kc + (int64_t)key * D + kch);
-                    vs_ = (const char *)(vc + (int64_t)key * D + vch);
-                }
-                load16(ks_, Kb + blk * 64 * 8);
-                load16(vs_, Vb + blk * 64 * 8);
+                load16(kv_src(kc, fused ? a.k_new : nullptr, a, g, D, key, (int)kch),
+                       Kb + blk * 64 * 8);
+                load16(kv_src(vc, fused ? a.v_new : nullptr, a, g, D, key, (int)vch),
+                       Vb + blk * 64 * 8);
             }
         }
     };
@@ -1484,6 +1489,7 @@ void attn_sched_kernel(AttnArgs a)
 #pragma unroll
             for (int s = 0; s < NS; ++s) kf[s] = *(const uint4 *)(kr + ((2 * s + hi) ^ sk) * 8);
         }
+        __builtin_amdgcn_sched_barrier(0);   // every K read is issued before the first MFMA
         f32x16_t sacc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
@@ -1507,9 +1513,8 @@ void attn_sched_kernel(AttnArgs a)
                 }
                 vf[db][s2] = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
             }
-        // issue order: the K fragment reads, then each matrix instruction
-        // followed by two of the V^T fragment reads
-        __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);
+        // issue order: each matrix instruction followed by two of the V^T
+        // fragment reads
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -1608,7 +1613,9 @@ void attn_sched_kernel(AttnArgs a)
             den += e * Ls[w * kQC + qc];
             if (w == ks) mine = e;
         }
-        const float f = den > 0.f ? mine / den : 0.f;
+        // split parts keep the slices' sum unnormalised (the combine
+        // normalises over all parts); otherwise normalise here
+        const float f = a.n_parts > 1 ? mine : (den > 0.f ? mine / den : 0.f);
         float *dst = orow(ks, qc);
         const int sw = TL::swz_o(qc);
 #pragma unroll
@@ -1628,7 +1635,37 @@ void attn_sched_kernel(AttnArgs a)
         const int oc = tid / PARTS;
         const int part = tid % PARTS;
         const int row = r0 + oc / G;
-        if (oc < BR * G && row < sv.out_rows) {
+        if (oc < BR * G && row < sv.out_rows && a.n_parts > 1) {
+            // partial record of this part: [M, den, 0, 0, O[D]]
+            const int head = g * G + oc % G;
+            float *rec =
+                a.part_ws + (((int64_t)blockIdx.y * sv.out_rows + row) * a.Hq + head) * (D + 4);
+            if (part == 0) {
+                float M = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) M = fmaxf(M, Ms[w * kQC + oc]);
+                float den = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float mw = Ms[w * kQC + oc];
+                    den += ((mw == -INFINITY) ? 0.f : exp2f(mw - M)) * Ls[w * kQC + oc];
+                }
+                *(float4 *)rec = make_float4(M, den, 0.f, 0.f);
+            }
+            const int sw = TL::swz_o(oc);
+#pragma unroll
+            for (int d4 = 0; d4 < DP; d4 += 4) {
+                const int d = part * DP + d4;
+                const int off = 4 * ((d >> 2) ^ sw);
+                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) {
+                    const float4 y = *(const float4 *)(orow(w4, oc) + off);
+                    x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+                }
+                *(float4 *)(rec + 4 + d) = x;
+            }
+        } else if (oc < BR * G && row < sv.out_rows) {
             const int head = g * G + oc % G;
             uint16_t *op = (uint16_t *)a.out + ((int64_t)(sv.out_row0 + row) * a.Hq + head) * D +
                            part * DP;
@@ -1861,8 +1898,9 @@ hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_
                             int kernel, hipStream_t st)
 {
     const dim3 grid(row_blocks * a.Hkv, a.n_parts > 1 ? a.n_parts : 1, n_seq_grid);
-    // the scheduled form covers the plain causal launch
-    const bool plain = !a.mask && a.ring_start == 0 && a.block_size == 0 && a.n_parts <= 1;
+    // the scheduled form covers every contiguous-cache launch without an
+    // explicit mask (causal or computed visibility, ring buffer, key split)
+    const bool plain = !a.mask && a.block_size == 0;
     if (kernel == kAttnWide && dtype != 0) {
         CPK_LAUNCH_MFMA(attn_wide_kernel, kWThreads);
     } else if (dtype == 0) {

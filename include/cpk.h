@@ -445,18 +445,20 @@ int cpk_version(void);
 
 /*
  * Which bf16/fp16 kernel serves chunk attention (cpk_chunk_attention,
- * cpk_prefill_chunk) and the prompt rows of cpk_varlen_step; fp32 and the
- * rolling form (cpk_roll_attention) are unaffected.  Both kernels compute
- * the same attention to within rounding; each alone is deterministic and
- * gives a row the same bits whether its prompt runs in one pass or in
- * chunks.  CPK_ATTN_AUTO takes the wide kernel when its launch has at
- * least as many workgroups as the GPU has compute units (256), else the
- * narrow one.  The narrow kernel runs in a latency-scheduled form wherever
- * the launch is the plain causal one (no additive mask, ring buffer, paging
- * or key split) and in its general form otherwise; the two forms give
- * identical bits, and CPK_ATTN_NARROW_GENERAL forces the general form.  The
- * setting is process-wide and meant for diagnostics and tests; it returns
- * the previous setting, or CPK_EINVAL for an unknown kind.
+ * cpk_prefill_chunk) and the prompt rows of cpk_varlen_step; fp32 is
+ * unaffected, and the rolling forms (cpk_roll_attention, cpk_ring_*)
+ * always take the narrow kernel (only CPK_ATTN_NARROW_GENERAL applies to
+ * them).  Both kernels compute the same attention to within rounding; each
+ * alone is deterministic and gives a row the same bits whether its prompt
+ * runs in one pass or in chunks.  CPK_ATTN_AUTO takes the wide kernel when
+ * its launch has at least as many workgroups as the GPU has compute units
+ * (256), else the narrow one.  The narrow kernel runs in a latency-scheduled
+ * form wherever the launch reads a contiguous cache without an explicit
+ * additive mask (causal or computed visibility, ring buffer, key split) and
+ * in its general form otherwise (mask, paging); the two forms give identical
+ * bits, and CPK_ATTN_NARROW_GENERAL forces the general form.  The setting is
+ * process-wide and meant for diagnostics and tests; it returns the previous
+ * setting, or CPK_EINVAL for an unknown kind.
  */
 int cpk_set_attention_kernel(int kind);
 

@@ -579,6 +579,51 @@ def test_ring_step_fused_matches_two_calls(dtype, C, c, Hq, Hkv, D):
                 assert bitwise(kb, ka) and bitwise(vb, va), f"{tag}: rings differ"
 
 
+@pytest.mark.parametrize("dtype,C,c,Hq,Hkv,D", [
+    ("f16", 512, 128, 4, 4, 128),     # start walks 0, 128, 256, 384 and wraps
+    ("bf16", 300, 96, 4, 2, 64),      # tiles that wrap the ring mid-tile, GQA
+])
+def test_scheduled_form_bit_equal_to_general_rolling(dtype, C, c, Hq, Hkv, D):
+    """Rolling launches (ring buffer, computed visibility, split into parts
+    and unsplit, the chunk's append fused in) give the same bits in the
+    latency-scheduled and the general form of the 64-column kernel: the
+    output of every chunk and both rings after it; the scheduled form also
+    matches the oracle's sliding window."""
+    say(f"case: scheduled vs general rolling {dtype} C={C} c={c} heads {Hq}/{Hkv} D={D}")
+    tdt = si.TORCH_DTYPE[dtype]
+    g = si.generator(530 + C)
+    n = 5
+    q = si.randn((n * c, Hq, D), dtype, g).cuda()
+    k = si.randn((n * c, Hkv, D), dtype, g).cuda()
+    v = si.randn((n * c, Hkv, D), dtype, g).cuda()
+    for split in (True, False):
+        res = {}
+        for kind in ("narrow", "general"):
+            with cpk.attention_kernel(KERNELS[kind]):
+                kr = torch.zeros((1, Hkv, C, D), dtype=tdt, device="cuda")
+                vr = torch.zeros_like(kr)
+                start, outs = 0, []
+                for j in range(n):
+                    sl = slice(j * c, (j + 1) * c)
+                    o, start = cpk.cpk_ring_step(q[sl], k[sl], v[sl], kr[0], vr[0],
+                                                 (j + 1) * c, 0, start, split=split)
+                    outs.append(o)
+                torch.cuda.synchronize()
+                res[kind] = (torch.cat(outs), kr, vr)
+        (oa, ka, va), (ob, kb, vb) = res["narrow"], res["general"]
+        assert bitwise(oa, ob), f"split={split}: outputs differ"
+        assert bitwise(ka, kb) and bitwise(va, vb), f"split={split}: rings differ"
+    odt = ODT[tdt]
+    L = n * c
+    rows = np.arange(L)
+    qq = oracle.widen(si.storage(q), odt)
+    kk = oracle.widen(np.ascontiguousarray(si.storage(k).transpose(1, 0, 2)), odt)
+    vv = oracle.widen(np.ascontiguousarray(si.storage(v).transpose(1, 0, 2)), odt)
+    lo = np.maximum(0, (rows // c + 1) * c - C).astype(np.int32)
+    ref = oracle.attention(qq, kk, vv, lo, rows.astype(np.int32), 1.0 / math.sqrt(D))
+    check(res["narrow"][0], ref, TOL[tdt], "scheduled rolling vs sliding-window oracle")
+
+
 def test_workload4_ring_full_size():
     L, C, c, H, D = 4096, 2048, 256, 16, 128
     say(f"case: workload 4 on the ring buffer, L={L} C={C} c={c} H={H}: bit-equal to the shift")
