@@ -1307,9 +1307,9 @@ void attn_wide_kernel(AttnArgs a)
 //
 // attn_sched_kernel: the 64-column kernel's work split (8 waves = 2 column
 // groups x 4 key slices of 128-key tiles, tiles double-buffered in LDS) for
-// launches over a contiguous cache without an explicit additive mask
-// (causal or computed visibility, a ring buffer, a key-range split into
-// parts), scheduled for latency:
+// launches over a contiguous cache (causal, computed or explicit additive
+// mask visibility, a ring buffer, a key-range split into parts; a paged
+// pool takes attn_mfma_kernel), scheduled for latency:
 // * all eight K fragment reads of a tile are issued before its first
 //   matrix instruction, so the QK^T chain is not broken by LDS round trips;
 // * the V^T fragments of the tile are read right after the QK^T
@@ -1324,7 +1324,7 @@ void attn_wide_kernel(AttnArgs a)
 // Arithmetic, fragment layouts, swizzles, the lazy maximum, the epilogue
 // merge and the fused append are those of attn_mfma_kernel, so results are
 // bit-identical to it.
-template <typename TR, int D>
+template <typename TR, int D, bool MASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_sched_kernel(AttnArgs a)
 {
@@ -1370,7 +1370,7 @@ void attn_sched_kernel(AttnArgs a)
 
     // ---- query fragment (B operand of S^T = K Q^T): column qc
     uint4 qf[NS];
-    int lim;
+    int lim, qrow;
     {
         const int row = r0 + qc / G;
         const bool ok = (qc < BR * G) && (row < sv.rows);
@@ -1378,6 +1378,7 @@ void attn_sched_kernel(AttnArgs a)
         const int srow = rr < sv.q_src_rows ? rr : sv.q_src_rows - 1;
         const int head = g * G + (ok ? qc % G : 0);
         lim = min(sv.causal_base + rr, sv.n_keys - 1);
+        qrow = rr;
         const uint16_t *qp =
             (const uint16_t *)a.q + ((int64_t)(sv.q_row0 + srow) * a.Hq + head) * D + 8 * hi;
 #pragma unroll
@@ -1465,6 +1466,27 @@ void attn_sched_kernel(AttnArgs a)
     float m_run = -INFINITY;
     float l_run = 0.f;
     const float c = a.scale_log2;
+    const float inv_scale = 1.0f / a.scale;
+
+    // Explicit additive mask (rolling form).  With an 8-byte aligned mask
+    // whose row length is a multiple of 4, the lane's 16 keys of a tile are
+    // 4 runs of 4 consecutive keys: one 8-byte load per run (a run starting
+    // at or past the row's end is re-read from the row's last run; those
+    // keys are masked out whatever the values), loaded one tile ahead behind
+    // the next tile's loads, so the wait at the start of a tile covers them.
+    // (a compile-time choice: MASK instances serve launches with a mask)
+    const uint16_t *maskp = MASK ? (const uint16_t *)a.mask : nullptr;
+    const uint16_t *mrow = MASK ? maskp + (int64_t)qrow * a.mask_ld : nullptr;
+    const bool mfast = MASK && (a.mask_ld & 3) == 0 && ((uintptr_t)maskp & 7u) == 0;
+    uint2 mnext[4];
+    auto load_mask = [&](int kt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key0 = min(kt * kBK + ks * 32 + 8 * r + 4 * hi, a.mask_ld - 4);
+            mnext[r] = *(const uint2 *)(mrow + key0);
+        }
+    };
+    if (MASK && mfast && t_last >= t_first) load_mask(t_first);
 
     const int g16 = (lane >> 4) & 1;
     const int si = lane & 15;
@@ -1477,7 +1499,30 @@ void attn_sched_kernel(AttnArgs a)
         __syncthreads();                   // ... and every wave's; `next` is free again
         if (kt == t_first && app_on)
             append_store<D, kThreads, 0, 1>(a, g, r0, app_rows, tid, app, true);
-        if (kt < t_last) issue_tile(kt + 1, next);
+        float mvals[16];
+        if constexpr (!MASK) {
+        } else if (mfast) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                mvals[4 * r + 0] = TR::to_f32(mnext[r].x & 0xffffu);
+                mvals[4 * r + 1] = TR::to_f32(mnext[r].x >> 16);
+                mvals[4 * r + 2] = TR::to_f32(mnext[r].y & 0xffffu);
+                mvals[4 * r + 3] = TR::to_f32(mnext[r].y >> 16);
+            }
+        } else {
+            // other layouts: element loads of this tile, issued before the
+            // next tile's loads so that waiting for them does not wait for those
+            const int kb0 = kt * kBK + ks * 32;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = kb0 + 8 * (j >> 2) + 4 * hi + (j & 3);
+                mvals[j] = TR::to_f32(mrow[key < sv.n_keys ? key : sv.n_keys - 1]);
+            }
+        }
+        if (kt < t_last) {
+            issue_tile(kt + 1, next);
+            if (MASK && mfast) load_mask(kt + 1);
+        }
         const uint16_t *Vb = Kb + kBK * D;
 
         // S^T[32 keys x 32 cols]: every K fragment read, then the chain
@@ -1527,7 +1572,17 @@ void attn_sched_kernel(AttnArgs a)
         const int kbase = kt * kBK + ks * 32;
         const bool full = (kt * kBK >= sv.key_lo) && ((kt + 1) * kBK <= sv.n_keys) &&
                           ((kt + 1) * kBK - 1 <= sv.causal_base + r0);
-        if (!full) {
+        if constexpr (MASK) {
+            // additive mask; entries at or below the fill value (-32768)
+            // exclude the slot (their weight underflows to exactly 0
+            // whenever the row sees any slot)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
+                const bool vis = key >= sv.key_lo && key < sv.n_keys && mvals[j] > -32768.0f;
+                sacc[j] = vis ? sacc[j] + mvals[j] * inv_scale : -INFINITY;
+            }
+        } else if (!full) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int key = kbase + 8 * (j >> 2) + 4 * hi + (j & 3);
@@ -1898,9 +1953,9 @@ hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_
                             int kernel, hipStream_t st)
 {
     const dim3 grid(row_blocks * a.Hkv, a.n_parts > 1 ? a.n_parts : 1, n_seq_grid);
-    // the scheduled form covers every contiguous-cache launch without an
-    // explicit mask (causal or computed visibility, ring buffer, key split)
-    const bool plain = !a.mask && a.block_size == 0;
+    // the scheduled form covers every launch over a contiguous cache
+    // (causal, computed or explicit-mask visibility, ring buffer, key split)
+    const bool plain = a.block_size == 0;
     if (kernel == kAttnWide && dtype != 0) {
         CPK_LAUNCH_MFMA(attn_wide_kernel, kWThreads);
     } else if (dtype == 0) {
@@ -1909,12 +1964,23 @@ hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_
         else
             hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, st, a);
     } else if (kernel == kAttnNarrow && plain) {
+        const dim3 blk(kThreads);
         if (dtype == 1) {
-            if (a.D == 64) hipLaunchKernelGGL((attn_sched_kernel<F16, 64>), grid, dim3(kThreads), 0, st, a);
-            else hipLaunchKernelGGL((attn_sched_kernel<F16, 128>), grid, dim3(kThreads), 0, st, a);
+            if (a.D == 64) {
+                if (a.mask) hipLaunchKernelGGL((attn_sched_kernel<F16, 64, true>), grid, blk, 0, st, a);
+                else hipLaunchKernelGGL((attn_sched_kernel<F16, 64, false>), grid, blk, 0, st, a);
+            } else {
+                if (a.mask) hipLaunchKernelGGL((attn_sched_kernel<F16, 128, true>), grid, blk, 0, st, a);
+                else hipLaunchKernelGGL((attn_sched_kernel<F16, 128, false>), grid, blk, 0, st, a);
+            }
         } else {
-            if (a.D == 64) hipLaunchKernelGGL((attn_sched_kernel<Bf16, 64>), grid, dim3(kThreads), 0, st, a);
-            else hipLaunchKernelGGL((attn_sched_kernel<Bf16, 128>), grid, dim3(kThreads), 0, st, a);
+            if (a.D == 64) {
+                if (a.mask) hipLaunchKernelGGL((attn_sched_kernel<Bf16, 64, true>), grid, blk, 0, st, a);
+                else hipLaunchKernelGGL((attn_sched_kernel<Bf16, 64, false>), grid, blk, 0, st, a);
+            } else {
+                if (a.mask) hipLaunchKernelGGL((attn_sched_kernel<Bf16, 128, true>), grid, blk, 0, st, a);
+                else hipLaunchKernelGGL((attn_sched_kernel<Bf16, 128, false>), grid, blk, 0, st, a);
+            }
         }
     } else {
         CPK_LAUNCH_MFMA(attn_mfma_kernel, kThreads);

@@ -584,11 +584,11 @@ def test_ring_step_fused_matches_two_calls(dtype, C, c, Hq, Hkv, D):
     ("bf16", 300, 96, 4, 2, 64),      # tiles that wrap the ring mid-tile, GQA
 ])
 def test_scheduled_form_bit_equal_to_general_rolling(dtype, C, c, Hq, Hkv, D):
-    """Rolling launches (ring buffer, computed visibility, split into parts
-    and unsplit, the chunk's append fused in) give the same bits in the
-    latency-scheduled and the general form of the 64-column kernel: the
-    output of every chunk and both rings after it; the scheduled form also
-    matches the oracle's sliding window."""
+    """Rolling launches (ring buffer, computed visibility and the explicit
+    additive mask, split into parts and unsplit, the chunk's append fused
+    in) give the same bits in the latency-scheduled and the general form of
+    the 64-column kernel: the output of every chunk and both rings after
+    it; the scheduled form also matches the oracle's sliding window."""
     say(f"case: scheduled vs general rolling {dtype} C={C} c={c} heads {Hq}/{Hkv} D={D}")
     tdt = si.TORCH_DTYPE[dtype]
     g = si.generator(530 + C)
@@ -596,25 +596,29 @@ def test_scheduled_form_bit_equal_to_general_rolling(dtype, C, c, Hq, Hkv, D):
     q = si.randn((n * c, Hq, D), dtype, g).cuda()
     k = si.randn((n * c, Hkv, D), dtype, g).cuda()
     v = si.randn((n * c, Hkv, D), dtype, g).cuda()
-    for split in (True, False):
-        res = {}
-        for kind in ("narrow", "general"):
-            with cpk.attention_kernel(KERNELS[kind]):
-                kr = torch.zeros((1, Hkv, C, D), dtype=tdt, device="cuda")
-                vr = torch.zeros_like(kr)
-                start, outs = 0, []
-                for j in range(n):
-                    sl = slice(j * c, (j + 1) * c)
-                    o, start = cpk.cpk_ring_step(q[sl], k[sl], v[sl], kr[0], vr[0],
-                                                 (j + 1) * c, 0, start, split=split)
-                    outs.append(o)
-                torch.cuda.synchronize()
-                res[kind] = (torch.cat(outs), kr, vr)
-        (oa, ka, va), (ob, kb, vb) = res["narrow"], res["general"]
-        assert bitwise(oa, ob), f"split={split}: outputs differ"
-        assert bitwise(ka, kb) and bitwise(va, vb), f"split={split}: rings differ"
-    odt = ODT[tdt]
     L = n * c
+    masks = [torch.from_numpy(oracle.chunk_mask(L, 0, j, c, C)).to(tdt).cuda() for j in range(n)]
+    for split in (True, False):
+        for explicit in (False, True):
+            res = {}
+            for kind in ("narrow", "general"):
+                with cpk.attention_kernel(KERNELS[kind]):
+                    kr = torch.zeros((1, Hkv, C, D), dtype=tdt, device="cuda")
+                    vr = torch.zeros_like(kr)
+                    start, outs = 0, []
+                    for j in range(n):
+                        sl = slice(j * c, (j + 1) * c)
+                        o, start = cpk.cpk_ring_step(q[sl], k[sl], v[sl], kr[0], vr[0],
+                                                     (j + 1) * c, 0, start, split=split,
+                                                     mask=masks[j] if explicit else None)
+                        outs.append(o)
+                    torch.cuda.synchronize()
+                    res[kind] = (torch.cat(outs), kr, vr)
+            (oa, ka, va), (ob, kb, vb) = res["narrow"], res["general"]
+            tag = f"split={split} mask={explicit}"
+            assert bitwise(oa, ob), f"{tag}: outputs differ"
+            assert bitwise(ka, kb) and bitwise(va, vb), f"{tag}: rings differ"
+    odt = ODT[tdt]
     rows = np.arange(L)
     qq = oracle.widen(si.storage(q), odt)
     kk = oracle.widen(np.ascontiguousarray(si.storage(k).transpose(1, 0, 2)), odt)
