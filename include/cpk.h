@@ -453,10 +453,10 @@ int cpk_version(void);
  * runs in one pass or in chunks.  CPK_ATTN_AUTO takes the wide kernel when
  * its launch has at least as many workgroups as the GPU has compute units
  * (256), else the narrow one.  The narrow kernel runs in a latency-scheduled
- * form wherever the launch reads a contiguous cache without an explicit
- * additive mask (causal or computed visibility, ring buffer, key split) and
- * in its general form otherwise (mask, paging); the two forms give identical
- * bits, and CPK_ATTN_NARROW_GENERAL forces the general form.  The setting is
+ * form wherever the launch reads a contiguous cache (causal, computed or
+ * explicit-mask visibility, ring buffer, key split) and in its general form
+ * over a paged pool; the two forms give identical bits, and
+ * CPK_ATTN_NARROW_GENERAL forces the general form.  The setting is
  * process-wide and meant for diagnostics and tests; it returns the previous
  * setting, or CPK_EINVAL for an unknown kind.
  */
