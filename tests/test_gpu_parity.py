@@ -138,8 +138,8 @@ def test_fp32_demo_chunked_and_one_shot():
 # ----------------------------------------------- GQA shapes, full compare
 
 # narrow: the 64-column kernel (its latency-scheduled form wherever the launch
-# is plain causal), wide: the 128-column kernel, general: the 64-column
-# kernel's general form everywhere
+# reads a contiguous cache), wide: the 128-column kernel, general: the
+# 64-column kernel's general form everywhere
 KERNELS = {"narrow": 1, "wide": 2, "general": 3}
 
 
