@@ -582,6 +582,7 @@ def test_ring_step_fused_matches_two_calls(dtype, C, c, Hq, Hkv, D):
 @pytest.mark.parametrize("dtype,C,c,Hq,Hkv,D", [
     ("f16", 512, 128, 4, 4, 128),     # start walks 0, 128, 256, 384 and wraps
     ("bf16", 300, 96, 4, 2, 64),      # tiles that wrap the ring mid-tile, GQA
+    ("f16", 301, 100, 2, 2, 64),      # mask rows of 301 entries: per-element mask loads
 ])
 def test_scheduled_form_bit_equal_to_general_rolling(dtype, C, c, Hq, Hkv, D):
     """Rolling launches (ring buffer, computed visibility and the explicit
