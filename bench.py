@@ -281,8 +281,9 @@ def bench_demo_fp32(cpk, si, torch, reps=20):
             "note": "eager calls (rewind + 4 chunk launches), HIP events over 20 passes"}
 
 
-def bench_steady_chunk(cpk, si, torch, reps=20):
-    """One W=512 chunk at past_len 7680 (cache 8192): steady-state point."""
+def bench_steady_chunk(cpk, si, torch, reps=200, warm=50):
+    """One W=512 chunk at past_len 7680 (cache 8192): steady-state point,
+    HIP events around reps back-to-back launches after warm ones."""
     Hq, Hkv, D, P, W = 32, 8, 128, 7680, 512
     cache = cpk.KVCache(1, Hkv, 8192, D, torch.bfloat16)
     si.fill_seeded(cache.k, 11)
@@ -290,7 +291,7 @@ def bench_steady_chunk(cpk, si, torch, reps=20):
     q = si.randn((W, Hq, D), "bf16", si.generator(13)).cuda()
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
-    for _ in range(3):
+    for _ in range(warm):
         cpk.cpk_chunk_attention(q, cache, 0, P, out=out)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -304,7 +305,7 @@ def bench_steady_chunk(cpk, si, torch, reps=20):
             "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
 
 
-def bench_decode(cpk, si, torch, reps=10):
+def bench_decode(cpk, si, torch, reps=100, warm=20):
     """Decode rows of the mixed-step workload as a decode-only packed step."""
     Hq, Hkv, D, CAP = 32, 8, 128, 16400
     ctxs = si.mixed_contexts()
@@ -324,7 +325,7 @@ def bench_decode(cpk, si, torch, reps=10):
                      dtype=torch.float32, device="cuda")
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
-    for _ in range(3):
+    for _ in range(warm):
         cpk.cpk_varlen_step(q, kn, vn, cache, slots, cu, ctxs, out=out, ws=ws, dev_meta=meta)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -358,7 +359,8 @@ def bench_decode(cpk, si, torch, reps=10):
                          "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
                          "traffic": read_traffic(sha, DECODE_TRAFFIC_FILE),
                          "kernel": "decode_kernel<bf16,128,4> + decode_combine (whole step)",
-                         "timer": "HIP events around 10 back-to-back steps on the launch stream",
+                         "timer": f"HIP events around {reps} back-to-back steps on the launch "
+                                  f"stream after {warm}",
                          "kernel_source_sha": sha},
             "kernel_roofline": own}
 
@@ -382,11 +384,12 @@ def issued_pairs(past, width):
     return width * past + width * (width + 1) // 2
 
 
-def bench_ladder(cpk, si, torch, reps=2):
+def bench_ladder(cpk, si, torch, reps=2, passes=10, warm=3):
     """Ladder workload: seven prompts (five seeded lengths, 1137, 1200), each
     prefilled twice on the same cache without clearing, through
     cpk_prefill_chunk with padding on.  Useful flops count real rows only,
-    issued flops the padded widths."""
+    issued flops the padded widths.  ms is one pass over the workload, the
+    average of `passes` timed passes after `warm` untimed ones."""
     Hq, Hkv, D, W, CAP = 32, 8, 128, 512, 8192
     lengths = si.ladder_prompt_lengths()
     prompts = [tuple(x.cuda() for x in si.gqa_prompt(L=L, seed=200 + i))
@@ -409,15 +412,17 @@ def bench_ladder(cpk, si, torch, reps=2):
                     cpk.cpk_prefill_chunk(q[sl], k[sl], v[sl], cache, 0, past, W, pad=True,
                                           out=out[sl])
 
-    run()
+    for _ in range(warm):
+        run()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    run()
+    for _ in range(passes):
+        run()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
+    ms = e0.elapsed_time(e1) / passes
     f_useful = 4 * D * Hq * useful * reps
     f_issued = 4 * D * Hq * issued * reps
     return {"prompts": lengths, "runs_each": reps, "ms": round(ms, 3),
@@ -427,7 +432,7 @@ def bench_ladder(cpk, si, torch, reps=2):
             "note": "eager cpk_prefill_chunk calls (append + attention per chunk)"}
 
 
-def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=5):
+def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=50, warm=10):
     """Rolling right-aligned cache: 4096 fp16 tokens, 16 heads, C = 2048,
     c = 256; per chunk roll_append (out of place, double-buffered: C rows
     moved) then roll_attention, or with ring=True one cpk_ring_step (the c
@@ -483,6 +488,8 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=5):
         run()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        graph.replay()
     times = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -513,10 +520,10 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=5):
     return {"chunks": n, "gflop": round(f / 1e9, 2), "ms": round(ms, 4), "ms_min": round(min(times), 4),
             "tflops": round(f / (ms * 1e-3) / 1e12, 1), "dtype": "fp16", "roofline": roof,
             "note": f"{what} with {how}, per chunk; 16 chunks replayed as a HIP graph, "
-                    f"median of {reps} replays"}
+                    f"median of {reps} replays after {warm}"}
 
 
-def bench_mixed(cpk, si, torch, budget, overlap=False, reps=3, paged=False):
+def bench_mixed(cpk, si, torch, budget, overlap=False, reps=10, paged=False, warm=3):
     """Mixed step: 64 running decodes (contexts U[512, 16384]) plus a
     20,000-token prompt under a token budget, one packed step per budget
     (packed inputs built before timing): cpk_varlen_step, or with
@@ -599,6 +606,8 @@ def bench_mixed(cpk, si, torch, budget, overlap=False, reps=3, paged=False):
     with torch.cuda.graph(graph):
         run()
     torch.cuda.synchronize()
+    for _ in range(warm):
+        graph.replay()
     g_ms = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
