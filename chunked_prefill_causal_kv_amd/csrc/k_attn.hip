@@ -1320,7 +1320,9 @@ void attn_wide_kernel(AttnArgs a)
 //   consecutive matrix instructions do not depend on each other;
 // * tiles that lie entirely inside the chunk's new rows (fused append) are
 //   loaded with per-lane offsets precomputed for the new rows' stride,
-//   without per-row source selection.
+//   without per-row source selection;
+// * the next tile's direct-to-LDS loads are issued by column group 0
+//   alone, so group 1's waves never stall on the address unit.
 // Arithmetic, fragment layouts, swizzles, the lazy maximum, the epilogue
 // merge and the fused append are those of attn_mfma_kernel, so results are
 // bit-identical to it.
@@ -1395,16 +1397,22 @@ void attn_sched_kernel(AttnArgs a)
         t_last = min(t_last, ((int)blockIdx.y + 1) * a.part_tiles - 1);
     }
 
-    // ---- tile loads: load i of this wave fills LDS chunks
-    // [(i*WAVES + wave)*64, +64), one 16-byte chunk per lane: tile row
-    // i*RSTEP + row0 (RSTEP = WAVES*64/NCH rows apart), chunk pos.  The
-    // swizzles depend on the row modulo NCH, which RSTEP leaves unchanged,
-    // so one per-lane offset serves every load of the tile and load i adds
-    // a uniform i*RSTEP rows to the (scalar) base: byte offsets for cache
-    // rows (stride D) and for the new rows (stride Hkv*D).
-    constexpr int RSTEP = TL::WAVES * 64 / NCH;
+    // ---- tile loads, issued by column group 0 alone (waves 0-3, one per
+    // SIMD): a wave stalls while the address unit works through its loads,
+    // and group 0 reaches the tile barrier early, so it absorbs that stall
+    // while group 1's waves keep their matrix work going.  Load i of loader
+    // wave lw fills LDS chunks [(i*LW + lw)*64, +64), one 16-byte chunk per
+    // lane: tile row i*RSTEP + row0 (RSTEP = LW*64/NCH rows apart), chunk
+    // pos.  The swizzles depend on the row modulo NCH, which RSTEP leaves
+    // unchanged, so one per-lane offset serves every load of the tile and
+    // load i adds a uniform i*RSTEP rows to the (scalar) base: byte offsets
+    // for cache rows (stride D) and for the new rows (stride Hkv*D).
+    constexpr int LW = TL::WAVES / 2;
+    const int lw = qg == 0 ? wave : -1;
+    constexpr int RSTEP = LW * 64 / NCH;
+    constexpr int NLD = kBK / RSTEP;
     static_assert(RSTEP % NCH == 0, "row step keeps the swizzle");
-    const int row0 = (wave * 64 + lane) / NCH;
+    const int row0 = ((lw < 0 ? 0 : lw) * 64 + lane) / NCH;
     const int pos0 = lane % NCH;
     const uint32_t kch = (uint32_t)((pos0 ^ TL::swz_k(row0)) * 8);
     const uint32_t vch = (uint32_t)((pos0 ^ TL::swz_v(row0)) * 8);
@@ -1416,7 +1424,8 @@ void attn_sched_kernel(AttnArgs a)
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
                                          (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
     };
-    auto issue_tile = [&](int kt, uint16_t *Kb) {
+    auto issue_tile = [&](int kt, uint16_t *Kb) __attribute__((always_inline)) {
+        if (lw < 0) return;   // wave-uniform: group 1 issues no loads
         uint16_t *Vb = Kb + kBK * D;
         const int key0 = kt * kBK;
         // physical row of the tile's first key (rolling ring buffer; the
@@ -1427,8 +1436,8 @@ void attn_sched_kernel(AttnArgs a)
         if (key0 + kBK <= sv.n_keys && key0 + kBK <= new_lo && nowrap) {
             // cache rows
 #pragma unroll
-            for (int i = 0; i < TL::LOADS; ++i) {
-                const int blk = i * TL::WAVES + wave;
+            for (int i = 0; i < NLD; ++i) {
+                const int blk = i * LW + lw;
                 const int64_t e = (int64_t)(phys0 + i * RSTEP) * D;
                 load16((const char *)(kc + e) + koff, Kb + blk * 64 * 8);
                 load16((const char *)(vc + e) + voff, Vb + blk * 64 * 8);
@@ -1436,8 +1445,8 @@ void attn_sched_kernel(AttnArgs a)
         } else if (key0 >= new_lo && key0 + kBK <= new_hi) {
             // new rows of the chunk (fused append), no clamping needed
 #pragma unroll
-            for (int i = 0; i < TL::LOADS; ++i) {
-                const int blk = i * TL::WAVES + wave;
+            for (int i = 0; i < NLD; ++i) {
+                const int blk = i * LW + lw;
                 const int64_t e = ((int64_t)(key0 - a.new_base + i * RSTEP) * a.Hkv + g) * D;
                 load16((const char *)((const uint16_t *)a.k_new + e) + nkoff, Kb + blk * 64 * 8);
                 load16((const char *)((const uint16_t *)a.v_new + e) + nvoff, Vb + blk * 64 * 8);
@@ -1447,8 +1456,8 @@ void attn_sched_kernel(AttnArgs a)
             // keys at or past new_base come from the new rows (fused); a
             // ring tile that wraps maps each row on its own
 #pragma unroll
-            for (int i = 0; i < TL::LOADS; ++i) {
-                const int blk = i * TL::WAVES + wave;
+            for (int i = 0; i < NLD; ++i) {
+                const int blk = i * LW + lw;
                 const int key = min(key0 + i * RSTEP + row0, sv.n_keys - 1);
                 load16(kv_src(kc, fused ? a.k_new : nullptr, a, g, D, key, (int)kch),
                        Kb + blk * 64 * 8);
