@@ -1322,7 +1322,11 @@ void attn_wide_kernel(AttnArgs a)
 //   loaded with per-lane offsets precomputed for the new rows' stride,
 //   without per-row source selection;
 // * the next tile's direct-to-LDS loads are issued by column group 0
-//   alone, so group 1's waves never stall on the address unit.
+//   alone, so group 1's waves never stall on the address unit;
+// * the workgroup's query rows are read from global memory once, into LDS
+//   by column group 1 beside the first tile's loads (the four key-slice
+//   waves of a column group need the same query fragments), and each wave
+//   takes its fragments from LDS after the first tile's barrier.
 // Arithmetic, fragment layouts, swizzles, the lazy maximum, the epilogue
 // merge and the fused append are those of attn_mfma_kernel, so results are
 // bit-identical to it.
@@ -1338,6 +1342,7 @@ void attn_sched_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t buf0[TL::STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t buf1[TL::STAGE];
     __shared__ float ml[2 * 4 * kQC];
+    __shared__ __attribute__((aligned(16))) uint16_t qbuf[kQC * D];   // the workgroup's query rows
 
     SeqView sv;
     if (!resolve_seq(a, blockIdx.z, sv)) return;
@@ -1370,22 +1375,45 @@ void attn_sched_kernel(AttnArgs a)
                                                                         false);
     }
 
-    // ---- query fragment (B operand of S^T = K Q^T): column qc
+    // ---- query fragment (B operand of S^T = K Q^T): column qc.  The
+    // 64 columns' query rows are read once per workgroup into LDS by column
+    // group 1 (chunk p of column c stored at p ^ (c mod NCH)), and every wave
+    // takes its fragments from there after the first tile's barrier.
     uint4 qf[NS];
     int lim, qrow;
     {
         const int row = r0 + qc / G;
         const bool ok = (qc < BR * G) && (row < sv.rows);
         const int rr = ok ? row : r0;
-        const int srow = rr < sv.q_src_rows ? rr : sv.q_src_rows - 1;
-        const int head = g * G + (ok ? qc % G : 0);
         lim = min(sv.causal_base + rr, sv.n_keys - 1);
         qrow = rr;
-        const uint16_t *qp =
-            (const uint16_t *)a.q + ((int64_t)(sv.q_row0 + srow) * a.Hq + head) * D + 8 * hi;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) qf[s] = *(const uint4 *)(qp + 16 * s);
     }
+    if (qg == 1) {
+        constexpr int QLD = kQC * NCH / (4 * 64);   // 1 KB loads per group-1 wave
+#pragma unroll
+        for (int i = 0; i < QLD; ++i) {
+            const int blk = i * 4 + (wave - 4);
+            const int t = blk * 64 + lane;          // destination chunk
+            const int col = t / NCH;
+            const int pch = (t % NCH) ^ (col % NCH);  // source chunk
+            const int row = r0 + col / G;
+            const bool ok = (col < BR * G) && (row < sv.rows);
+            const int rr = ok ? row : r0;
+            const int srow = rr < sv.q_src_rows ? rr : sv.q_src_rows - 1;
+            const int head = g * G + (ok ? col % G : 0);
+            const uint16_t *src =
+                (const uint16_t *)a.q + ((int64_t)(sv.q_row0 + srow) * a.Hq + head) * D + pch * 8;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)(qbuf + blk * 64 * 8),
+                                             16, 0, 0);
+        }
+    }
+    auto read_q = [&]() __attribute__((always_inline)) {
+        const uint16_t *qr = qbuf + qc * D;
+        const int sq = qc % NCH;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qf[s] = *(const uint4 *)(qr + ((2 * s + hi) ^ sq) * 8);
+    };
 
     const int last_row = min(r0 + BR, sv.rows) - 1;
     const int key_end = min(sv.n_keys, sv.causal_base + last_row + 1);   // exclusive
@@ -1506,6 +1534,7 @@ void attn_sched_kernel(AttnArgs a)
     auto tile_step = [&](int kt, const uint16_t *Kb, uint16_t *next) {
         __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of tile kt have landed
         __syncthreads();                   // ... and every wave's; `next` is free again
+        if (kt == t_first) read_q();       // the query rows have landed too
         if (kt == t_first && app_on)
             append_store<D, kThreads, 0, 1>(a, g, r0, app_rows, tid, app, true);
         float mvals[16];
