@@ -1344,6 +1344,14 @@ void attn_sched_kernel(AttnArgs a)
     __shared__ float ml[2 * 4 * kQC];
     __shared__ __attribute__((aligned(16))) uint16_t qbuf[kQC * D];   // the workgroup's query rows
 
+    {
+        // one round trip brings all four cache lines of the arguments into
+        // the scalar cache; the later field reads then hit it instead of
+        // waiting on one miss after another
+        const void *f0 = a.q;
+        const int f1 = a.varlen, f2 = a.n_parts, f3 = a.ring_start;
+        asm volatile("" ::"s"(f0), "s"(f1), "s"(f2), "s"(f3));
+    }
     SeqView sv;
     if (!resolve_seq(a, blockIdx.z, sv)) return;
     const int G = a.Hq / a.Hkv;
