@@ -154,6 +154,18 @@ struct Tile {
     static __device__ __forceinline__ int swz_o(int col) { return col & (D4 - 1); }
 };
 
+// One field from each 64-byte line of the argument block, read at kernel
+// entry: the four scalar-cache misses are then in flight together, and the
+// kernel's later argument reads (each behind a data-dependent branch) hit
+// the scalar cache instead of waiting on one miss after another.
+__device__ __forceinline__ void prefetch_args(const AttnArgs &a)
+{
+    static_assert(sizeof(AttnArgs) <= 256, "four lines");
+    const void *f0 = a.q;
+    const int f1 = a.varlen, f2 = a.n_parts, f3 = a.ring_start;
+    asm volatile("" ::"s"(f0), "s"(f1), "s"(f2), "s"(f3));
+}
+
 struct SeqView {
     int slot, q_row0, out_row0, rows, q_src_rows, out_rows, n_keys, key_lo, causal_base;
 };
@@ -319,6 +331,7 @@ void attn_mfma_kernel(AttnArgs a)
     __shared__ float ml[2 * 4 * kQC];
     __shared__ int ptab[PAGED ? kMaxTableBlocks : 1];
 
+    prefetch_args(a);
     SeqView sv;
     if (!resolve_seq(a, blockIdx.z, sv)) return;
     const int G = a.Hq / a.Hkv;
@@ -1300,6 +1313,7 @@ template <typename TR, int D, bool PAGED>
 __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_wide_kernel(AttnArgs a)
 {
+    prefetch_args(a);
     attn_wide_item<TR, D, PAGED>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
@@ -1344,14 +1358,7 @@ void attn_sched_kernel(AttnArgs a)
     __shared__ float ml[2 * 4 * kQC];
     __shared__ __attribute__((aligned(16))) uint16_t qbuf[kQC * D];   // the workgroup's query rows
 
-    {
-        // one round trip brings all four cache lines of the arguments into
-        // the scalar cache; the later field reads then hit it instead of
-        // waiting on one miss after another
-        const void *f0 = a.q;
-        const int f1 = a.varlen, f2 = a.n_parts, f3 = a.ring_start;
-        asm volatile("" ::"s"(f0), "s"(f1), "s"(f2), "s"(f3));
-    }
+    prefetch_args(a);
     SeqView sv;
     if (!resolve_seq(a, blockIdx.z, sv)) return;
     const int G = a.Hq / a.Hkv;
