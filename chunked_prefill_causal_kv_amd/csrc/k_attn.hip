@@ -1418,9 +1418,9 @@ void attn_sched_kernel(AttnArgs a)
             const int head = g * G + (ok ? col % G : 0);
             const uint16_t *src =
                 (const uint16_t *)a.q + ((int64_t)(sv.q_row0 + srow) * a.Hq + head) * D + pch * 8;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                             (__attribute__((address_space(3))) void *)(qbuf + blk * 64 * 8),
-                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)src,
+                (__attribute__((address_space(3))) void *)(qbuf + blk * 64 * 8), 16, 0, 0);
         }
     }
     auto read_q = [&]() __attribute__((always_inline)) {
