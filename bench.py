@@ -432,14 +432,17 @@ def bench_ladder(cpk, si, torch, reps=2, passes=10, warm=3):
             "note": "eager cpk_prefill_chunk calls (append + attention per chunk)"}
 
 
-def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=50, warm=10):
+def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=50, warm=10,
+                  deferred=False):
     """Rolling right-aligned cache: 4096 fp16 tokens, 16 heads, C = 2048,
     c = 256; per chunk roll_append (out of place, double-buffered: C rows
     moved) then roll_attention, or with ring=True one cpk_ring_step (the c
-    new rows written into the ring by the attention launch); with the
-    explicit (c, C) additive mask (0 visible,
-    -32768 masked) or visibility computed in the kernel.  Median of reps
-    timed passes over the 16 chunks."""
+    new rows written into the ring by the attention launch), or with
+    deferred=True too one cpk_ring_step_deferred (the chunk's key-range
+    parts merged by the next chunk's launch, the last chunk's by one flush);
+    with the explicit (c, C) additive mask (0 visible, -32768 masked) or
+    visibility computed in the kernel.  Median of reps timed passes over the
+    16 chunks."""
     L, H, D, C, c = 4096, 16, 128, 2048, 256
     q, k, v = (x.cuda() for x in si.rolling_inputs())
     n = L // c
@@ -455,12 +458,21 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=50, warm=
     assert pairs == rolling_work(L, H, D, C, c, explicit_mask)[0]
     bufs = [torch.zeros((1, H, C, D), dtype=torch.float16, device="cuda") for _ in range(4)]
     out = torch.empty_like(q)
+    nws = cpk.cpk_roll_workspace_size(H, H, C, c, D, torch.float16)
+    wss = [torch.empty(nws // 4 + 4, dtype=torch.float32, device="cuda") for _ in range(2)]
 
     def run():
-        cur, start = 0, 0
+        cur, start, pending = 0, 0, None
         for j in range(n):
             sl = slice(j * c, (j + 1) * c)
             m = masks[j] if explicit_mask else None
+            if ring and deferred:
+                pending, start = cpk.cpk_ring_step_deferred(
+                    q[sl], k[sl], v[sl], bufs[0][0], bufs[1][0], (j + 1) * c, 0, start,
+                    wss[j % 2], prev=pending, mask=m, out=out[sl])
+                if j == n - 1:
+                    cpk.cpk_ring_flush(pending)
+                continue
             if ring:
                 # the append runs inside the attention launch
                 _, start = cpk.cpk_ring_step(q[sl], k[sl], v[sl], bufs[0][0], bufs[1][0],
@@ -516,7 +528,10 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=50, warm=
                  "note": "whole 16-chunk schedule against the larger of its HBM and fp16 "
                          "MFMA bounds"})
     how = "the explicit (c, C) mask" if explicit_mask else "visibility computed in the kernel"
-    what = "ring_step (append fused into the attention)" if ring else "roll_append + roll_attention"
+    what = ("ring_step_deferred (append fused into the attention, each chunk's split merged "
+            "by the next chunk's launch, the last by a flush)" if ring and deferred else
+            "ring_step (append fused into the attention)" if ring else
+            "roll_append + roll_attention")
     return {"chunks": n, "gflop": round(f / 1e9, 2), "ms": round(ms, 4), "ms_min": round(min(times), 4),
             "tflops": round(f / (ms * 1e-3) / 1e12, 1), "dtype": "fp16", "roofline": roof,
             "note": f"{what} with {how}, per chunk; 16 chunks replayed as a HIP graph, "
@@ -811,7 +826,8 @@ def main():
                          "ladder, rolling, mixed (default all)")
     ap.add_argument("--rolling", default="all",
                     help="comma list of rolling schedules to run: shift_mask, shift_computed, "
-                         "ring_mask, ring_computed (default all)")
+                         "ring_mask, ring_computed, ring_deferred_mask, ring_deferred_computed "
+                         "(default all)")
     ap.add_argument("--mixed", default="all",
                     help="comma list of mixed steps to run, as budget[_two_streams][_paged] "
                          "(default all five)")
@@ -856,14 +872,17 @@ def main():
         secondary["ladder"] = bench_ladder(cpk, si, torch)
         log(f"bench: ladder {secondary['ladder']}")
     if not args.no_secondary and "rolling" in groups:
-        variants = {"shift_mask": ("rolling_fp16", True, False),
-                    "shift_computed": ("rolling_fp16_computed_mask", False, False),
-                    "ring_mask": ("rolling_fp16_ring", True, True),
-                    "ring_computed": ("rolling_fp16_ring_computed_mask", False, True)}
+        variants = {"shift_mask": ("rolling_fp16", True, False, False),
+                    "shift_computed": ("rolling_fp16_computed_mask", False, False, False),
+                    "ring_mask": ("rolling_fp16_ring", True, True, False),
+                    "ring_computed": ("rolling_fp16_ring_computed_mask", False, True, False),
+                    "ring_deferred_mask": ("rolling_fp16_ring_deferred", True, True, True),
+                    "ring_deferred_computed": ("rolling_fp16_ring_deferred_computed_mask", False,
+                                               True, True)}
         names = list(variants) if args.rolling == "all" else args.rolling.split(",")
         for name in names:
-            key, explicit, ring = variants[name]
-            secondary[key] = bench_rolling(cpk, si, torch, explicit, ring=ring)
+            key, explicit, ring, deferred = variants[name]
+            secondary[key] = bench_rolling(cpk, si, torch, explicit, ring=ring, deferred=deferred)
             log(f"bench: rolling {secondary[key]}")
     if not args.no_secondary and "mixed" in groups:
         for budget, overlap, paged in ((2048, False, False), (2048, True, False),

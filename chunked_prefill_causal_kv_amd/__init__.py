@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-from typing import List, Optional, Sequence, Tuple
+from typing import List, NamedTuple, Optional, Sequence, Tuple
 
 import torch
 
@@ -86,6 +86,9 @@ def _load() -> ctypes.CDLL:
         "cpk_ring_append": ([P, P, P, P, I, I, I, I, I, I, I, P], I),
         "cpk_ring_attention": ([P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, Z, P], I),
         "cpk_ring_step": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, Z, P], I),
+        "cpk_ring_step_deferred": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, Z, P,
+                                    P, P], I),
+        "cpk_ring_flush": ([P, Z, P, I, I, I, I, I, I, P], I),
         "cpk_ring_view": ([P, P, P, P, I, I, I, I, I, I, P], I),
     }
     for name, (args, res) in sig.items():
@@ -446,14 +449,15 @@ def cpk_roll_workspace_size(Hq: int, Hkv: int, C: int, c: int, head_dim: int, dt
 _roll_ws = {}
 
 
-def _roll_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
-    """A reusable device workspace of at least nbytes (None for 0)."""
+def _roll_workspace(nbytes: int, device, index: int = 0) -> Optional[torch.Tensor]:
+    """A reusable device workspace of at least nbytes (None for 0); index
+    selects one of several (a deferred ring chain alternates two)."""
     if nbytes == 0:
         return None
-    key = torch.device(device)
+    key = (torch.device(device), index)
     ws = _roll_ws.get(key)
     if ws is None or ws.numel() * 4 < nbytes:
-        ws = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=key)
+        ws = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=key[0])
         _roll_ws[key] = ws
     return ws
 
@@ -528,6 +532,45 @@ def cpk_ring_step(q, k_chunk, v_chunk, k_ring, v_ring, abs_end: int, n_leftpad: 
     return out, (start + c) % C
 
 
+class RingPending(NamedTuple):
+    """Parts a deferred ring step left unmerged: merged into `out` by the
+    next deferred call (passed as prev) or by cpk_ring_flush."""
+    ws: torch.Tensor
+    out: torch.Tensor
+    Hq: int
+    Hkv: int
+    C: int
+    c: int
+
+
+def cpk_ring_step_deferred(q, k_chunk, v_chunk, k_ring, v_ring, abs_end: int, n_leftpad: int,
+                           start: int, ws, prev: Optional[RingPending] = None, mask=None,
+                           scale: float = 0.0, out=None, stream=None):
+    """cpk_ring_step whose key-range parts stay in ws (a workspace of
+    cpk_roll_workspace_size bytes; the previous call's must be another) and
+    are merged into out by the next deferred call or cpk_ring_flush; this
+    launch merges prev's parts.  Returns (pending, new start)."""
+    c, Hq, D = q.shape
+    Hkv, C, _ = k_ring.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(_lib.cpk_ring_step_deferred(
+        _ptr(q), _ptr(k_chunk), _ptr(v_chunk), _ptr(k_ring), _ptr(v_ring), _ptr(mask), abs_end,
+        n_leftpad, Hq, Hkv, C, c, D, DTYPE_CODE[q.dtype], float(scale), start, _ptr(out),
+        _ptr(ws), ws.numel() * ws.element_size(), None if prev is None else _ptr(prev.ws),
+        None if prev is None else _ptr(prev.out), _stream(stream)))
+    return RingPending(ws, out, Hq, Hkv, C, c), (start + c) % C
+
+
+def cpk_ring_flush(pending: RingPending, stream=None) -> torch.Tensor:
+    """Merge the parts a deferred ring step left pending; returns its out."""
+    ws, out = pending.ws, pending.out
+    _check(_lib.cpk_ring_flush(_ptr(ws), ws.numel() * ws.element_size(), _ptr(out), pending.Hq,
+                               pending.Hkv, pending.C, pending.c, out.shape[2],
+                               DTYPE_CODE[out.dtype], _stream(stream)))
+    return out
+
+
 def cpk_ring_view(k_ring, v_ring, start: int, k_out=None, v_out=None, stream=None):
     """The logical (literal-shift) view of rings [B, H, C, D]."""
     B, H, C, D = k_ring.shape
@@ -587,12 +630,14 @@ def roll_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream
 
 
 def ring_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream=None,
-                 split: bool = True, fused: bool = True):
+                 split: bool = True, fused: bool = True, defer: bool = True):
     """roll_prefill over a ring buffer: per chunk, cpk_ring_step (append of
     the c rows fused into the attention launch), or with fused=False
-    cpk_ring_append then cpk_ring_attention.  Same outputs, bit for bit.
-    Returns (out over the padded sequence, n_leftpad, k ring, v ring,
-    start)."""
+    cpk_ring_append then cpk_ring_attention.  Where the key range splits
+    (fused, split, bf16/fp16) and defer is set, each chunk runs
+    cpk_ring_step_deferred (its parts merged by the next chunk's launch, the
+    last by cpk_ring_flush).  Same outputs, bit for bit.  Returns (out over
+    the padded sequence, n_leftpad, k ring, v ring, start)."""
     L, Hq, D = q.shape
     Hkv = k.shape[1]
     n_left = (-L) % c
@@ -605,6 +650,19 @@ def ring_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream
     vr = torch.zeros_like(kr)
     out = torch.empty_like(q)
     start = 0
+    nbytes = cpk_roll_workspace_size(Hq, Hkv, C, c, D, q.dtype) if fused and split else 0
+    if defer and nbytes:
+        wss = [_roll_workspace(nbytes, q.device, 1 + i) for i in range(2)]
+        pending = None
+        for j in range(Lp // c):
+            sl = slice(j * c, (j + 1) * c)
+            pending, start = cpk_ring_step_deferred(
+                q[sl], k[sl], v[sl], kr[0], vr[0], (j + 1) * c, n_left, start, wss[j % 2],
+                prev=pending, mask=None if masks is None else masks[j], scale=scale,
+                out=out[sl], stream=stream)
+        if pending is not None:
+            cpk_ring_flush(pending, stream)
+        return out, n_left, kr[0], vr[0], start
     for j in range(Lp // c):
         sl = slice(j * c, (j + 1) * c)
         m = None if masks is None else masks[j]

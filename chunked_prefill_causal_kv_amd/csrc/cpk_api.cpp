@@ -129,7 +129,7 @@ int pick_kernel(int dtype, int group, int kv_heads, int rows)
 
 extern "C" {
 
-int cpk_version(void) { return 102; }
+int cpk_version(void) { return 103; }
 
 int cpk_set_attention_kernel(int kind)
 {
@@ -625,11 +625,15 @@ static int roll_check(const void *q, const void *k, const void *v, const void *m
 // logical slot 0 is ring_start).  With k_chunk / v_chunk set (bf16/fp16),
 // the kernel also appends the chunk: its rows are the keys of the last c
 // slots, read from the chunk and written to their ring slots.
+// Deferred (defer, bf16/fp16 with a split): the parts stay in ws for a later
+// merge instead of a combine launch, and the parts an earlier deferred call
+// left in prev_ws (same shapes) are merged into prev_out by this launch.
 static int roll_attention_impl(const void *q, const void *k, const void *v, const void *mask,
                                int abs_end, int n_leftpad, int Hq, int Hkv, int C, int c, int D,
                                int dtype, float scale, int ring_start, void *out, void *ws,
                                size_t ws_bytes, void *stream, const void *k_chunk = nullptr,
-                               const void *v_chunk = nullptr)
+                               const void *v_chunk = nullptr, bool defer = false,
+                               const void *prev_ws = nullptr, void *prev_out = nullptr)
 {
     int r = roll_check(q, k, v, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D, dtype, out, ws,
                        ws_bytes);
@@ -666,9 +670,24 @@ static int roll_attention_impl(const void *q, const void *k, const void *v, cons
     const int kern = g_attn_kernel.load(std::memory_order_relaxed) == CPK_ATTN_NARROW_GENERAL
                          ? cpk::kAttnNarrowGeneral
                          : cpk::kAttnNarrow;
+    if (prev_ws) {
+        if (kern == cpk::kAttnNarrow) {
+            // the scheduled form merges them beside its first tile's loads
+            a.prev_ws = (const float *)prev_ws;
+            a.prev_out = prev_out;
+        } else {
+            // the general form has no carried merge: a combine launch first
+            cpk::AttnArgs m = a;
+            m.part_ws = (float *)prev_ws;
+            m.out = prev_out;
+            r = hip_status(cpk::launch_attention_combine(m, dtype, (hipStream_t)stream),
+                           "ring_step_deferred merge");
+            if (r) return r;
+        }
+    }
     r = hip_status(cpk::launch_attention(a, dtype, (c + br - 1) / br, 1, kern, (hipStream_t)stream),
                    "roll_attention launch");
-    if (r || parts <= 1) return r;
+    if (r || parts <= 1 || defer) return r;
     return hip_status(cpk::launch_attention_combine(a, dtype, (hipStream_t)stream),
                       "roll_attention combine");
 }
@@ -718,14 +737,10 @@ int cpk_ring_append(const void *k_chunk, const void *v_chunk, void *k_ring, void
                       "ring_append launch");
 }
 
-int cpk_ring_step(const void *q, const void *k_chunk, const void *v_chunk, void *k_ring,
-                  void *v_ring, const void *mask, int abs_end, int n_leftpad, int Hq, int Hkv,
-                  int C, int c, int D, int dtype, float scale, int start, void *out, void *ws,
-                  size_t ws_bytes, void *stream)
+// Checks of a ring step's chunk, rings and start (after roll_check).
+static int ring_step_check(const void *k_chunk, const void *v_chunk, const void *k_ring,
+                           const void *v_ring, int Hkv, int C, int c, int D, int dtype, int start)
 {
-    int r = roll_check(q, k_ring, v_ring, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D, dtype, out,
-                       ws, ws_bytes);
-    if (r) return r;
     if (start < 0 || start >= C)
         return fail(CPK_EINVAL, "ring_step: start=%d outside [0, C=%d)", start, C);
     if (!k_chunk || !v_chunk) return fail(CPK_EINVAL, "ring_step: NULL chunk");
@@ -740,6 +755,19 @@ int cpk_ring_step(const void *q, const void *k_chunk, const void *v_chunk, void 
             return fail(CPK_EINVAL, "ring_step: a chunk overlaps a ring");
     if (overlaps(k_ring, ring_bytes, v_ring, ring_bytes))
         return fail(CPK_EINVAL, "ring_step: k_ring and v_ring overlap");
+    return ok();
+}
+
+int cpk_ring_step(const void *q, const void *k_chunk, const void *v_chunk, void *k_ring,
+                  void *v_ring, const void *mask, int abs_end, int n_leftpad, int Hq, int Hkv,
+                  int C, int c, int D, int dtype, float scale, int start, void *out, void *ws,
+                  size_t ws_bytes, void *stream)
+{
+    int r = roll_check(q, k_ring, v_ring, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D, dtype, out,
+                       ws, ws_bytes);
+    if (r) return r;
+    if ((r = ring_step_check(k_chunk, v_chunk, k_ring, v_ring, Hkv, C, c, D, dtype, start)))
+        return r;
     const int next = (start + c) % C;
     if (dtype == CPK_F32) {
         // fp32 has no fused form: the append, then the attention
@@ -752,6 +780,69 @@ int cpk_ring_step(const void *q, const void *k_chunk, const void *v_chunk, void 
     }
     return roll_attention_impl(q, k_ring, v_ring, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D,
                                dtype, scale, next, out, ws, ws_bytes, stream, k_chunk, v_chunk);
+}
+
+int cpk_ring_step_deferred(const void *q, const void *k_chunk, const void *v_chunk,
+                           void *k_ring, void *v_ring, const void *mask, int abs_end,
+                           int n_leftpad, int Hq, int Hkv, int C, int c, int D, int dtype,
+                           float scale, int start, void *out, void *ws, size_t ws_bytes,
+                           const void *prev_ws, void *prev_out, void *stream)
+{
+    int r = roll_check(q, k_ring, v_ring, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D, dtype, out,
+                       ws, ws_bytes);
+    if (r) return r;
+    if ((r = ring_step_check(k_chunk, v_chunk, k_ring, v_ring, Hkv, C, c, D, dtype, start)))
+        return r;
+    const size_t need = cpk_roll_workspace_size(Hq, Hkv, C, c, D, dtype);
+    if (need == 0 || !ws)
+        return fail(CPK_EINVAL, "ring_step_deferred: these shapes do not split the key range "
+                                "(use cpk_ring_step)");
+    if (prev_ws) {
+        if (!prev_out) return fail(CPK_EINVAL, "ring_step_deferred: prev_ws without prev_out");
+        if (!aligned16(prev_ws) || !aligned16(prev_out))
+            return fail(CPK_EALIGN, "ring_step_deferred: prev_ws / prev_out not aligned");
+        const size_t out_bytes = (size_t)c * Hq * D * elem_size(dtype);
+        const size_t ring_bytes = (size_t)Hkv * C * D * elem_size(dtype);
+        const size_t chunk_bytes = (size_t)c * Hkv * D * elem_size(dtype);
+        if (overlaps(prev_ws, need, ws, need))
+            return fail(CPK_EINVAL, "ring_step_deferred: prev_ws overlaps ws");
+        const void *read[6] = {q, k_chunk, v_chunk, k_ring, v_ring, prev_ws};
+        const size_t len[6] = {out_bytes, chunk_bytes, chunk_bytes, ring_bytes, ring_bytes, need};
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(prev_out, out_bytes, read[i], len[i]))
+                return fail(CPK_EINVAL, "ring_step_deferred: prev_out overlaps an input");
+        if (overlaps(prev_out, out_bytes, ws, need))
+            return fail(CPK_EINVAL, "ring_step_deferred: prev_out overlaps ws");
+    }
+    return roll_attention_impl(q, k_ring, v_ring, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D,
+                               dtype, scale, (start + c) % C, out, ws, ws_bytes, stream, k_chunk,
+                               v_chunk, true, prev_ws, prev_out);
+}
+
+int cpk_ring_flush(const void *ws, size_t ws_bytes, void *out, int Hq, int Hkv, int C, int c,
+                   int D, int dtype, void *stream)
+{
+    int r = check_dtype_dim(dtype, D);
+    if (r) return r;
+    if ((r = check_heads(Hq, Hkv))) return r;
+    if (C < 1 || c < 1 || c > C) return fail(CPK_EINVAL, "ring_flush: C=%d c=%d", C, c);
+    const size_t need = cpk_roll_workspace_size(Hq, Hkv, C, c, D, dtype);
+    if (need == 0)
+        return fail(CPK_EINVAL, "ring_flush: these shapes do not split the key range");
+    if (!ws || !out) return fail(CPK_EINVAL, "ring_flush: NULL buffer");
+    if (ws_bytes < need)
+        return fail(CPK_EWORKSPACE, "ring_flush: workspace %zu bytes, need %zu", ws_bytes, need);
+    if (!aligned16(ws) || !aligned16(out)) return fail(CPK_EALIGN, "ring_flush: not aligned");
+    if (overlaps(out, (size_t)c * Hq * D * elem_size(dtype), ws, need))
+        return fail(CPK_EINVAL, "ring_flush: out overlaps ws");
+    int parts, pt;
+    roll_split(Hq, Hkv, C, c, dtype, &parts, &pt);
+    cpk::AttnArgs a = {};
+    a.out = out; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
+    a.out_row0 = 0; a.out_rows = c;
+    a.n_parts = parts; a.part_tiles = pt; a.part_ws = (float *)ws;
+    return hip_status(cpk::launch_attention_combine(a, dtype, (hipStream_t)stream),
+                      "ring_flush combine");
 }
 
 int cpk_ring_view(const void *k_ring, const void *v_ring, void *k_out, void *v_out, int B, int H,

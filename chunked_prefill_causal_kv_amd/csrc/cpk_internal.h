@@ -82,6 +82,15 @@ struct AttnArgs {
     // clamped into [0, n_blocks)); block_size is a multiple of 256
     const int32_t *block_table;
     int max_blocks, block_size, n_blocks;
+
+    // carried merge (scalar mode, key split; the 64-column kernel's
+    // scheduled form): with prev_ws set, the launch also merges the parts
+    // that an earlier split launch of the same shapes left in prev_ws
+    // (part_ws's layout: n_parts records per (row, query head) of out_rows
+    // rows) into prev_out [out_rows][Hq][D] with the combine's arithmetic,
+    // the (row, head) pairs spread over the grid's workgroups
+    const float *prev_ws;
+    void *prev_out;
 };
 
 // Row of position `pos` (head g) in a paged pool, as an element offset; the
@@ -157,9 +166,9 @@ hipError_t launch_ring_view(const void *k_ring, const void *v_ring, void *k_out,
 constexpr int kWideMinGroups = 256;   // auto choice: wide once its grid fills the CUs
 int attn_rows_per_block(int dtype, int group, bool wide);
 // bf16/fp16 kernel of a launch: the 64-column kernel (its latency-scheduled
-// form wherever the call has no additive mask, ring buffer, paging or key
-// split), the 128-column kernel, or the 64-column kernel's general form
-// everywhere (diagnostics)
+// form wherever the launch reads a contiguous cache, its general form over
+// a paged pool), the 128-column kernel, or the 64-column kernel's general
+// form everywhere (diagnostics)
 enum AttnKernel { kAttnNarrow = 0, kAttnWide = 1, kAttnNarrowGeneral = 2 };
 hipError_t launch_attention(const AttnArgs &a, int dtype, int row_blocks, int n_seq_grid,
                             int kernel, hipStream_t st);

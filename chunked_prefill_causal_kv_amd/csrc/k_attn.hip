@@ -283,6 +283,80 @@ __device__ __forceinline__ const char *kv_src(const uint16_t *cache_head, const 
     return (const char *)(cache_head + (int64_t)phys * D + chunk_elem);
 }
 
+// Merge of the split parts of a key range: for each (row, query head), in
+// part order, M = max_p M_p, f_p = 2^(M_p - M), out = sum_p f_p O_p /
+// sum_p f_p den_p.  One unit is 8 consecutive outputs of one (row, head)
+// (unit / (D / 8) is the pair row * Hq + head): two 16-byte record loads
+// per part and one 16-byte store.  The records of up to kCombineBatch parts
+// are loaded at once (one memory round trip); more parts are merged batch
+// by batch, rescaling the running sums when a later batch raises the
+// maximum (for at most kCombineBatch parts, exactly the two-pass formula
+// above).  The combine launch and the carried merge of the scheduled
+// 64-column kernel both run this, so their outputs are identical.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineBatch = 4;
+
+template <typename TR, int D>
+__device__ __forceinline__ void combine_unit(const float *part_ws, int n_parts, int out_rows,
+                                             int Hq, void *out, int out_row0, int unit)
+{
+    constexpr int TPP = D / 8;                       // units per (row, head)
+    const int pair = unit / TPP;
+    const int row = pair / Hq;
+    const int head = pair % Hq;
+    const int d0 = (unit % TPP) * 8;
+    const int64_t stride = (int64_t)out_rows * Hq * (D + 4);
+    const float *rec = part_ws + (int64_t)pair * (D + 4);
+    float M = -INFINITY;
+    float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    for (int p0 = 0; p0 < n_parts; p0 += kCombineBatch) {
+        float2 md[kCombineBatch];
+        float4 x0[kCombineBatch], x1[kCombineBatch];
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) {
+            // past the last part: re-read a valid record, weighted 0 below
+            const float *r = rec + (int64_t)min(p0 + i, n_parts - 1) * stride;
+            md[i] = *(const float2 *)r;
+            x0[i] = *(const float4 *)(r + 4 + d0);
+            x1[i] = *(const float4 *)(r + 8 + d0);
+        }
+        float bm = M;
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i)
+            if (p0 + i < n_parts) bm = fmaxf(bm, md[i].x);
+        if (bm != M) {   // M == -inf: nothing merged yet, the sums are 0
+            const float alpha = M == -INFINITY ? 0.f : exp2f(M - bm);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) num[e] *= alpha;
+            den *= alpha;
+            M = bm;
+        }
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) {
+            const float f = (p0 + i >= n_parts || md[i].x == -INFINITY) ? 0.f : exp2f(md[i].x - M);
+            num[0] = __builtin_fmaf(f, x0[i].x, num[0]);
+            num[1] = __builtin_fmaf(f, x0[i].y, num[1]);
+            num[2] = __builtin_fmaf(f, x0[i].z, num[2]);
+            num[3] = __builtin_fmaf(f, x0[i].w, num[3]);
+            num[4] = __builtin_fmaf(f, x1[i].x, num[4]);
+            num[5] = __builtin_fmaf(f, x1[i].y, num[5]);
+            num[6] = __builtin_fmaf(f, x1[i].z, num[6]);
+            num[7] = __builtin_fmaf(f, x1[i].w, num[7]);
+            den = __builtin_fmaf(f, md[i].y, den);
+        }
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float o0 = den > 0.f ? num[2 * i] / den : 0.f;
+        const float o1 = den > 0.f ? num[2 * i + 1] / den : 0.f;
+        w[i] = TR::pack(o0, o1);
+    }
+    uint16_t *op = (uint16_t *)out + ((int64_t)(out_row0 + row) * Hq + head) * D + d0;
+    *(uint4 *)op = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Block rows of a paged pool for one workgroup's key tiles.  At the start
 // the workgroup stages the block ids of its key range (clamped into the
 // pool) in LDS; a tile's lookup is then an LDS read, so no extra global
@@ -1422,6 +1496,20 @@ void attn_sched_kernel(AttnArgs a)
                 (const __attribute__((address_space(1))) void *)src,
                 (__attribute__((address_space(3))) void *)(qbuf + blk * 64 * 8), 16, 0, 0);
         }
+        // carried merge of an earlier split launch's parts: this
+        // workgroup's share of the merge units, taken by column group 1
+        // while the first tile is in flight (every workgroup of a scalar
+        // launch has rows, so all of them get here)
+        if (__builtin_expect(a.prev_ws != nullptr, 0)) {   // laid out off the hot path
+            constexpr int kMT = kThreads / 2;
+            const int units = a.out_rows * a.Hq * (D / 8);
+            const int n_wg = gridDim.x * gridDim.y;
+            const int per = (units + n_wg - 1) / n_wg;
+            const int u0 = (blockIdx.y * gridDim.x + blockIdx.x) * per;
+            const int u1 = min(units, u0 + per);
+            for (int u = u0 + (tid - kMT); u < u1; u += kMT)
+                combine_unit<TR, D>(a.prev_ws, a.n_parts, a.out_rows, a.Hq, a.prev_out, 0, u);
+        }
     }
     auto read_q = [&]() __attribute__((always_inline)) {
         const uint16_t *qr = qbuf + qc * D;
@@ -1800,76 +1888,14 @@ void attn_sched_kernel(AttnArgs a)
     }
 }
 
-// Merge of the split parts of a key range: for each (row, query head), in
-// part order, M = max_p M_p, f_p = 2^(M_p - M), out = sum_p f_p O_p /
-// sum_p f_p den_p.  Each thread produces 8 consecutive outputs of one
-// (row, head): two 16-byte record loads per part and one 16-byte store.
-// The records of up to kCombineBatch parts are loaded at once (one memory
-// round trip); more parts are merged batch by batch, rescaling the running
-// sums when a later batch raises the maximum (for at most kCombineBatch
-// parts, exactly the two-pass formula above).
-constexpr int kCombineThreads = 256;
-constexpr int kCombineBatch = 4;
-
+// Merge of the split parts of a key range (combine_unit above), one
+// thread per 8 consecutive outputs of a (row, head).
 template <typename TR, int D>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a)
 {
-    constexpr int TPP = D / 8;                       // threads per (row, head)
-    const int pair = blockIdx.x * (kCombineThreads / TPP) + threadIdx.x / TPP;
-    if (pair >= a.out_rows * a.Hq) return;
-    const int row = pair / a.Hq;
-    const int head = pair % a.Hq;
-    const int d0 = (threadIdx.x % TPP) * 8;
-    const int64_t stride = (int64_t)a.out_rows * a.Hq * (D + 4);
-    const float *rec = a.part_ws + (int64_t)pair * (D + 4);
-    float M = -INFINITY;
-    float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    for (int p0 = 0; p0 < a.n_parts; p0 += kCombineBatch) {
-        float2 md[kCombineBatch];
-        float4 x0[kCombineBatch], x1[kCombineBatch];
-#pragma unroll
-        for (int i = 0; i < kCombineBatch; ++i) {
-            // past the last part: re-read a valid record, weighted 0 below
-            const float *r = rec + (int64_t)min(p0 + i, a.n_parts - 1) * stride;
-            md[i] = *(const float2 *)r;
-            x0[i] = *(const float4 *)(r + 4 + d0);
-            x1[i] = *(const float4 *)(r + 8 + d0);
-        }
-        float bm = M;
-#pragma unroll
-        for (int i = 0; i < kCombineBatch; ++i)
-            if (p0 + i < a.n_parts) bm = fmaxf(bm, md[i].x);
-        if (bm != M) {   // M == -inf: nothing merged yet, the sums are 0
-            const float alpha = M == -INFINITY ? 0.f : exp2f(M - bm);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) num[e] *= alpha;
-            den *= alpha;
-            M = bm;
-        }
-#pragma unroll
-        for (int i = 0; i < kCombineBatch; ++i) {
-            const float f = (p0 + i >= a.n_parts || md[i].x == -INFINITY) ? 0.f : exp2f(md[i].x - M);
-            num[0] = __builtin_fmaf(f, x0[i].x, num[0]);
-            num[1] = __builtin_fmaf(f, x0[i].y, num[1]);
-            num[2] = __builtin_fmaf(f, x0[i].z, num[2]);
-            num[3] = __builtin_fmaf(f, x0[i].w, num[3]);
-            num[4] = __builtin_fmaf(f, x1[i].x, num[4]);
-            num[5] = __builtin_fmaf(f, x1[i].y, num[5]);
-            num[6] = __builtin_fmaf(f, x1[i].z, num[6]);
-            num[7] = __builtin_fmaf(f, x1[i].w, num[7]);
-            den = __builtin_fmaf(f, md[i].y, den);
-        }
-    }
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float o0 = den > 0.f ? num[2 * i] / den : 0.f;
-        const float o1 = den > 0.f ? num[2 * i + 1] / den : 0.f;
-        w[i] = TR::pack(o0, o1);
-    }
-    uint16_t *op = (uint16_t *)a.out + ((int64_t)(a.out_row0 + row) * a.Hq + head) * D + d0;
-    *(uint4 *)op = make_uint4(w[0], w[1], w[2], w[3]);
+    const int unit = blockIdx.x * kCombineThreads + threadIdx.x;
+    if (unit < a.out_rows * a.Hq * (D / 8))
+        combine_unit<TR, D>(a.part_ws, a.n_parts, a.out_rows, a.Hq, a.out, a.out_row0, unit);
 }
 
 // ------------------------------------------------------------------ fp32

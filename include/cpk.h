@@ -417,6 +417,41 @@ int cpk_ring_step(const void *q, const void *k_chunk, const void *v_chunk, void 
                   size_t ws_bytes, void *stream);
 
 /*
+ * cpk_ring_step with the merge of its key-range parts carried into the
+ * next chunk's launch (the same rolling step, Horizon developer blog
+ * "Chunk Prefill", sections 3 and 4, run as a pipeline over the chunks):
+ * the launch appends the chunk and leaves this chunk's parts unmerged in
+ * ws (out is not written yet), and, with prev_ws set, merges the parts an
+ * earlier deferred call of the same shapes left in prev_ws into that
+ * call's out, passed here as prev_out.  The chunk's output is complete
+ * once the next deferred call (or cpk_ring_flush(ws, out)) has run on the
+ * same stream; it is bit-identical to cpk_ring_step's.  A chain of calls
+ * alternates two workspaces (each cpk_roll_workspace_size bytes): call j
+ * writes ws_j and merges ws_(j-1).  Only shapes that split the key range
+ * (bf16/fp16, cpk_roll_workspace_size > 0) are deferred.  Errors: those of
+ * cpk_ring_step, all checked before anything is launched; CPK_EINVAL if
+ * the shapes do not split or ws is NULL, if prev_ws is set without
+ * prev_out, if prev_ws overlaps ws, or if prev_out overlaps q, a chunk, a
+ * ring, ws or prev_ws; CPK_EALIGN if prev_ws or prev_out is not 16-byte
+ * aligned.  The caller keeps prev_ws's shapes equal to this call's.
+ */
+int cpk_ring_step_deferred(const void *q, const void *k_chunk, const void *v_chunk,
+                           void *k_ring, void *v_ring, const void *mask, int abs_end,
+                           int n_leftpad, int Hq, int Hkv, int C, int c, int D, int dtype,
+                           float scale, int start, void *out, void *ws, size_t ws_bytes,
+                           const void *prev_ws, void *prev_out, void *stream);
+
+/*
+ * The merge a deferred ring step left pending: the parts in ws (written by
+ * cpk_ring_step_deferred with these shapes) merged into out
+ * [c][Hq][D] (one combine launch).  CPK_EINVAL if the shapes do not split,
+ * a buffer is NULL or out overlaps ws; CPK_EWORKSPACE if ws_bytes is below
+ * cpk_roll_workspace_size; CPK_EALIGN if ws or out is not 16-byte aligned.
+ */
+int cpk_ring_flush(const void *ws, size_t ws_bytes, void *out, int Hq, int Hkv, int C, int c,
+                   int D, int dtype, void *stream);
+
+/*
  * The logical view of a ring as a contiguous cache: out slot s = physical
  * slot (start + s) mod C, for K and V, [B][H][C][D] each (interoperation
  * and checks; not on the per-chunk path).  CPK_EINVAL if start is outside

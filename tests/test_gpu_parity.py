@@ -579,6 +579,60 @@ def test_ring_step_fused_matches_two_calls(dtype, C, c, Hq, Hkv, D):
                 assert bitwise(kb, ka) and bitwise(vb, va), f"{tag}: rings differ"
 
 
+@pytest.mark.parametrize("kernel", ["narrow", "general"])
+@pytest.mark.parametrize("dtype,C,c,Hq,Hkv,D", [
+    ("f16", 512, 128, 4, 4, 128),     # 4 parts of 1 tile; start walks and wraps
+    ("bf16", 300, 96, 4, 2, 64),      # 3 parts, tiles that wrap the ring mid-tile, GQA
+    ("f16", 2048, 256, 16, 16, 128),  # the rolling workload's shapes: 4 parts of 4 tiles
+])
+def test_ring_step_deferred_bit_equal(kernel, dtype, C, c, Hq, Hkv, D):
+    """A chain of deferred ring steps (each chunk's key-range parts merged
+    by the next chunk's launch, the last by the flush; the scheduled form
+    merges inside its launch, the general form with a combine launch ahead
+    of it) gives cpk_ring_step's bits: the output of every chunk and both
+    rings, with computed visibility and with the explicit mask."""
+    say(f"case: deferred ring step {kernel} {dtype} C={C} c={c} heads {Hq}/{Hkv} D={D}")
+    tdt = si.TORCH_DTYPE[dtype]
+    g = si.generator(520 + C)
+    n = 5
+    q = si.randn((n * c, Hq, D), dtype, g).cuda()
+    k = si.randn((n * c, Hkv, D), dtype, g).cuda()
+    v = si.randn((n * c, Hkv, D), dtype, g).cuda()
+    L = n * c
+    nbytes = cpk.cpk_roll_workspace_size(Hq, Hkv, C, c, D, tdt)
+    assert nbytes > 0, "the case must split the key range"
+    wss = [torch.full((nbytes // 4 + 4,), float("nan"), device="cuda") for _ in range(2)]
+    with cpk.attention_kernel(KERNELS[kernel]):
+        for explicit in (False, True):
+            masks = [torch.from_numpy(oracle.chunk_mask(L, 0, j, c, C)).to(tdt).cuda()
+                     if explicit else None for j in range(n)]
+            res = []
+            for deferred in (False, True):
+                kr = torch.zeros((1, Hkv, C, D), dtype=tdt, device="cuda")
+                vr = torch.zeros_like(kr)
+                out = torch.full((L, Hq, D), float("nan"), dtype=tdt, device="cuda")
+                start, pending = 0, None
+                for j in range(n):
+                    sl = slice(j * c, (j + 1) * c)
+                    if deferred:
+                        pending, start = cpk.cpk_ring_step_deferred(
+                            q[sl], k[sl], v[sl], kr[0], vr[0], (j + 1) * c, 0, start,
+                            wss[j % 2], prev=pending, mask=masks[j], out=out[sl])
+                    else:
+                        _, start = cpk.cpk_ring_step(q[sl], k[sl], v[sl], kr[0], vr[0],
+                                                     (j + 1) * c, 0, start, mask=masks[j],
+                                                     out=out[sl])
+                if pending is not None:
+                    cpk.cpk_ring_flush(pending)
+                torch.cuda.synchronize()
+                res.append((out, kr, vr, start))
+            (oa, ka, va, sa), (ob, kb, vb, sb) = res
+            tag = f"mask={explicit}"
+            assert sa == sb
+            assert bitwise(oa, ob), f"{tag}: outputs differ"
+            assert bitwise(ka, kb) and bitwise(va, vb), f"{tag}: rings differ"
+
+
 @pytest.mark.parametrize("dtype,C,c,Hq,Hkv,D", [
     ("f16", 512, 128, 4, 4, 128),     # start walks 0, 128, 256, 384 and wraps
     ("bf16", 300, 96, 4, 2, 64),      # tiles that wrap the ring mid-tile, GQA

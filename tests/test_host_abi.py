@@ -270,6 +270,45 @@ def test_ring_step_validation():
     assert call(abs_end=3) == cpk.CPK_EINVAL          # abs_end < c
 
 
+def test_ring_step_deferred_validation():
+    """The deferred ring step and its flush reject, on the host, shapes that
+    do not split, a missing or short workspace, and a carried merge whose
+    buffers alias the launch's other buffers (fake aligned pointers, 64 MiB
+    apart; every call here fails before a launch)."""
+    F16 = cpk.CPK_F16
+    M = 1 << 26
+    q, kc, vc, kr, vr, out, ws, pws, pout = (M * i for i in range(1, 10))
+    Hq = Hkv = 16
+    C, c, D = 2048, 256, 128
+    need = cpk.cpk_roll_workspace_size(Hq, Hkv, C, c, D, torch.float16)
+    assert need > 0
+    st = cpk._lib.cpk_ring_step_deferred
+
+    def call(heads=Hq, ws=ws, ws_bytes=need, pws=pws, pout=pout, q=q):
+        return st(q, kc, vc, kr, vr, None, C, 0, heads, heads, C, c, D, F16, 0.0, 0, out,
+                  ws, ws_bytes, pws, pout, None)
+
+    assert cpk.cpk_roll_workspace_size(64, 64, C, c, D, torch.float16) == 0
+    assert call(heads=64, ws=None, ws_bytes=0) == cpk.CPK_EINVAL    # no split
+    assert call(ws=None, ws_bytes=0) == cpk.CPK_EINVAL              # no workspace
+    assert call(ws_bytes=need - 4) == cpk.CPK_EWORKSPACE
+    assert call(pout=None) == cpk.CPK_EINVAL                        # prev_ws alone
+    assert call(pws=ws + 4096) == cpk.CPK_EINVAL                    # prev_ws overlaps ws
+    assert call(pout=kr + 64) == cpk.CPK_EINVAL                     # prev_out on a ring
+    assert call(pout=q) == cpk.CPK_EINVAL                           # prev_out on q
+    assert call(pout=ws + 1024) == cpk.CPK_EINVAL                   # prev_out on ws
+    assert call(pout=pws) == cpk.CPK_EINVAL                         # prev_out on prev_ws
+    assert call(pout=pout + 8) == cpk.CPK_EALIGN
+    assert call(pws=pws + 8) == cpk.CPK_EALIGN
+    fl = cpk._lib.cpk_ring_flush
+    assert fl(ws, need, out, 64, 64, C, c, D, F16, None) == cpk.CPK_EINVAL   # no split
+    assert fl(ws, need - 4, out, Hq, Hkv, C, c, D, F16, None) == cpk.CPK_EWORKSPACE
+    assert fl(ws, need, ws + 4096, Hq, Hkv, C, c, D, F16, None) == cpk.CPK_EINVAL
+    assert fl(None, need, out, Hq, Hkv, C, c, D, F16, None) == cpk.CPK_EINVAL
+    assert fl(ws, need, out + 8, Hq, Hkv, C, c, D, F16, None) == cpk.CPK_EALIGN
+    assert fl(ws, need, out, Hq, Hkv, C, c, 96, F16, None) == cpk.CPK_EDTYPE
+
+
 def test_varlen_phases_validation():
     """cpk_varlen_step_phases takes a nonzero subset of the three phases."""
     f = cpk._lib.cpk_varlen_step_phases
