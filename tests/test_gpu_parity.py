@@ -712,6 +712,50 @@ def test_graph_replay_of_chunked_prefill(kernel):
         _graph_replay_of_chunked_prefill()
 
 
+def test_graph_replay_of_deferred_ring_prefill():
+    """ring_prefill with deferred ring steps (each chunk's split merged by
+    the next chunk's launch, the last by the flush) captured once as a HIP
+    graph: every replay, with eager work between replays, matches the eager
+    run bit for bit (outputs and both rings), with the explicit mask and
+    with computed visibility."""
+    L, C, c, H, D = 1000, 512, 128, 4, 128
+    say(f"case: HIP graph of the deferred ring prefill fp16 L={L} C={C} c={c} H={H}, 3 replays")
+    q, k, v = (x.cuda() for x in si.rolling_inputs(L=L, H=H, D=D, seed=720))
+    assert cpk.cpk_roll_workspace_size(H, H, C, c, D, torch.float16) > 0
+    n_left = (-L) % c
+    masks = [torch.from_numpy(oracle.chunk_mask(L + n_left, n_left, j, c, C).astype(np.float16))
+             .cuda() for j in range((L + n_left) // c)]
+    for m in (None, masks):
+        res = {}
+
+        def run():
+            res["r"] = cpk.ring_prefill(q, k, v, C, c, masks=m)
+
+        run()
+        torch.cuda.synchronize()
+        ref_out, _, ref_k, ref_v, _ = (x.clone() if torch.is_tensor(x) else x for x in res["r"])
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        torch.cuda.synchronize()
+        out, _, kr, vr, _ = res["r"]
+        for rep in range(3):
+            out.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            tag = f"mask={m is not None} replay {rep}"
+            assert bitwise(out, ref_out), f"{tag}: output differs"
+            assert bitwise(kr, ref_k) and bitwise(vr, ref_v), f"{tag}: rings differ"
+            cpk.ring_prefill(q, k, v, C, c, masks=m)   # eager work between replays
+            torch.cuda.synchronize()
+
+
 def _graph_replay_of_chunked_prefill():
     L, W, Hq, Hkv, D = 1300, 512, 16, 4, 128
     q, k, v = si.gqa_prompt(L=L, Hq=Hq, Hkv=Hkv, D=D, seed=700)
