@@ -806,10 +806,12 @@ int cpk_ring_step_deferred(const void *q, const void *k_chunk, const void *v_chu
         const size_t chunk_bytes = (size_t)c * Hkv * D * elem_size(dtype);
         if (overlaps(prev_ws, need, ws, need))
             return fail(CPK_EINVAL, "ring_step_deferred: prev_ws overlaps ws");
-        const void *read[6] = {q, k_chunk, v_chunk, k_ring, v_ring, prev_ws};
-        const size_t len[6] = {out_bytes, chunk_bytes, chunk_bytes, ring_bytes, ring_bytes, need};
-        for (int i = 0; i < 6; ++i)
-            if (overlaps(prev_out, out_bytes, read[i], len[i]))
+        const size_t mask_bytes = (size_t)c * C * elem_size(dtype);
+        const void *read[7] = {q, k_chunk, v_chunk, k_ring, v_ring, prev_ws, mask};
+        const size_t len[7] = {out_bytes, chunk_bytes, chunk_bytes, ring_bytes, ring_bytes,
+                               need, mask_bytes};
+        for (int i = 0; i < 7; ++i)
+            if (read[i] && overlaps(prev_out, out_bytes, read[i], len[i]))
                 return fail(CPK_EINVAL, "ring_step_deferred: prev_out overlaps an input");
         if (overlaps(prev_out, out_bytes, ws, need))
             return fail(CPK_EINVAL, "ring_step_deferred: prev_out overlaps ws");

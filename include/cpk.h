@@ -432,7 +432,7 @@ int cpk_ring_step(const void *q, const void *k_chunk, const void *v_chunk, void 
  * cpk_ring_step, all checked before anything is launched; CPK_EINVAL if
  * the shapes do not split or ws is NULL, if prev_ws is set without
  * prev_out, if prev_ws overlaps ws, or if prev_out overlaps q, a chunk, a
- * ring, ws or prev_ws; CPK_EALIGN if prev_ws or prev_out is not 16-byte
+ * ring, the mask, ws or prev_ws; CPK_EALIGN if prev_ws or prev_out is not 16-byte
  * aligned.  The caller keeps prev_ws's shapes equal to this call's.
  */
 int cpk_ring_step_deferred(const void *q, const void *k_chunk, const void *v_chunk,

@@ -220,6 +220,7 @@ def test_attention_kernel_setting():
         cpk.cpk_set_attention_kernel(cpk.ATTN_AUTO)
 
 
+@no_gpu
 def test_ring_validation():
     """Ring-buffer entry points reject bad shapes, start indices and aliasing
     on the host (fake aligned pointers, never dereferenced)."""
@@ -247,6 +248,7 @@ def test_ring_validation():
     assert vw(FAKE, FAKE * 2, FAKE, big * 2, 1, 2, 8, 64, F16, 0, None) == cpk.CPK_EINVAL
 
 
+@no_gpu
 def test_ring_step_validation():
     """cpk_ring_step checks the append's and the attention's arguments on
     the host before anything is launched (fake aligned pointers)."""
@@ -270,6 +272,7 @@ def test_ring_step_validation():
     assert call(abs_end=3) == cpk.CPK_EINVAL          # abs_end < c
 
 
+@no_gpu
 def test_ring_step_deferred_validation():
     """The deferred ring step and its flush reject, on the host, shapes that
     do not split, a missing or short workspace, and a carried merge whose
@@ -284,8 +287,8 @@ def test_ring_step_deferred_validation():
     assert need > 0
     st = cpk._lib.cpk_ring_step_deferred
 
-    def call(heads=Hq, ws=ws, ws_bytes=need, pws=pws, pout=pout, q=q):
-        return st(q, kc, vc, kr, vr, None, C, 0, heads, heads, C, c, D, F16, 0.0, 0, out,
+    def call(heads=Hq, ws=ws, ws_bytes=need, pws=pws, pout=pout, q=q, mask=None):
+        return st(q, kc, vc, kr, vr, mask, C, 0, heads, heads, C, c, D, F16, 0.0, 0, out,
                   ws, ws_bytes, pws, pout, None)
 
     assert cpk.cpk_roll_workspace_size(64, 64, C, c, D, torch.float16) == 0
@@ -298,6 +301,7 @@ def test_ring_step_deferred_validation():
     assert call(pout=q) == cpk.CPK_EINVAL                           # prev_out on q
     assert call(pout=ws + 1024) == cpk.CPK_EINVAL                   # prev_out on ws
     assert call(pout=pws) == cpk.CPK_EINVAL                         # prev_out on prev_ws
+    assert call(pout=M * 10 + 4096, mask=M * 10) == cpk.CPK_EINVAL   # prev_out on the mask
     assert call(pout=pout + 8) == cpk.CPK_EALIGN
     assert call(pws=pws + 8) == cpk.CPK_EALIGN
     fl = cpk._lib.cpk_ring_flush
@@ -309,6 +313,7 @@ def test_ring_step_deferred_validation():
     assert fl(ws, need, out, Hq, Hkv, C, c, 96, F16, None) == cpk.CPK_EDTYPE
 
 
+@no_gpu
 def test_varlen_phases_validation():
     """cpk_varlen_step_phases takes a nonzero subset of the three phases."""
     f = cpk._lib.cpk_varlen_step_phases
@@ -318,6 +323,7 @@ def test_varlen_phases_validation():
         assert r == cpk.CPK_EINVAL, bad
 
 
+@no_gpu
 def test_paged_validation():
     """Paged caches: block_size a positive multiple of 256, a block table,
     positive counts, at most 512 blocks per sequence, bf16/fp16 only --
@@ -335,6 +341,7 @@ def test_paged_validation():
     assert f(*args(desc(dt=cpk.CPK_F32))) == cpk.CPK_EDTYPE
 
 
+@no_gpu
 def test_copy_prefix_validation():
     c = cpk.cpk_kv_cache(FAKE, FAKE * 2, FAKE * 3, 2, 4, 1024, 128, cpk.CPK_BF16)
     f = cpk._lib.cpk_kv_copy_prefix
