@@ -1414,7 +1414,10 @@ void attn_wide_kernel(AttnArgs a)
 // * the workgroup's query rows are read from global memory once, into LDS
 //   by column group 1 beside the first tile's loads (the four key-slice
 //   waves of a column group need the same query fragments), and each wave
-//   takes its fragments from LDS after the first tile's barrier.
+//   takes its fragments from LDS after the first tile's barrier;
+// * with prev_ws set (a deferred ring step), column group 1 also merges its
+//   workgroup's share of the previous split launch's parts (combine_unit)
+//   while the first tile is in flight.
 // Arithmetic, fragment layouts, swizzles, the lazy maximum, the epilogue
 // merge and the fused append are those of attn_mfma_kernel, so results are
 // bit-identical to it.
