@@ -437,9 +437,10 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=50, warm=
     """Rolling right-aligned cache: 4096 fp16 tokens, 16 heads, C = 2048,
     c = 256; per chunk roll_append (out of place, double-buffered: C rows
     moved) then roll_attention, or with ring=True one cpk_ring_step (the c
-    new rows written into the ring by the attention launch), or with
-    deferred=True too one cpk_ring_step_deferred (the chunk's key-range
-    parts merged by the next chunk's launch, the last chunk's by one flush);
+    new rows written into the ring by the attention launch); deferred=True
+    takes the deferred form of either (cpk_roll_attention_deferred or
+    cpk_ring_step_deferred: the chunk's key-range parts merged by the next
+    chunk's launch, the last chunk's by one flush);
     with the explicit (c, C) additive mask (0 visible, -32768 masked) or
     visibility computed in the kernel.  Median of reps timed passes over the
     16 chunks."""
@@ -471,7 +472,7 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=50, warm=
                     q[sl], k[sl], v[sl], bufs[0][0], bufs[1][0], (j + 1) * c, 0, start,
                     wss[j % 2], prev=pending, mask=m, out=out[sl])
                 if j == n - 1:
-                    cpk.cpk_ring_flush(pending)
+                    cpk.cpk_roll_flush(pending)
                 continue
             if ring:
                 # the append runs inside the attention launch
@@ -482,6 +483,13 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=50, warm=
             kn, vn = bufs[2 * (1 - cur)], bufs[2 * (1 - cur) + 1]
             cpk.cpk_roll_append(ko, vo, k[sl].unsqueeze(0), v[sl].unsqueeze(0), kn, vn)
             cur = 1 - cur
+            if deferred:
+                pending = cpk.cpk_roll_attention_deferred(q[sl], kn[0], vn[0], (j + 1) * c, 0,
+                                                          wss[j % 2], prev=pending, mask=m,
+                                                          out=out[sl])
+                if j == n - 1:
+                    cpk.cpk_roll_flush(pending)
+                continue
             cpk.cpk_roll_attention(q[sl], kn[0], vn[0], (j + 1) * c, 0, mask=m, out=out[sl])
 
     # the 16 chunks are captured once as a HIP graph (after an eager pass
@@ -531,6 +539,8 @@ def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=50, warm=
     what = ("ring_step_deferred (append fused into the attention, each chunk's split merged "
             "by the next chunk's launch, the last by a flush)" if ring and deferred else
             "ring_step (append fused into the attention)" if ring else
+            "roll_append + roll_attention_deferred (each chunk's split merged by the next "
+            "chunk's launch, the last by a flush)" if deferred else
             "roll_append + roll_attention")
     return {"chunks": n, "gflop": round(f / 1e9, 2), "ms": round(ms, 4), "ms_min": round(min(times), 4),
             "tflops": round(f / (ms * 1e-3) / 1e12, 1), "dtype": "fp16", "roofline": roof,
@@ -826,8 +836,8 @@ def main():
                          "ladder, rolling, mixed (default all)")
     ap.add_argument("--rolling", default="all",
                     help="comma list of rolling schedules to run: shift_mask, shift_computed, "
-                         "ring_mask, ring_computed, ring_deferred_mask, ring_deferred_computed "
-                         "(default all)")
+                         "ring_mask, ring_computed, shift_deferred_mask, shift_deferred_computed, "
+                         "ring_deferred_mask, ring_deferred_computed (default all)")
     ap.add_argument("--mixed", default="all",
                     help="comma list of mixed steps to run, as budget[_two_streams][_paged] "
                          "(default all five)")
@@ -876,6 +886,9 @@ def main():
                     "shift_computed": ("rolling_fp16_computed_mask", False, False, False),
                     "ring_mask": ("rolling_fp16_ring", True, True, False),
                     "ring_computed": ("rolling_fp16_ring_computed_mask", False, True, False),
+                    "shift_deferred_mask": ("rolling_fp16_deferred", True, False, True),
+                    "shift_deferred_computed": ("rolling_fp16_deferred_computed_mask", False,
+                                                False, True),
                     "ring_deferred_mask": ("rolling_fp16_ring_deferred", True, True, True),
                     "ring_deferred_computed": ("rolling_fp16_ring_deferred_computed_mask", False,
                                                True, True)}

@@ -88,7 +88,9 @@ def _load() -> ctypes.CDLL:
         "cpk_ring_step": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, Z, P], I),
         "cpk_ring_step_deferred": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, Z, P,
                                     P, P], I),
-        "cpk_ring_flush": ([P, Z, P, I, I, I, I, I, I, P], I),
+        "cpk_roll_flush": ([P, Z, P, I, I, I, I, I, I, P], I),
+        "cpk_roll_attention_deferred": ([P, P, P, P, I, I, I, I, I, I, I, I, F, P, P, Z, P, P,
+                                         P], I),
         "cpk_ring_view": ([P, P, P, P, I, I, I, I, I, I, P], I),
     }
     for name, (args, res) in sig.items():
@@ -532,9 +534,9 @@ def cpk_ring_step(q, k_chunk, v_chunk, k_ring, v_ring, abs_end: int, n_leftpad: 
     return out, (start + c) % C
 
 
-class RingPending(NamedTuple):
-    """Parts a deferred ring step left unmerged: merged into `out` by the
-    next deferred call (passed as prev) or by cpk_ring_flush."""
+class RollPending(NamedTuple):
+    """Parts a deferred rolling call left unmerged: merged into `out` by the
+    next deferred call (passed as prev) or by cpk_roll_flush."""
     ws: torch.Tensor
     out: torch.Tensor
     Hq: int
@@ -544,11 +546,11 @@ class RingPending(NamedTuple):
 
 
 def cpk_ring_step_deferred(q, k_chunk, v_chunk, k_ring, v_ring, abs_end: int, n_leftpad: int,
-                           start: int, ws, prev: Optional[RingPending] = None, mask=None,
+                           start: int, ws, prev: Optional[RollPending] = None, mask=None,
                            scale: float = 0.0, out=None, stream=None):
     """cpk_ring_step whose key-range parts stay in ws (a workspace of
     cpk_roll_workspace_size bytes; the previous call's must be another) and
-    are merged into out by the next deferred call or cpk_ring_flush; this
+    are merged into out by the next deferred call or cpk_roll_flush; this
     launch merges prev's parts.  Returns (pending, new start)."""
     c, Hq, D = q.shape
     Hkv, C, _ = k_ring.shape
@@ -559,13 +561,33 @@ def cpk_ring_step_deferred(q, k_chunk, v_chunk, k_ring, v_ring, abs_end: int, n_
         n_leftpad, Hq, Hkv, C, c, D, DTYPE_CODE[q.dtype], float(scale), start, _ptr(out),
         _ptr(ws), ws.numel() * ws.element_size(), None if prev is None else _ptr(prev.ws),
         None if prev is None else _ptr(prev.out), _stream(stream)))
-    return RingPending(ws, out, Hq, Hkv, C, c), (start + c) % C
+    return RollPending(ws, out, Hq, Hkv, C, c), (start + c) % C
 
 
-def cpk_ring_flush(pending: RingPending, stream=None) -> torch.Tensor:
+def cpk_roll_attention_deferred(q, k, v, abs_end: int, n_leftpad: int, ws,
+                                prev: Optional[RollPending] = None, mask=None, scale: float = 0.0,
+                                out=None, stream=None):
+    """cpk_roll_attention over the literal cache k/v [Hkv, C, D] whose
+    key-range parts stay in ws (cpk_roll_workspace_size bytes; the previous
+    call's must be another) and are merged into out by the next deferred
+    call or cpk_roll_flush; this launch merges prev's parts.  Returns the
+    pending merge."""
+    c, Hq, D = q.shape
+    Hkv, C, _ = k.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(_lib.cpk_roll_attention_deferred(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(mask), abs_end, n_leftpad, Hq, Hkv, C, c, D,
+        DTYPE_CODE[q.dtype], float(scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+        None if prev is None else _ptr(prev.ws), None if prev is None else _ptr(prev.out),
+        _stream(stream)))
+    return RollPending(ws, out, Hq, Hkv, C, c)
+
+
+def cpk_roll_flush(pending: RollPending, stream=None) -> torch.Tensor:
     """Merge the parts a deferred ring step left pending; returns its out."""
     ws, out = pending.ws, pending.out
-    _check(_lib.cpk_ring_flush(_ptr(ws), ws.numel() * ws.element_size(), _ptr(out), pending.Hq,
+    _check(_lib.cpk_roll_flush(_ptr(ws), ws.numel() * ws.element_size(), _ptr(out), pending.Hq,
                                pending.Hkv, pending.C, pending.c, out.shape[2],
                                DTYPE_CODE[out.dtype], _stream(stream)))
     return out
@@ -600,11 +622,14 @@ def prefill_chunked(cache: KVCache, b: int, q, k, v, W: int, pad: bool = True,
 
 
 def roll_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream=None,
-                 split: bool = True):
+                 split: bool = True, defer: bool = True):
     """Rolling fixed-capacity prefill of one sequence (batch 1).  q/k/v are
     token-major real tokens; the sequence is left-padded with zero rows to a
     multiple of c.  masks: optional list of per-chunk (c, C) additive masks;
-    without it visibility is computed in the kernel.  Returns
+    without it visibility is computed in the kernel.  Where the key range
+    splits (split, bf16/fp16) and defer is set, each chunk's attention runs
+    cpk_roll_attention_deferred (its parts merged by the next chunk's
+    launch, the last by cpk_roll_flush); same outputs, bit for bit.  Returns
     (out over the padded sequence, n_leftpad, k cache, v cache)."""
     L, Hq, D = q.shape
     Hkv = k.shape[1]
@@ -616,7 +641,9 @@ def roll_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream
     Lp = L + n_left
     bufs = [torch.zeros((1, Hkv, C, D), dtype=q.dtype, device=q.device) for _ in range(4)]
     out = torch.empty_like(q)
-    cur = 0
+    nbytes = cpk_roll_workspace_size(Hq, Hkv, C, c, D, q.dtype) if split and defer else 0
+    wss = [_roll_workspace(nbytes, q.device, 1 + i) for i in range(2)] if nbytes else None
+    cur, pending = 0, None
     for j in range(Lp // c):
         sl = slice(j * c, (j + 1) * c)
         ko, vo = bufs[2 * cur], bufs[2 * cur + 1]
@@ -624,8 +651,15 @@ def roll_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream
         cpk_roll_append(ko, vo, k[sl].unsqueeze(0), v[sl].unsqueeze(0), kn, vn, stream)
         cur = 1 - cur
         m = None if masks is None else masks[j]
+        if wss:
+            pending = cpk_roll_attention_deferred(q[sl], kn[0], vn[0], (j + 1) * c, n_left,
+                                                  wss[j % 2], prev=pending, mask=m, scale=scale,
+                                                  out=out[sl], stream=stream)
+            continue
         cpk_roll_attention(q[sl], kn[0], vn[0], (j + 1) * c, n_left, mask=m, scale=scale,
                            out=out[sl], stream=stream, split=split)
+    if pending is not None:
+        cpk_roll_flush(pending, stream)
     return out, n_left, bufs[2 * cur][0], bufs[2 * cur + 1][0]
 
 
@@ -636,7 +670,7 @@ def ring_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream
     cpk_ring_append then cpk_ring_attention.  Where the key range splits
     (fused, split, bf16/fp16) and defer is set, each chunk runs
     cpk_ring_step_deferred (its parts merged by the next chunk's launch, the
-    last by cpk_ring_flush).  Same outputs, bit for bit.  Returns (out over
+    last by cpk_roll_flush).  Same outputs, bit for bit.  Returns (out over
     the padded sequence, n_leftpad, k ring, v ring, start)."""
     L, Hq, D = q.shape
     Hkv = k.shape[1]
@@ -661,7 +695,7 @@ def ring_prefill(q, k, v, C: int, c: int, masks=None, scale: float = 0.0, stream
                 prev=pending, mask=None if masks is None else masks[j], scale=scale,
                 out=out[sl], stream=stream)
         if pending is not None:
-            cpk_ring_flush(pending, stream)
+            cpk_roll_flush(pending, stream)
         return out, n_left, kr[0], vr[0], start
     for j in range(Lp // c):
         sl = slice(j * c, (j + 1) * c)

@@ -681,7 +681,7 @@ static int roll_attention_impl(const void *q, const void *k, const void *v, cons
             m.part_ws = (float *)prev_ws;
             m.out = prev_out;
             r = hip_status(cpk::launch_attention_combine(m, dtype, (hipStream_t)stream),
-                           "ring_step_deferred merge");
+                           "deferred merge");
             if (r) return r;
         }
     }
@@ -782,6 +782,51 @@ int cpk_ring_step(const void *q, const void *k_chunk, const void *v_chunk, void 
                                dtype, scale, next, out, ws, ws_bytes, stream, k_chunk, v_chunk);
 }
 
+// Checks of a deferred rolling call (after roll_check): the shapes split
+// the key range, ws is set, and a carried merge's buffers are aligned and
+// overlap nothing this launch reads or writes.  k / v are the cache or the
+// rings; k_extra / v_extra the chunk rows of a ring step (or NULL).
+static int deferred_check(const char *who, const void *q, const void *k, const void *v,
+                          const void *mask, int Hq, int Hkv, int C, int c, int D, int dtype,
+                          const void *ws, const void *prev_ws, const void *prev_out,
+                          const void *k_extra, const void *v_extra, size_t extra_bytes)
+{
+    const size_t need = cpk_roll_workspace_size(Hq, Hkv, C, c, D, dtype);
+    if (need == 0 || !ws)
+        return fail(CPK_EINVAL, "%s: these shapes do not split the key range", who);
+    if (!prev_ws) return ok();
+    if (!prev_out) return fail(CPK_EINVAL, "%s: prev_ws without prev_out", who);
+    if (!aligned16(prev_ws) || !aligned16(prev_out))
+        return fail(CPK_EALIGN, "%s: prev_ws / prev_out not aligned", who);
+    if (overlaps(prev_ws, need, ws, need)) return fail(CPK_EINVAL, "%s: prev_ws overlaps ws", who);
+    const size_t out_bytes = (size_t)c * Hq * D * elem_size(dtype);
+    const size_t kv_bytes = (size_t)Hkv * C * D * elem_size(dtype);
+    const size_t mask_bytes = (size_t)c * C * elem_size(dtype);
+    const void *read[8] = {q, k, v, prev_ws, mask, k_extra, v_extra, ws};
+    const size_t len[8] = {out_bytes, kv_bytes, kv_bytes, need, mask_bytes, extra_bytes,
+                           extra_bytes, need};
+    for (int i = 0; i < 8; ++i)
+        if (read[i] && overlaps(prev_out, out_bytes, read[i], len[i]))
+            return fail(CPK_EINVAL, "%s: prev_out overlaps another buffer of the call", who);
+    return ok();
+}
+
+int cpk_roll_attention_deferred(const void *q, const void *k, const void *v, const void *mask,
+                                int abs_end, int n_leftpad, int Hq, int Hkv, int C, int c, int D,
+                                int dtype, float scale, void *out, void *ws, size_t ws_bytes,
+                                const void *prev_ws, void *prev_out, void *stream)
+{
+    int r = roll_check(q, k, v, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D, dtype, out, ws,
+                       ws_bytes);
+    if (r) return r;
+    if ((r = deferred_check("roll_attention_deferred", q, k, v, mask, Hq, Hkv, C, c, D, dtype,
+                            ws, prev_ws, prev_out, nullptr, nullptr, 0)))
+        return r;
+    return roll_attention_impl(q, k, v, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D, dtype, scale,
+                               0, out, ws, ws_bytes, stream, nullptr, nullptr, true, prev_ws,
+                               prev_out);
+}
+
 int cpk_ring_step_deferred(const void *q, const void *k_chunk, const void *v_chunk,
                            void *k_ring, void *v_ring, const void *mask, int abs_end,
                            int n_leftpad, int Hq, int Hkv, int C, int c, int D, int dtype,
@@ -793,50 +838,31 @@ int cpk_ring_step_deferred(const void *q, const void *k_chunk, const void *v_chu
     if (r) return r;
     if ((r = ring_step_check(k_chunk, v_chunk, k_ring, v_ring, Hkv, C, c, D, dtype, start)))
         return r;
-    const size_t need = cpk_roll_workspace_size(Hq, Hkv, C, c, D, dtype);
-    if (need == 0 || !ws)
-        return fail(CPK_EINVAL, "ring_step_deferred: these shapes do not split the key range "
-                                "(use cpk_ring_step)");
-    if (prev_ws) {
-        if (!prev_out) return fail(CPK_EINVAL, "ring_step_deferred: prev_ws without prev_out");
-        if (!aligned16(prev_ws) || !aligned16(prev_out))
-            return fail(CPK_EALIGN, "ring_step_deferred: prev_ws / prev_out not aligned");
-        const size_t out_bytes = (size_t)c * Hq * D * elem_size(dtype);
-        const size_t ring_bytes = (size_t)Hkv * C * D * elem_size(dtype);
-        const size_t chunk_bytes = (size_t)c * Hkv * D * elem_size(dtype);
-        if (overlaps(prev_ws, need, ws, need))
-            return fail(CPK_EINVAL, "ring_step_deferred: prev_ws overlaps ws");
-        const size_t mask_bytes = (size_t)c * C * elem_size(dtype);
-        const void *read[7] = {q, k_chunk, v_chunk, k_ring, v_ring, prev_ws, mask};
-        const size_t len[7] = {out_bytes, chunk_bytes, chunk_bytes, ring_bytes, ring_bytes,
-                               need, mask_bytes};
-        for (int i = 0; i < 7; ++i)
-            if (read[i] && overlaps(prev_out, out_bytes, read[i], len[i]))
-                return fail(CPK_EINVAL, "ring_step_deferred: prev_out overlaps an input");
-        if (overlaps(prev_out, out_bytes, ws, need))
-            return fail(CPK_EINVAL, "ring_step_deferred: prev_out overlaps ws");
-    }
+    const size_t chunk_bytes = (size_t)c * Hkv * D * elem_size(dtype);
+    if ((r = deferred_check("ring_step_deferred", q, k_ring, v_ring, mask, Hq, Hkv, C, c, D,
+                            dtype, ws, prev_ws, prev_out, k_chunk, v_chunk, chunk_bytes)))
+        return r;
     return roll_attention_impl(q, k_ring, v_ring, mask, abs_end, n_leftpad, Hq, Hkv, C, c, D,
                                dtype, scale, (start + c) % C, out, ws, ws_bytes, stream, k_chunk,
                                v_chunk, true, prev_ws, prev_out);
 }
 
-int cpk_ring_flush(const void *ws, size_t ws_bytes, void *out, int Hq, int Hkv, int C, int c,
+int cpk_roll_flush(const void *ws, size_t ws_bytes, void *out, int Hq, int Hkv, int C, int c,
                    int D, int dtype, void *stream)
 {
     int r = check_dtype_dim(dtype, D);
     if (r) return r;
     if ((r = check_heads(Hq, Hkv))) return r;
-    if (C < 1 || c < 1 || c > C) return fail(CPK_EINVAL, "ring_flush: C=%d c=%d", C, c);
+    if (C < 1 || c < 1 || c > C) return fail(CPK_EINVAL, "roll_flush: C=%d c=%d", C, c);
     const size_t need = cpk_roll_workspace_size(Hq, Hkv, C, c, D, dtype);
     if (need == 0)
-        return fail(CPK_EINVAL, "ring_flush: these shapes do not split the key range");
-    if (!ws || !out) return fail(CPK_EINVAL, "ring_flush: NULL buffer");
+        return fail(CPK_EINVAL, "roll_flush: these shapes do not split the key range");
+    if (!ws || !out) return fail(CPK_EINVAL, "roll_flush: NULL buffer");
     if (ws_bytes < need)
-        return fail(CPK_EWORKSPACE, "ring_flush: workspace %zu bytes, need %zu", ws_bytes, need);
-    if (!aligned16(ws) || !aligned16(out)) return fail(CPK_EALIGN, "ring_flush: not aligned");
+        return fail(CPK_EWORKSPACE, "roll_flush: workspace %zu bytes, need %zu", ws_bytes, need);
+    if (!aligned16(ws) || !aligned16(out)) return fail(CPK_EALIGN, "roll_flush: not aligned");
     if (overlaps(out, (size_t)c * Hq * D * elem_size(dtype), ws, need))
-        return fail(CPK_EINVAL, "ring_flush: out overlaps ws");
+        return fail(CPK_EINVAL, "roll_flush: out overlaps ws");
     int parts, pt;
     roll_split(Hq, Hkv, C, c, dtype, &parts, &pt);
     cpk::AttnArgs a = {};
@@ -844,7 +870,7 @@ int cpk_ring_flush(const void *ws, size_t ws_bytes, void *out, int Hq, int Hkv, 
     a.out_row0 = 0; a.out_rows = c;
     a.n_parts = parts; a.part_tiles = pt; a.part_ws = (float *)ws;
     return hip_status(cpk::launch_attention_combine(a, dtype, (hipStream_t)stream),
-                      "ring_flush combine");
+                      "roll_flush combine");
 }
 
 int cpk_ring_view(const void *k_ring, const void *v_ring, void *k_out, void *v_out, int B, int H,

@@ -424,7 +424,7 @@ int cpk_ring_step(const void *q, const void *k_chunk, const void *v_chunk, void 
  * ws (out is not written yet), and, with prev_ws set, merges the parts an
  * earlier deferred call of the same shapes left in prev_ws into that
  * call's out, passed here as prev_out.  The chunk's output is complete
- * once the next deferred call (or cpk_ring_flush(ws, out)) has run on the
+ * once the next deferred call (or cpk_roll_flush(ws, out)) has run on the
  * same stream; it is bit-identical to cpk_ring_step's.  A chain of calls
  * alternates two workspaces (each cpk_roll_workspace_size bytes): call j
  * writes ws_j and merges ws_(j-1).  Only shapes that split the key range
@@ -432,8 +432,8 @@ int cpk_ring_step(const void *q, const void *k_chunk, const void *v_chunk, void 
  * cpk_ring_step, all checked before anything is launched; CPK_EINVAL if
  * the shapes do not split or ws is NULL, if prev_ws is set without
  * prev_out, if prev_ws overlaps ws, or if prev_out overlaps q, a chunk, a
- * ring, the mask, ws or prev_ws; CPK_EALIGN if prev_ws or prev_out is not 16-byte
- * aligned.  The caller keeps prev_ws's shapes equal to this call's.
+ * ring, the mask, ws or prev_ws; CPK_EALIGN if prev_ws or prev_out is not
+ * 16-byte aligned.  The caller keeps prev_ws's shapes equal to this call's.
  */
 int cpk_ring_step_deferred(const void *q, const void *k_chunk, const void *v_chunk,
                            void *k_ring, void *v_ring, const void *mask, int abs_end,
@@ -442,13 +442,31 @@ int cpk_ring_step_deferred(const void *q, const void *k_chunk, const void *v_chu
                            const void *prev_ws, void *prev_out, void *stream);
 
 /*
- * The merge a deferred ring step left pending: the parts in ws (written by
- * cpk_ring_step_deferred with these shapes) merged into out
- * [c][Hq][D] (one combine launch).  CPK_EINVAL if the shapes do not split,
- * a buffer is NULL or out overlaps ws; CPK_EWORKSPACE if ws_bytes is below
- * cpk_roll_workspace_size; CPK_EALIGN if ws or out is not 16-byte aligned.
+ * cpk_roll_attention over the literal shifted cache with the same carried
+ * merge as cpk_ring_step_deferred (Horizon developer blog "Chunk Prefill",
+ * section 4, run as a pipeline over the chunks): this chunk's parts stay in
+ * ws, and the parts a previous deferred call of the same shapes left in
+ * prev_ws are merged into prev_out by this launch; bit-identical to
+ * cpk_roll_attention once merged.  Errors: those of cpk_roll_attention,
+ * all checked before anything is launched; CPK_EINVAL if the shapes do not
+ * split or ws is NULL, if prev_ws is set without prev_out, if prev_ws
+ * overlaps ws, or if prev_out overlaps q, k, v, the mask, ws or prev_ws;
+ * CPK_EALIGN if prev_ws or prev_out is not 16-byte aligned.
  */
-int cpk_ring_flush(const void *ws, size_t ws_bytes, void *out, int Hq, int Hkv, int C, int c,
+int cpk_roll_attention_deferred(const void *q, const void *k, const void *v, const void *mask,
+                                int abs_end, int n_leftpad, int Hq, int Hkv, int C, int c, int D,
+                                int dtype, float scale, void *out, void *ws, size_t ws_bytes,
+                                const void *prev_ws, void *prev_out, void *stream);
+
+/*
+ * The merge a deferred rolling call (cpk_ring_step_deferred or
+ * cpk_roll_attention_deferred) left pending: the parts in ws, written with
+ * these shapes, merged into out [c][Hq][D] (one combine launch).
+ * CPK_EINVAL if the shapes do not split, a buffer is NULL or out overlaps
+ * ws; CPK_EWORKSPACE if ws_bytes is below cpk_roll_workspace_size;
+ * CPK_EALIGN if ws or out is not 16-byte aligned.
+ */
+int cpk_roll_flush(const void *ws, size_t ws_bytes, void *out, int Hq, int Hkv, int C, int c,
                    int D, int dtype, void *stream);
 
 /*

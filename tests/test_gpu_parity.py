@@ -623,7 +623,7 @@ def test_ring_step_deferred_bit_equal(kernel, dtype, C, c, Hq, Hkv, D):
                                                      (j + 1) * c, 0, start, mask=masks[j],
                                                      out=out[sl])
                 if pending is not None:
-                    cpk.cpk_ring_flush(pending)
+                    cpk.cpk_roll_flush(pending)
                 torch.cuda.synchronize()
                 res.append((out, kr, vr, start))
             (oa, ka, va, sa), (ob, kb, vb, sb) = res
@@ -631,6 +631,56 @@ def test_ring_step_deferred_bit_equal(kernel, dtype, C, c, Hq, Hkv, D):
             assert sa == sb
             assert bitwise(oa, ob), f"{tag}: outputs differ"
             assert bitwise(ka, kb) and bitwise(va, vb), f"{tag}: rings differ"
+
+
+@pytest.mark.parametrize("kernel", ["narrow", "general"])
+@pytest.mark.parametrize("dtype,C,c,Hq,Hkv,D", [
+    ("f16", 512, 128, 4, 4, 128),     # 4 parts of 1 tile
+    ("bf16", 300, 96, 4, 2, 64),      # 3 parts, GQA, C not a multiple of the key tile
+])
+def test_roll_attention_deferred_bit_equal(kernel, dtype, C, c, Hq, Hkv, D):
+    """The literal-shift schedule with each chunk's split merged by the next
+    chunk's attention launch (cpk_roll_attention_deferred, the last chunk by
+    cpk_roll_flush) gives cpk_roll_attention's bits for every chunk, with
+    computed visibility and with the explicit mask."""
+    say(f"case: deferred roll attention {kernel} {dtype} C={C} c={c} heads {Hq}/{Hkv} D={D}")
+    tdt = si.TORCH_DTYPE[dtype]
+    g = si.generator(560 + C)
+    n = 5
+    q = si.randn((n * c, Hq, D), dtype, g).cuda()
+    k = si.randn((n * c, Hkv, D), dtype, g).cuda()
+    v = si.randn((n * c, Hkv, D), dtype, g).cuda()
+    L = n * c
+    nbytes = cpk.cpk_roll_workspace_size(Hq, Hkv, C, c, D, tdt)
+    assert nbytes > 0, "the case must split the key range"
+    wss = [torch.full((nbytes // 4 + 4,), float("nan"), device="cuda") for _ in range(2)]
+    with cpk.attention_kernel(KERNELS[kernel]):
+        for explicit in (False, True):
+            masks = [torch.from_numpy(oracle.chunk_mask(L, 0, j, c, C)).to(tdt).cuda()
+                     if explicit else None for j in range(n)]
+            outs = []
+            for deferred in (False, True):
+                bufs = [torch.zeros((1, Hkv, C, D), dtype=tdt, device="cuda") for _ in range(4)]
+                out = torch.full((L, Hq, D), float("nan"), dtype=tdt, device="cuda")
+                cur, pending = 0, None
+                for j in range(n):
+                    sl = slice(j * c, (j + 1) * c)
+                    ko, vo = bufs[2 * cur], bufs[2 * cur + 1]
+                    kn, vn = bufs[2 * (1 - cur)], bufs[2 * (1 - cur) + 1]
+                    cpk.cpk_roll_append(ko, vo, k[sl].unsqueeze(0), v[sl].unsqueeze(0), kn, vn)
+                    cur = 1 - cur
+                    if deferred:
+                        pending = cpk.cpk_roll_attention_deferred(
+                            q[sl], kn[0], vn[0], (j + 1) * c, 0, wss[j % 2], prev=pending,
+                            mask=masks[j], out=out[sl])
+                    else:
+                        cpk.cpk_roll_attention(q[sl], kn[0], vn[0], (j + 1) * c, 0,
+                                               mask=masks[j], out=out[sl])
+                if pending is not None:
+                    cpk.cpk_roll_flush(pending)
+                torch.cuda.synchronize()
+                outs.append(out)
+            assert bitwise(outs[0], outs[1]), f"mask={explicit}: outputs differ"
 
 
 @pytest.mark.parametrize("dtype,C,c,Hq,Hkv,D", [

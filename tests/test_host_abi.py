@@ -304,13 +304,43 @@ def test_ring_step_deferred_validation():
     assert call(pout=M * 10 + 4096, mask=M * 10) == cpk.CPK_EINVAL   # prev_out on the mask
     assert call(pout=pout + 8) == cpk.CPK_EALIGN
     assert call(pws=pws + 8) == cpk.CPK_EALIGN
-    fl = cpk._lib.cpk_ring_flush
+    fl = cpk._lib.cpk_roll_flush
     assert fl(ws, need, out, 64, 64, C, c, D, F16, None) == cpk.CPK_EINVAL   # no split
     assert fl(ws, need - 4, out, Hq, Hkv, C, c, D, F16, None) == cpk.CPK_EWORKSPACE
     assert fl(ws, need, ws + 4096, Hq, Hkv, C, c, D, F16, None) == cpk.CPK_EINVAL
     assert fl(None, need, out, Hq, Hkv, C, c, D, F16, None) == cpk.CPK_EINVAL
     assert fl(ws, need, out + 8, Hq, Hkv, C, c, D, F16, None) == cpk.CPK_EALIGN
     assert fl(ws, need, out, Hq, Hkv, C, c, 96, F16, None) == cpk.CPK_EDTYPE
+
+
+@no_gpu
+def test_roll_attention_deferred_validation():
+    """The deferred literal-shift attention rejects, on the host, shapes that
+    do not split, a missing or short workspace and a carried merge whose
+    buffers alias the call's other buffers (fake aligned pointers, 64 MiB
+    apart; every call here fails before a launch)."""
+    F16 = cpk.CPK_F16
+    M = 1 << 26
+    q, k, v, out, ws, pws, pout, mask = (M * i for i in range(1, 9))
+    Hq = Hkv = 16
+    C, c, D = 2048, 256, 128
+    need = cpk.cpk_roll_workspace_size(Hq, Hkv, C, c, D, torch.float16)
+    f = cpk._lib.cpk_roll_attention_deferred
+
+    def call(heads=Hq, ws=ws, ws_bytes=need, pws=pws, pout=pout, mask=None, abs_end=C):
+        return f(q, k, v, mask, abs_end, 0, heads, heads, C, c, D, F16, 0.0, out, ws, ws_bytes,
+                 pws, pout, None)
+
+    assert call(heads=64, ws=None, ws_bytes=0) == cpk.CPK_EINVAL    # no split
+    assert call(ws=None, ws_bytes=0) == cpk.CPK_EINVAL              # no workspace
+    assert call(ws_bytes=need - 4) == cpk.CPK_EWORKSPACE
+    assert call(abs_end=c - 1) == cpk.CPK_EINVAL                    # abs_end < c
+    assert call(pout=None) == cpk.CPK_EINVAL                        # prev_ws alone
+    assert call(pws=ws + 4096) == cpk.CPK_EINVAL                    # prev_ws overlaps ws
+    assert call(pout=k + 64) == cpk.CPK_EINVAL                      # prev_out on the cache
+    assert call(pout=ws + 1024) == cpk.CPK_EINVAL                   # prev_out on ws
+    assert call(pout=mask + 4096, mask=mask) == cpk.CPK_EINVAL      # prev_out on the mask
+    assert call(pout=pout + 8) == cpk.CPK_EALIGN
 
 
 @no_gpu
