@@ -22,7 +22,8 @@ secondary = the fp32 demo (time only); decode rows of the mixed-step
          workload (64 sequences, contexts uniform in [512, 16384]) as a
          decode-only packed step: KV bytes read per second against the 8 TB/s
          HBM peak, for the whole step and for the decode kernel alone; a
-         steady-state W=512 chunk at past_len 7680; the ladder prompts (useful
+         steady-state W=512 chunk at past_len 7680; the same prompt chunked at
+         W = 256, 512, 1024 and 2048; the ladder prompts (useful
          and issued TFLOP/s); the rolling fp16 cache against the larger of its
          HBM and MFMA bounds; the mixed decode + prefill step at budgets 2048
          and 8192 against its sum and max bounds.
@@ -279,6 +280,55 @@ def bench_demo_fp32(cpk, si, torch, reps=20):
     return {"chunks": [list(c) for c in chunks], "gflop": round(f / 1e9, 3), "ms": round(ms, 4),
             "tflops": round(f / (ms * 1e-3) / 1e12, 2), "dtype": "fp32",
             "note": "eager calls (rewind + 4 chunk launches), HIP events over 20 passes"}
+
+
+def bench_widths(cpk, si, torch, q, k, v, widths=(256, 512, 1024, 2048), reps=10, warm=3):
+    """The 4000-token GQA prompt chunked at other widths W (the chunk-size
+    trade-off of the pages: small chunks re-read the growing cache more
+    often): rewind + cpk_prefill_chunk per chunk (padded tail), captured once
+    as a HIP graph per W; median of reps replays after warm.  Each chunk
+    launch takes the kernel the library picks for its size (W >= 1024: the
+    128-column kernel).  TFLOP/s counts the prompt's causal pairs once."""
+    L, Hq, Hkv, D = q.shape[0], q.shape[1], k.shape[1], q.shape[2]
+    f = 4 * D * Hq * (L * (L + 1) // 2)
+    table = {}
+    for W in widths:
+        cache = cpk.KVCache(1, Hkv, 8192, D, torch.bfloat16)
+        out = torch.empty_like(q)
+        chunks = cpk.cpk_split_chunks(L, W)
+
+        def run():
+            cpk.cpk_rewind(cache, 0, 0)
+            for past, rows in chunks:
+                sl = slice(past, past + rows)
+                cpk.cpk_prefill_chunk(q[sl], k[sl], v[sl], cache, 0, past, W, pad=True,
+                                      out=out[sl])
+
+        cache.lens[0] = 0
+        run()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        for _ in range(warm):
+            graph.replay()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = statistics.median(times)
+        table[f"W{W}"] = {"chunks": len(chunks), "ms": round(ms, 4),
+                          "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
+    return {"prompt_tokens": L, "gflop": round(f / 1e9, 2), "per_width": table,
+            "note": "rewind + padded cpk_prefill_chunk per chunk, graph-replayed, median of "
+                    f"{reps} replays after {warm}"}
 
 
 def bench_steady_chunk(cpk, si, torch, reps=200, warm=50):
@@ -832,8 +882,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary", default="all",
-                    help="comma list of secondary groups to run: demo, steady, decode, "
-                         "ladder, rolling, mixed (default all)")
+                    help="comma list of secondary groups to run: demo, steady, widths, "
+                         "decode, ladder, rolling, mixed (default all)")
     ap.add_argument("--rolling", default="all",
                     help="comma list of rolling schedules to run: shift_mask, shift_computed, "
                          "ring_mask, ring_computed, shift_deferred_mask, shift_deferred_computed, "
@@ -864,7 +914,7 @@ def main():
     ms_graph = bench_step_graph(cpk, si, torch, args.steps, args.warmup, r["q"], r["k"], r["v"])
     log(f"bench: graph-replayed step {ms_graph:.3f} ms")
     secondary = {}
-    groups = {"demo", "steady", "decode", "ladder", "rolling", "mixed"}
+    groups = {"demo", "steady", "widths", "decode", "ladder", "rolling", "mixed"}
     if args.secondary != "all":
         groups = set(args.secondary.split(","))
     if not args.no_secondary:
@@ -875,6 +925,9 @@ def main():
     if not args.no_secondary and "steady" in groups:
         secondary["steady_chunk"] = bench_steady_chunk(cpk, si, torch)
         log(f"bench: steady chunk {secondary['steady_chunk']}")
+    if not args.no_secondary and "widths" in groups:
+        secondary["chunk_widths"] = bench_widths(cpk, si, torch, r["q"], r["k"], r["v"])
+        log(f"bench: chunk widths {secondary['chunk_widths']}")
     if not args.no_secondary and "decode" in groups:
         secondary["decode_rows"] = bench_decode(cpk, si, torch)
         log(f"bench: decode {secondary['decode_rows']}")

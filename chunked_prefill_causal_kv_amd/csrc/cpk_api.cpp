@@ -111,9 +111,12 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 std::atomic<int> g_attn_kernel{CPK_ATTN_AUTO};
 
 // The kernel serving a bf16/fp16 chunk or varlen attention launch of `rows`
-// rows (the longest sequence's, in varlen): the 128-column kernel once its
-// grid fills the CUs, else the 64-column one (unless overridden).
-int pick_kernel(int dtype, int group, int kv_heads, int rows)
+// rows (the longest sequence's, in varlen) and `pairs` visible (row, key)
+// pairs per query head (summed over the launch's sequences): the 128-column
+// kernel once its grid fills the CUs and the launch is long enough to
+// amortise its per-workgroup fixed cost, else the 64-column one (unless
+// overridden).
+int pick_kernel(int dtype, int group, int kv_heads, int rows, int64_t pairs)
 {
     if (dtype == CPK_F32) return cpk::kAttnNarrow;
     const int k = g_attn_kernel.load(std::memory_order_relaxed);
@@ -121,8 +124,14 @@ int pick_kernel(int dtype, int group, int kv_heads, int rows)
     if (k == CPK_ATTN_NARROW) return cpk::kAttnNarrow;
     if (k == CPK_ATTN_NARROW_GENERAL) return cpk::kAttnNarrowGeneral;
     const int br = cpk::attn_rows_per_block(dtype, group, true);
-    return (int64_t)((rows + br - 1) / br) * kv_heads >= cpk::kWideMinGroups ? cpk::kAttnWide
-                                                                              : cpk::kAttnNarrow;
+    const bool fills = (int64_t)((rows + br - 1) / br) * kv_heads >= cpk::kWideMinGroups;
+    return fills && pairs >= cpk::kWideMinPairs ? cpk::kAttnWide : cpk::kAttnNarrow;
+}
+
+// Visible (row, key) pairs per query head of `rows` causal rows after `past` keys.
+int64_t causal_pairs(int past, int rows)
+{
+    return (int64_t)rows * past + (int64_t)rows * (rows + 1) / 2;
 }
 
 }  // namespace
@@ -252,7 +261,8 @@ static int attention_common(const void *q, const cpk_kv_cache *cache, int b, int
         a.k_new = k_new; a.v_new = v_new; a.new_base = past_len; a.new_rows = real_rows;
         a.seqlens = cache->seqlens_k; a.len_after = past_len + real_rows;
     }
-    const int kern = pick_kernel(cache->dtype, q_heads / cache->kv_heads, cache->kv_heads, rows);
+    const int kern = pick_kernel(cache->dtype, q_heads / cache->kv_heads, cache->kv_heads, rows,
+                                 causal_pairs(past_len, rows));
     const int br = cpk::attn_rows_per_block(cache->dtype, q_heads / cache->kv_heads,
                                             kern == cpk::kAttnWide);
     return hip_status(cpk::launch_attention(a, cache->dtype, (rows + br - 1) / br, 1, kern, st),
@@ -448,6 +458,7 @@ static int varlen_impl(const void *q, const void *k_new, const void *v_new,
         return fail(CPK_EINVAL, "varlen: cu_rows must run from 0 to total_rows");
     std::vector<char> used((size_t)cache->batch, 0);
     int max_ctx = 0, max_rows = 0, n_dec = 0, n_pre = 0;
+    int64_t pre_pairs = 0;   // visible pairs per head of the prompt rows
     int pre_lo = n_seqs, pre_hi = 0;   // range of the sequences with prompt rows
     const int G = q_heads / cache->kv_heads;
     const bool dec_ok = cpk::decode_supported(cache->dtype, cache->head_dim, G, cache->capacity);
@@ -468,6 +479,7 @@ static int varlen_impl(const void *q, const void *k_new, const void *v_new,
             if (past + 1 > max_ctx) max_ctx = past + 1;
         } else {
             ++n_pre;
+            pre_pairs += causal_pairs(past, rows);
             if (rows > max_rows) max_rows = rows;
             if (s < pre_lo) pre_lo = s;
             pre_hi = s + 1;
@@ -526,7 +538,7 @@ static int varlen_impl(const void *q, const void *k_new, const void *v_new,
             a.block_table = pg->table; a.max_blocks = pg->max_blocks;
             a.block_size = pg->block_size; a.n_blocks = pg->n_blocks;
         }
-        const int kern = pick_kernel(cache->dtype, G, cache->kv_heads, max_rows);
+        const int kern = pick_kernel(cache->dtype, G, cache->kv_heads, max_rows, pre_pairs);
         const int br = cpk::attn_rows_per_block(cache->dtype, G, kern == cpk::kAttnWide);
         r = hip_status(cpk::launch_attention(a, cache->dtype, (max_rows + br - 1) / br,
                                              pre_hi - pre_lo, kern, st),

@@ -163,7 +163,12 @@ hipError_t launch_ring_view(const void *k_ring, const void *v_ring, void *k_out,
 // `wide` selects the 128-column bf16/fp16 kernel (chunk and varlen
 // attention only: the rolling form keeps the 64-column kernel, which also
 // takes the explicit additive mask, so both of its forms stay bit-equal).
-constexpr int kWideMinGroups = 256;   // auto choice: wide once its grid fills the CUs
+constexpr int kWideMinGroups = 256;   // auto choice: wide once its grid fills the CUs ...
+// ... and the launch holds at least this many visible (row, key) pairs per
+// query head (rows x (past + rows / 2)): below it the 64-column kernel's
+// smaller per-workgroup fixed cost outweighs the 128-column kernel's cheaper
+// tiles (measured on the 32/8-head, D = 128 shapes)
+constexpr int64_t kWideMinPairs = (int64_t)24 << 20;
 int attn_rows_per_block(int dtype, int group, bool wide);
 // bf16/fp16 kernel of a launch: the 64-column kernel (its latency-scheduled
 // form wherever the launch reads a contiguous cache, its general form over

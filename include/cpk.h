@@ -505,7 +505,9 @@ int cpk_version(void);
  * alone is deterministic and gives a row the same bits whether its prompt
  * runs in one pass or in chunks.  CPK_ATTN_AUTO takes the wide kernel when
  * its launch has at least as many workgroups as the GPU has compute units
- * (256), else the narrow one.  The narrow kernel runs in a latency-scheduled
+ * (256) and at least 24 x 2^20 visible (row, key) pairs per query head
+ * (rows x past + rows x (rows + 1) / 2, summed over a varlen launch's
+ * prompt sequences), else the narrow one.  The narrow kernel runs in a latency-scheduled
  * form wherever the launch reads a contiguous cache (causal, computed or
  * explicit-mask visibility, ring buffer, key split) and in its general form
  * over a paged pool; the two forms give identical bits, and

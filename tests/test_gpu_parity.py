@@ -343,15 +343,43 @@ def test_workload2_gqa_bf16_full_size():
     for kind in ("narrow", "wide"):
         assert bitwise(*res[kind]), f"[{kind}] chunked != one-shot"
     # the automatic choice: 512-row chunks fill 128 wide workgroups (fewer
-    # than the 256 CUs) and take the narrow kernel; the 4000-row pass the wide
+    # than the 256 CUs) and take the narrow kernel; the 4000-row pass fills
+    # 1,000 but holds 8.0 x 10^6 visible pairs per head, below the wide
+    # kernel's 24 x 2^20, and takes the narrow kernel too
     assert bitwise(res["auto"][0], res["narrow"][0])
-    assert bitwise(res["auto"][1], res["wide"][1])
+    assert bitwise(res["auto"][1], res["narrow"][1])
     assert int(cache.seqlens_k[0]) == 4000
     assert np.array_equal(si.storage(cache.k[0, :, :4000]), ks.transpose(1, 0, 2))
     assert np.array_equal(si.storage(cache.v[0, :, :4000]), vs.transpose(1, 0, 2))
 
 
 # ------------------------------------------------- workload 3: padding ladder
+
+@pytest.mark.parametrize("past,rows,expect", [
+    (4096, 4096, "wide"),     # 1,024 wide workgroups, 25.2 x 10^6 pairs per head
+    (0, 4096, "narrow"),      # 1,024 wide workgroups but 8.4 x 10^6 pairs
+    (12288, 992, "narrow"),   # 12.7 x 10^6 pairs, but 248 wide workgroups
+])
+def test_auto_kernel_choice(past, rows, expect):
+    """The automatic kernel choice: the 128-column kernel only for launches
+    that fill the CUs with its workgroups and hold at least 24 x 2^20
+    visible pairs per query head; the output under CPK_ATTN_AUTO has the
+    chosen kernel's bits."""
+    say(f"case: automatic kernel choice, past {past}, rows {rows}: {expect}")
+    Hq, Hkv, D = 32, 8, 128
+    cache = cpk.KVCache(1, Hkv, past + rows, D, torch.bfloat16)
+    si.fill_seeded(cache.k, 41)
+    si.fill_seeded(cache.v, 42)
+    q = si.randn((rows, Hq, D), "bf16", si.generator(43)).cuda()
+    res = {}
+    for kind in ("auto", "narrow", "wide"):
+        with cpk.attention_kernel({"auto": 0, **KERNELS}[kind]):
+            res[kind] = cpk.cpk_chunk_attention(q, cache, 0, past)
+    torch.cuda.synchronize()
+    other = "narrow" if expect == "wide" else "wide"
+    assert bitwise(res["auto"], res[expect])
+    assert not bitwise(res["auto"], res[other]), "the two kernels round differently"
+
 
 def test_workload3_ladder_twice_on_dirty_cache():
     lengths = si.ladder_prompt_lengths()
