@@ -62,7 +62,7 @@ enum cpk_varlen_phase {
 
 /* bf16/fp16 attention kernel choice (cpk_set_attention_kernel) */
 enum cpk_attention_kernel {
-    CPK_ATTN_AUTO = 0,     /* by launch size (the default)                  */
+    CPK_ATTN_AUTO = 0,     /* by grid size and work (the default)           */
     CPK_ATTN_NARROW = 1,   /* 64 query columns per workgroup, 8 waves       */
     CPK_ATTN_WIDE = 2,     /* 128 query columns per workgroup, 4 waves      */
     CPK_ATTN_NARROW_GENERAL = 3, /* the 64-column kernel's general form even
