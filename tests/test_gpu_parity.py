@@ -281,6 +281,125 @@ def test_fused_append_matches_two_launches(kernel, dtype, Hq, Hkv, D, past, real
     check(outs[0], ref, TOL[dtype], "fused vs oracle")
 
 
+def _random_chunk_cases(n=40, seed=4242):
+    """Seeded random shapes for a single padded (or unpadded) prefill chunk
+    after a cached prefix: dtype, head dim, KV heads, GQA group (3 included),
+    past length, chunk width, real rows, padding switch, kernel choice and
+    spare capacity past the chunk."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        W = int(rng.choice([64, 128, 171, 256, 512]))
+        cases.append(dict(i=i, dn=str(rng.choice(["bf16", "f16"])), D=int(rng.choice([64, 128])),
+                          Hkv=int(rng.choice([1, 2, 4])), G=int(rng.choice([1, 2, 3, 4, 8])),
+                          past=int(rng.integers(0, 700)), W=W, real=int(rng.integers(1, W + 1)),
+                          pad=bool(rng.integers(2)),
+                          kernel=str(rng.choice(["auto", "narrow", "wide", "general"])),
+                          spare=int(rng.integers(0, 40))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_chunk_cases(), ids=lambda c: f"r{c['i']}")
+def test_random_prefill_chunk_vs_oracle(case):
+    """cpk_prefill_chunk on seeded random shapes (every kernel choice, GQA
+    groups 1-8 including 3, head dims 64 and 128, padded and unpadded, tight
+    and loose capacity) against the oracle: the real rows' outputs within
+    tolerance, the cache's valid rows byte for byte, seqlens_k, and no byte
+    written past the issued width."""
+    c = case
+    Hq, Hkv, D, past, W, real = c["G"] * c["Hkv"], c["Hkv"], c["D"], c["past"], c["W"], c["real"]
+    dtype = si.TORCH_DTYPE[c["dn"]]
+    say(f"case r{c['i']}: {c['dn']} heads {Hq}/{Hkv} D={D} past={past} real={real} W={W} "
+        f"pad={c['pad']} kernel={c['kernel']}")
+    q, k, v = si.gqa_prompt(L=past + real, Hq=Hq, Hkv=Hkv, D=D, dtype=c["dn"], seed=5000 + c["i"])
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    width = cpk.cpk_ladder_width(W, real) if c["pad"] else real
+    cache = cpk.KVCache(1, Hkv, past + width + c["spare"], D, dtype)
+    poison(cache)
+    with cpk.attention_kernel({"auto": 0, **KERNELS}[c["kernel"]]):
+        if past:
+            cpk.cpk_kv_append(cache, 0, kd[:past], vd[:past], 0)
+        out, w = cpk.cpk_prefill_chunk(qd[past:], kd[past:], vd[past:], cache, 0, past, W,
+                                       pad=c["pad"])
+        torch.cuda.synchronize()
+    assert w == width
+    assert int(cache.seqlens_k[0]) == past + real
+    ks, vs = si.storage(k), si.storage(v)
+    n = past + real
+    assert np.array_equal(si.storage(cache.k[0, :, :n]), ks.transpose(1, 0, 2))
+    assert np.array_equal(si.storage(cache.v[0, :, :n]), vs.transpose(1, 0, 2))
+    assert torch.isnan(cache.k[:, :, past + width:].float()).all()
+    ref = oracle_rows(si.storage(q), ks, vs, np.arange(past, n), ODT[dtype])
+    check(out, ref, TOL[dtype], "random chunk vs oracle")
+
+
+def _random_varlen_cases(n=16, seed=777):
+    """Seeded random packed steps: 1-6 sequences, each a decode row or a
+    prompt chunk of 2-260 rows after 0-1500 cached positions, in random
+    slots of a larger cache and a random pack order."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        n_seqs = int(rng.integers(1, 7))
+        seqs = [(int(rng.integers(0, 1500)), 1 if rng.integers(2) else int(rng.integers(2, 261)))
+                for _ in range(n_seqs)]
+        batch = n_seqs + int(rng.integers(0, 3))
+        cases.append(dict(i=i, dn=str(rng.choice(["bf16", "f16"])), D=int(rng.choice([64, 128])),
+                          Hkv=int(rng.choice([1, 2, 4])), G=int(rng.choice([1, 2, 3, 4, 8])),
+                          kernel=str(rng.choice(["auto", "narrow", "wide", "general"])),
+                          seqs=seqs, batch=batch,
+                          slots=[int(x) for x in rng.permutation(batch)[:n_seqs]]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_varlen_cases(), ids=lambda c: f"v{c['i']}")
+def test_random_varlen_step_vs_oracle(case):
+    """cpk_varlen_step on seeded random packs (decode rows and prompt chunks
+    mixed, random slots and order, GQA groups 1-8 including 3, whose one-row
+    sequences take the prompt path) against the oracle over the cached
+    prefix and the new rows: every output row within tolerance, the new K/V
+    rows in the cache byte for byte, seqlens_k of every slot."""
+    c = case
+    Hkv, D = c["Hkv"], c["D"]
+    Hq = c["G"] * Hkv
+    dtype = si.TORCH_DTYPE[c["dn"]]
+    say(f"case v{c['i']}: {c['dn']} heads {Hq}/{Hkv} D={D} kernel={c['kernel']} "
+        f"seqs (past, rows) {c['seqs']} slots {c['slots']}")
+    cap = max(p + r for p, r in c["seqs"]) + 8
+    cache = cpk.KVCache(c["batch"], Hkv, cap, D, dtype)
+    si.fill_seeded(cache.k, 600 + c["i"])
+    si.fill_seeded(cache.v, 700 + c["i"])
+    g = si.generator(800 + c["i"])
+    new = [tuple(si.randn((r, h, D), c["dn"], g).cuda() for h in (Hq, Hkv, Hkv))
+           for _, r in c["seqs"]]
+    prefix = [(si.storage(cache.k[sl, :, :p]), si.storage(cache.v[sl, :, :p]))
+              for sl, (p, _) in zip(c["slots"], c["seqs"])]
+    for sl, (p, _) in zip(c["slots"], c["seqs"]):
+        cache.lens[sl] = p
+    cu = [0]
+    for _, r in c["seqs"]:
+        cu.append(cu[-1] + r)
+    q = torch.cat([x[0] for x in new])
+    kn = torch.cat([x[1] for x in new])
+    vn = torch.cat([x[2] for x in new])
+    with cpk.attention_kernel({"auto": 0, **KERNELS}[c["kernel"]]):
+        out = cpk.cpk_varlen_step(q, kn, vn, cache, c["slots"], cu, [p for p, _ in c["seqs"]])
+        torch.cuda.synchronize()
+    odt = ODT[dtype]
+    for j, (sl, (p, r)) in enumerate(zip(c["slots"], c["seqs"])):
+        assert int(cache.seqlens_k[sl]) == p + r, f"seq {j}: seqlens_k"
+        ks_new = si.storage(new[j][1]).transpose(1, 0, 2)
+        vs_new = si.storage(new[j][2]).transpose(1, 0, 2)
+        assert np.array_equal(si.storage(cache.k[sl, :, p:p + r]), ks_new), f"seq {j}: K rows"
+        assert np.array_equal(si.storage(cache.v[sl, :, p:p + r]), vs_new), f"seq {j}: V rows"
+        kk = oracle.widen(np.ascontiguousarray(np.concatenate([prefix[j][0], ks_new], axis=1)), odt)
+        vv = oracle.widen(np.ascontiguousarray(np.concatenate([prefix[j][1], vs_new], axis=1)), odt)
+        qq = oracle.widen(si.storage(new[j][0]), odt)
+        lim = (p + np.arange(r)).astype(np.int32)
+        ref = oracle.attention(qq, kk, vv, np.zeros(r, np.int32), lim, 1.0 / math.sqrt(D))
+        check(out[cu[j]:cu[j + 1]], ref, TOL[dtype], f"seq {j} (past {p}, rows {r}) vs oracle")
+
+
 @pytest.mark.parametrize("kernel", ["narrow", "wide"])
 def test_prefix_reuse(kernel):
     """Prompt-prefix reuse: prompt A = prefix + suffix A is prefilled in slot
