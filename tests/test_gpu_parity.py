@@ -582,6 +582,55 @@ def test_rolling_small_with_left_pad_full_compare():
     assert bitwise(out_a[n_left:], out_m[n_left:]), "explicit != computed mask"
 
 
+def _random_rolling_cases(n=10, seed=991):
+    """Seeded random rolling schedules: length, window C, chunk c (c <= C,
+    so ring starts wrap mid-tile and C need not be a multiple of the key
+    tile), heads, head dim, dtype, GQA group."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        C = int(rng.integers(64, 700))
+        c = int(rng.integers(16, C + 1))
+        cases.append(dict(i=i, C=C, c=c, L=int(rng.integers(c, 4 * C + 1)),
+                          Hkv=int(rng.choice([1, 2, 4])), G=int(rng.choice([1, 2, 4])),
+                          D=int(rng.choice([64, 128])), dn=str(rng.choice(["f16", "bf16"]))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_rolling_cases(), ids=lambda c: f"roll{c['i']}")
+def test_random_rolling_vs_oracle(case):
+    """Seeded random rolling schedules through roll_prefill and ring_prefill
+    (deferred merges wherever the key range splits) against the oracle's
+    literal rolling prefill: real rows within tolerance with computed
+    visibility and with the explicit masks, both schedules bit-equal, the
+    final caches byte for byte."""
+    c_ = case
+    C, c, L, Hkv, D = c_["C"], c_["c"], c_["L"], c_["Hkv"], c_["D"]
+    Hq = c_["G"] * Hkv
+    dtype = si.TORCH_DTYPE[c_["dn"]]
+    odt = ODT[dtype]
+    say(f"case roll{c_['i']}: {c_['dn']} L={L} C={C} c={c} heads {Hq}/{Hkv} D={D}")
+    g = si.generator(900 + c_["i"])
+    q = si.randn((L, Hq, D), c_["dn"], g)
+    k = si.randn((L, Hkv, D), c_["dn"], g)
+    v = si.randn((L, Hkv, D), c_["dn"], g)
+    qs, ks, vs = (si.storage(x) for x in (q, k, v))
+    ref, n_left, rk, rv, masks = oracle.roll_prefill(qs, ks, vs, C, c, odt)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    mk = [torch.from_numpy(m).to(dtype).cuda() for m in masks]
+    for m in (None, mk):
+        tag = "explicit mask" if m is not None else "computed visibility"
+        out_l, nl, lk, lv = cpk.roll_prefill(qd, kd, vd, C, c, masks=m)
+        out_r, nl2, gk, gv, st = cpk.ring_prefill(qd, kd, vd, C, c, masks=m)
+        torch.cuda.synchronize()
+        assert nl == nl2 == n_left
+        assert np.array_equal(si.storage(lk), rk) and np.array_equal(si.storage(lv), rv)
+        kview, vview = cpk.cpk_ring_view(gk.unsqueeze(0), gv.unsqueeze(0), st)
+        assert np.array_equal(si.storage(kview[0]), rk) and np.array_equal(si.storage(vview[0]), rv)
+        assert bitwise(out_l, out_r), f"{tag}: ring != literal shift"
+        check(out_l[n_left:], ref[n_left:], TOL[dtype], f"{tag} vs oracle (real rows)")
+
+
 def test_rolling_split_vs_unsplit():
     """The rolling attention with a workspace (key range split over 4 parts
     of one 128-key tile each, merged in part order) and without one: both
