@@ -400,6 +400,72 @@ def test_random_varlen_step_vs_oracle(case):
         check(out[cu[j]:cu[j + 1]], ref, TOL[dtype], f"seq {j} (past {p}, rows {r}) vs oracle")
 
 
+@pytest.mark.parametrize("case", _random_varlen_cases(n=8, seed=4711), ids=lambda c: f"p{c['i']}")
+def test_random_paged_step_vs_oracle(case):
+    """The random packed steps over a paged cache (256-position blocks handed
+    out in a seeded random order): a first packed step writes every
+    sequence's cached prefix as a prompt chunk, the second is the random
+    pack; both steps' outputs against the oracle, and the blocks gathered
+    back through the table equal the prefix and new rows byte for byte."""
+    c = case
+    Hkv, D = c["Hkv"], c["D"]
+    Hq = c["G"] * Hkv
+    dtype = si.TORCH_DTYPE[c["dn"]]
+    odt = ODT[dtype]
+    say(f"case p{c['i']}: paged {c['dn']} heads {Hq}/{Hkv} D={D} kernel={c['kernel']} "
+        f"seqs {c['seqs']} slots {c['slots']}")
+    bs = 256
+    maxb = (max(p + r for p, r in c["seqs"]) + bs - 1) // bs
+    nblk = c["batch"] * maxb + 3
+    paged = cpk.PagedKVCache(c["batch"], Hkv, nblk, bs, maxb, D, dtype)
+    rng = np.random.default_rng(1000 + c["i"])
+    perm = rng.permutation(nblk)[:c["batch"] * maxb].reshape(c["batch"], maxb)
+    paged.block_table.copy_(torch.from_numpy(perm.astype(np.int32)))
+    g = si.generator(1100 + c["i"])
+    pre = [tuple(si.randn((p, h, D), c["dn"], g).cuda() for h in (Hq, Hkv, Hkv))
+           for p, _ in c["seqs"]]
+    new = [tuple(si.randn((r, h, D), c["dn"], g).cuda() for h in (Hq, Hkv, Hkv))
+           for _, r in c["seqs"]]
+
+    def step(parts, pasts, rows):
+        use = [j for j in range(len(parts)) if rows[j] > 0]
+        cu = [0]
+        for j in use:
+            cu.append(cu[-1] + rows[j])
+        q = torch.cat([parts[j][0] for j in use])
+        kn = torch.cat([parts[j][1] for j in use])
+        vn = torch.cat([parts[j][2] for j in use])
+        out = cpk.cpk_paged_varlen_step(q, kn, vn, paged, [c["slots"][j] for j in use], cu,
+                                        [pasts[j] for j in use])
+        torch.cuda.synchronize()
+        return {j: out[cu[i]:cu[i + 1]] for i, j in enumerate(use)}, use
+
+    def ref_rows(qx, kx, vx, past):
+        r = qx.shape[0]
+        kk = oracle.widen(np.ascontiguousarray(kx.transpose(1, 0, 2)), odt)
+        vv = oracle.widen(np.ascontiguousarray(vx.transpose(1, 0, 2)), odt)
+        lim = (past + np.arange(r)).astype(np.int32)
+        return oracle.attention(oracle.widen(qx, odt), kk, vv, np.zeros(r, np.int32), lim,
+                                1.0 / math.sqrt(D))
+
+    with cpk.attention_kernel({"auto": 0, **KERNELS}[c["kernel"]]):
+        pasts0 = [0] * len(c["seqs"])
+        out0, use0 = step(pre, pasts0, [p for p, _ in c["seqs"]])
+        out1, _ = step(new, [p for p, _ in c["seqs"]], [r for _, r in c["seqs"]])
+    for j in use0:
+        ps = [si.storage(x) for x in pre[j]]
+        check(out0[j], ref_rows(ps[0], ps[1], ps[2], 0), TOL[dtype], f"seq {j} prefix step")
+    for j, (sl, (p, r)) in enumerate(zip(c["slots"], c["seqs"])):
+        assert int(paged.seqlens_k[sl]) == p + r
+        ks = np.concatenate([si.storage(pre[j][1]), si.storage(new[j][1])])
+        vs = np.concatenate([si.storage(pre[j][2]), si.storage(new[j][2])])
+        gk, gv = paged.gather(sl, p + r)
+        assert np.array_equal(si.storage(gk), ks.transpose(1, 0, 2)), f"seq {j}: K blocks"
+        assert np.array_equal(si.storage(gv), vs.transpose(1, 0, 2)), f"seq {j}: V blocks"
+        ref = ref_rows(si.storage(new[j][0]), ks, vs, p)
+        check(out1[j], ref, TOL[dtype], f"seq {j} (past {p}, rows {r}) vs oracle")
+
+
 @pytest.mark.parametrize("kernel", ["narrow", "wide"])
 def test_prefix_reuse(kernel):
     """Prompt-prefix reuse: prompt A = prefix + suffix A is prefilled in slot
