@@ -473,13 +473,35 @@ def bench_ladder(cpk, si, torch, reps=2, passes=10, warm=3):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / passes
+    # the same pass captured once as a HIP graph (host launch gaps drop out),
+    # checked against the eager pass, then replayed
+    ref = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    for o, r in zip(outs, ref):
+        if not torch.equal(o.view(torch.int16), r.view(torch.int16)):
+            raise RuntimeError("ladder graph replay differs from the eager pass")
+    e0.record(stream)
+    for _ in range(passes):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    g_ms = e0.elapsed_time(e1) / passes
     f_useful = 4 * D * Hq * useful * reps
     f_issued = 4 * D * Hq * issued * reps
     return {"prompts": lengths, "runs_each": reps, "ms": round(ms, 3),
             "useful_gflop": round(f_useful / 1e9, 2), "issued_gflop": round(f_issued / 1e9, 2),
             "useful_tflops": round(f_useful / (ms * 1e-3) / 1e12, 1),
             "issued_tflops": round(f_issued / (ms * 1e-3) / 1e12, 1),
-            "note": "eager cpk_prefill_chunk calls (append + attention per chunk)"}
+            "graph_ms": round(g_ms, 3),
+            "graph_useful_tflops": round(f_useful / (g_ms * 1e-3) / 1e12, 1),
+            "graph_issued_tflops": round(f_issued / (g_ms * 1e-3) / 1e12, 1),
+            "note": "eager cpk_prefill_chunk calls (append + attention per chunk); graph_*: "
+                    "the same pass captured as a HIP graph and replayed"}
 
 
 def bench_rolling(cpk, si, torch, explicit_mask=True, ring=False, reps=50, warm=10,
