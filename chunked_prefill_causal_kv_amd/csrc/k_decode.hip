@@ -12,11 +12,13 @@
 // * GQA packing: the G query heads of one KV head are computed together,
 //   so each K/V byte is read from HBM once per KV head, not once per query
 //   head.
-// * A key row is spread over D/8 lanes, 16 bytes (8 elements) per lane, so
-//   a wave's load instruction covers whole 128-byte lines of consecutive
-//   keys.  Each of the 4 waves streams 64 keys in steps of 4 keys per lane
-//   group, with the next step's K/V loads in flight while the current step
-//   computes (double buffering in registers, non-temporal loads).
+// * A key row is spread over D/8 lanes, 16 bytes (8 elements) per lane, and
+//   the lane groups of a wave take consecutive keys, so each load
+//   instruction reads one contiguous 1 KB span of rows (measured 0.7%
+//   faster than lane groups each taking 4 consecutive keys).  Each of the 4
+//   waves streams 64 keys in steps of 4 keys per lane group, with the next
+//   step's K/V loads in flight while the current step computes (double
+//   buffering in registers, non-temporal loads).
 // * QK^T: packed 2-element dot products (v_dot2_f32_{bf16,f16}) in fp32,
 //   summed over the lane group with DPP butterflies that leave identical
 //   bits in every lane.  Softmax is online per query head with a lazy
@@ -192,15 +194,18 @@ void decode_kernel(DecodeArgs a)
     for (int h = 0; h < G; ++h) qv[h] = *(const uint4 *)(qp + (int64_t)h * D);
 
     // the wave streams keys [wbase, wlast]; in step st, lane group gq takes
-    // keys wbase + st*STEP + kKK*gq + (0 .. kKK-1).  Keys are clamped to
+    // keys wbase + st*STEP + kk*GPW + gq (kk = 0 .. kKK-1), so each load
+    // instruction (one kk) reads GPW consecutive keys: one contiguous
+    // 64 x 16-byte span per wave.  Keys are clamped to
     // wlast, so a step past the end re-reads only that row.
     const int wbase = sb + wave * kKeysPerWave;
     const int wlast = min(n_keys, wbase + kKeysPerWave) - 1;
     auto load_step = [&](int st, KVStep &b) __attribute__((always_inline)) {
-        const int key0 = wbase + st * STEP + kKK * gq;
+        const int key0 = wbase + st * STEP + gq;
 #pragma unroll
         for (int kk = 0; kk < kKK; ++kk) {
-            const uint32_t off = (uint32_t)(min(key0 + kk, wlast) - key_org) * (D * 2) + 16u * j;
+            const uint32_t off =
+                (uint32_t)(min(key0 + kk * GPW, wlast) - key_org) * (D * 2) + 16u * j;
             b.k[kk] = load_stream(kbase, off);
             b.v[kk] = load_stream(vbase, off);
         }
@@ -217,7 +222,7 @@ void decode_kernel(DecodeArgs a)
 
     const float c = a.scale_log2;   // > 0: the maximum of raw scores is the maximum of scaled ones
     auto compute_step = [&](int st, const KVStep &b) __attribute__((always_inline)) {
-        const int key0 = wbase + st * STEP + kKK * gq;
+        const int key0 = wbase + st * STEP + gq;
         float s[kKK][G];
 #pragma unroll
         for (int kk = 0; kk < kKK; ++kk)
@@ -233,7 +238,7 @@ void decode_kernel(DecodeArgs a)
             for (int kk = 0; kk < kKK; ++kk)
 #pragma unroll
                 for (int h = 0; h < G; ++h)
-                    if (key0 + kk > wlast) s[kk][h] = -INFINITY;
+                    if (key0 + kk * GPW > wlast) s[kk][h] = -INFINITY;
         }
         // online softmax per head with a lazy maximum: the reference m (log2
         // domain) is raised only when a step's maximum exceeds it by more
