@@ -29,6 +29,13 @@
 //
 // * Fused append: in a step that also appends, the workgroup whose segment
 //   holds a sequence's new key writes that K/V row into the cache itself.
+// * Epilogue: the 16 lane groups' (m, l, acc) meet in LDS; one thread per
+//   head forms the weights exp2(m - M) and the merged l, then every thread
+//   folds two adjacent columns over the lane groups in lane-group order.
+//   The segment record goes out with non-temporal stores: measured on a
+//   2.33 GB step of 64 sequences, the kernel gains 10 us and the combine,
+//   whose reads of the records then come from memory rather than L2,
+//   loses 2 us.
 //
 // decode_combine merges the per-segment (max, sum, acc) partials of every
 // (sequence, query head) in a fixed order (deterministic, no atomics).
@@ -140,6 +147,9 @@ void decode_kernel(DecodeArgs a)
     constexpr int WS = D + 4;                  // workspace record: m, l, pad, pad, acc[D]
     __shared__ float Mg[NG][G];
     __shared__ float Lg[NG][G];
+    __shared__ float Eg[NG][G];   // per (lane group, head) merge weights
+    __shared__ float Mh[G];       // per head maximum over the lane groups
+    __shared__ float Lh[G];       // per head weighted sum of l
     __shared__ __attribute__((aligned(16))) float Ag[NG][G][D];
 
     const int z = blockIdx.z;
@@ -322,25 +332,45 @@ void decode_kernel(DecodeArgs a)
     }
     __syncthreads();
 
-    for (int idx = tid; idx < G * D; idx += kThreadsDec) {
-        const int h = idx / D;
-        const int d = idx % D;
+    // each head's maximum over the lane groups, the lane groups' weights
+    // exp2(m - M) and the weighted sum of l, once per head
+    if (tid < G) {
+        const int h = tid;
         float M = -INFINITY;
 #pragma unroll
         for (int q = 0; q < NG; ++q) M = fmaxf(M, Mg[q][h]);
-        float acc = 0.f, lsum = 0.f;
+        float lsum = 0.f;
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
             const float mq = Mg[q][h];
             const float e = (mq == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mq - M);
-            acc = __builtin_fmaf(e, Ag[q][h][d], acc);
+            Eg[q][h] = e;
             lsum = __builtin_fmaf(e, Lg[q][h], lsum);
         }
+        Mh[h] = M;
+        Lh[h] = lsum;
+    }
+    __syncthreads();
+
+    // two adjacent columns per thread
+    static_assert((G * D / 2) % kThreadsDec == 0 || G * D / 2 < kThreadsDec, "column pairs");
+    for (int idx = tid; idx < G * D / 2; idx += kThreadsDec) {
+        const int h = (2 * idx) / D;
+        const int d = (2 * idx) % D;
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            const float e = Eg[q][h];
+            const float2 x = *(const float2 *)&Ag[q][h][d];
+            acc0 = __builtin_fmaf(e, x.x, acc0);
+            acc1 = __builtin_fmaf(e, x.y, acc1);
+        }
         float *rec = a.ws + (((int64_t)z * a.Hq + g * G + h) * a.max_segs + seg) * WS;
-        rec[4 + d] = acc;
+        typedef float f2v __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(f2v{acc0, acc1}, (f2v *)(rec + 4 + d));
         if (d == 0) {
-            rec[0] = M;
-            rec[1] = lsum;
+            __builtin_nontemporal_store(Mh[h], rec);
+            __builtin_nontemporal_store(Lh[h], rec + 1);
         }
     }
 }
