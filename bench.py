@@ -3,10 +3,10 @@
 
 Step = one chunked prefill of a 4000-token GQA prompt (32 query / 8 KV
 heads, head dim 128, bf16, cache bound at capacity 8192) in W = 512 chunks
-through the C ABI: rewind to 0, then cpk_prefill_chunk per chunk (one
-launch each: chunk attention that also appends the padded chunk's K/V to
-the cache, the 416-row tail padded to 512, truncation, true length
-recorded).  The step is captured once as a HIP graph and replayed
+through the C ABI: cpk_prefill_chunk per chunk (one launch each: chunk
+attention that also appends the padded chunk's K/V to the cache, the
+416-row tail padded to 512, truncation, true length recorded; the first
+chunk, at past 0, starts the prompt over, so no separate length reset).  The step is captured once as a HIP graph and replayed
 (checked bit for bit against an eager step); the eager per-call step time is
 reported beside it.  Inputs are seeded synthetic N(0,1) values already
 resident in HBM.
@@ -144,9 +144,9 @@ def bench_chunked(cpk, si, torch, steps, warmup):
 
     def step(events):
         # each padded chunk is one launch of the attention kernel, which
-        # also appends the chunk's K/V to the cache (fused append)
-        if cache.lens[0]:
-            cpk.cpk_rewind(cache, 0, 0)
+        # also appends the chunk's K/V to the cache (fused append) and
+        # records the slot's length; the first chunk (past 0) starts the
+        # prompt over, so a pass needs no separate reset of the length
         for i, (past, rows) in enumerate(chunks):
             sl = slice(past, past + rows)
             if events is not None:
@@ -192,7 +192,7 @@ def bench_chunked(cpk, si, torch, steps, warmup):
 
 def bench_step_graph(cpk, si, torch, steps, warmup, q, k, v):
     """The whole hot path for one prompt through the product entry point:
-    rewind to 0, then cpk_prefill_chunk (append + attention, padded tail) for
+    cpk_prefill_chunk (append + attention, padded tail, length recorded) for
     every W=512 chunk.  Eight consecutive steps are captured once as a HIP
     graph and replayed (one step per graph when the step count is not a
     multiple of 8), so host launch gaps drop out and each replay's own
@@ -205,7 +205,6 @@ def bench_step_graph(cpk, si, torch, steps, warmup, q, k, v):
     chunks = cpk.cpk_split_chunks(L, W)
 
     def step():
-        cpk.cpk_rewind(cache, 0, 0)
         for past, rows in chunks:
             sl = slice(past, past + rows)
             cpk.cpk_prefill_chunk(q[sl], k[sl], v[sl], cache, 0, past, W, pad=True, out=out[sl])
@@ -1006,7 +1005,7 @@ def main():
                                "(7x512 + 416 padded to 512), 32 query / 8 KV heads, "
                                "head_dim 128, cache capacity 8192, seqlens_k",
                    "global_batch": 1, "seq_len": 4000, "chunk": 512, "parallelism": "none",
-                   "step": "rewind + cpk_prefill_chunk per chunk; 8 steps captured per HIP "
+                   "step": "cpk_prefill_chunk per chunk; 8 steps captured per HIP "
                            "graph, replayed steps/8 times",
                    "ms_per_step_eager_calls": round(r["ms_step"], 4)},
         "roofline": {"bound": "mfma", "achieved": round(r["achieved"], 2),
