@@ -536,6 +536,19 @@ def test_workload2_gqa_bf16_full_size():
     assert int(cache.seqlens_k[0]) == 4000
     assert np.array_equal(si.storage(cache.k[0, :, :4000]), ks.transpose(1, 0, 2))
     assert np.array_equal(si.storage(cache.v[0, :, :4000]), vs.transpose(1, 0, 2))
+    # the prompt again on the full cache with no length reset in between: the
+    # first chunk (past 0) records the slot's new length itself, and the
+    # second pass gives the first pass's bits
+    again = torch.empty_like(qd)
+    for i, (past, n) in enumerate(chunks):
+        sl = slice(past, past + n)
+        cpk.cpk_prefill_chunk(qd[sl], kd[sl], vd[sl], cache, 0, past, 512, pad=True, out=again[sl])
+        if i == 0:
+            torch.cuda.synchronize()
+            assert int(cache.seqlens_k[0]) == n
+    torch.cuda.synchronize()
+    assert bitwise(again, res["auto"][0]), "second pass without a reset != first pass"
+    assert int(cache.seqlens_k[0]) == 4000
 
 
 # ------------------------------------------------- workload 3: padding ladder
